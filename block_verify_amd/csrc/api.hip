@@ -1,0 +1,536 @@
+// C ABI of the block-verify path: validation, HBM layouts, orchestration.
+// Kernels live in kernels_forward.hip and kernels_round.hip.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "round_dev.h"
+
+namespace {
+thread_local int32_t g_last_hip = 0;
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SPECDEC_OK;
+  g_last_hip = (int32_t)e;
+  return SPECDEC_EHIP;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+namespace sd {
+
+int dims_from_desc(const specdec_model_desc* d, Dims* o) {
+  if (!d || !o) return SPECDEC_EINVAL;
+  Dims x;
+  x.L = d->n_layers; x.H = d->hidden; x.nq = d->n_q_heads; x.nkv = d->n_kv_heads; x.hd = d->head_dim;
+  x.F = d->ffn; x.V = d->vocab; x.theta = d->rope_theta; x.eps = d->rms_eps; x.wfmt = d->weight_format;
+  if (x.L <= 0 || x.H <= 0 || x.nq <= 0 || x.nkv <= 0 || x.hd <= 0 || x.F <= 0 || x.V <= 0) return SPECDEC_EINVAL;
+  if (!(x.theta > 0.f) || !(x.eps >= 0.f)) return SPECDEC_EINVAL;
+  if (x.wfmt != SPECDEC_W_BF16 && x.wfmt != SPECDEC_W_Q4G64) return SPECDEC_EINVAL;
+  if (x.hd != 64 && x.hd != 128) return SPECDEC_ESHAPE;
+  if (x.nq % x.nkv != 0 || x.nq / x.nkv > 8) return SPECDEC_ESHAPE;
+  if (x.H % 32 || x.F % 32 || x.qdim() % 32 || x.V % 16 || x.H % 16) return SPECDEC_ESHAPE;
+  if (x.H > 8192 || x.V > (1 << 24)) return SPECDEC_ESHAPE;
+  *o = x;
+  return SPECDEC_OK;
+}
+
+BlobLayout blob_layout(const Dims& d) {
+  BlobLayout b;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  b.embed = take((size_t)d.V * d.H * 2);
+  b.layer.resize(d.L);
+  for (int l = 0; l < d.L; ++l) {
+    LayerOffsets& o = b.layer[l];
+    o.attn_norm = take((size_t)d.H * 4);
+    o.wqkv = take((size_t)d.qkv_rows() * d.H * 2);
+    o.wo = take((size_t)d.H * d.qdim() * 2);
+    o.mlp_norm = take((size_t)d.H * 4);
+    o.wgu = take((size_t)2 * d.F * d.H * 2);
+    o.wdown = take((size_t)d.H * d.F * 2);
+  }
+  b.final_norm = take((size_t)d.H * 4);
+  b.lm_head = take((size_t)d.V * d.H * 2);
+  b.total = off;
+  return b;
+}
+
+WsPlan ws_plan(const Dims& d, int max_rows, int max_len) {
+  WsPlan p;
+  p.max_rows = kMaxRows;
+  p.nt = kMaxNT;
+  p.max_chunks = (max_len + kAttnChunk - 1) / kAttnChunk;
+  p.lm_wgs = (d.V / 16 + 3) / 4;
+  (void)max_rows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t R = kMaxRows;
+  p.err = take(256);
+  p.x = take(R * d.H * 4);
+  p.xb = take((size_t)kMaxNT * d.H * 32);
+  p.ss = take(R * (d.H / 16) * 4);
+  p.q = take(R * d.qdim() * 4);
+  p.ob = take((size_t)kMaxNT * d.qdim() * 32);
+  p.hb = take((size_t)kMaxNT * d.F * 32);
+  p.att_o = take((size_t)d.nkv * p.max_chunks * (R * 8) * d.hd * 4);
+  p.att_ml = take((size_t)d.nkv * p.max_chunks * (R * 8) * 2 * 4);
+  p.lm_part = take(R * p.lm_wgs * 3 * 4);
+  p.toks = take(R * 4 * 2);
+  p.logits = take(R * (size_t)d.V * 4);
+  p.total = off;
+  return p;
+}
+
+RoundWsPlan round_ws_plan(int V, int k) {
+  RoundWsPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t K1 = (size_t)kMaxK + 1;
+  (void)k;
+  p.flags = take(kNumFlags * 4);
+  p.block = take(K1 * 4);
+  p.repair_tok = take(4);
+  p.rows_argmax = take(K1 * 4);
+  p.rows_lse = take(K1 * 4);
+  p.repair_argmax = take(4);
+  p.repair_lse = take(4);
+  p.q_lse = take(K1 * 4);
+  p.snap = take(kNumSnap * 4);
+  p.dbg = take((2 * kMaxK + 2) * 4);
+  p.draft_argmax = take(4);
+  p.rows_logits = take(K1 * V * 4);
+  p.saved_logits = take((size_t)V * 4);
+  p.q_logits = take(K1 * V * 4);
+  p.z = take((size_t)V * 4);
+  p.draft_logits = take((size_t)V * 4);
+  p.snap_logits = take((size_t)V * 4);
+  p.total = off;
+  return p;
+}
+
+hipError_t launch_copy_last(const FwdArgs& a, float* logits_dst, int32_t* argmax_dst, float* lse_dst);
+hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStream_t s);
+
+}  // namespace sd
+
+using namespace sd;
+
+struct specdec_round {
+  specdec_round_desc desc;
+  RoundDev dev;
+  WsPlan tplan, dplan;
+  int prompt_len;
+};
+
+extern "C" {
+
+int32_t specdec_last_hip_error(void) { return g_last_hip; }
+
+const char* specdec_status_str(int s) {
+  switch (s) {
+    case SPECDEC_OK: return "ok";
+    case SPECDEC_EINVAL: return "invalid argument";
+    case SPECDEC_ECAPACITY: return "capacity exceeded";
+    case SPECDEC_ESHAPE: return "unsupported shape";
+    case SPECDEC_EHIP: return "HIP runtime error";
+    case SPECDEC_EDEVICE: return "device error flag set";
+    case SPECDEC_EUNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+int32_t specdec_tensor_count(const specdec_model_desc* desc) {
+  if (!desc || desc->n_layers <= 0) return 0;
+  return 3 + 9 * desc->n_layers;
+}
+
+int specdec_weights_bytes(const specdec_model_desc* desc, size_t* bytes) {
+  Dims d;
+  int rc = dims_from_desc(desc, &d);
+  if (rc) return rc;
+  if (!bytes) return SPECDEC_EINVAL;
+  if (d.wfmt != SPECDEC_W_BF16) return SPECDEC_EUNSUPPORTED;
+  *bytes = blob_layout(d).total;
+  return SPECDEC_OK;
+}
+
+int specdec_weights_pack(const specdec_model_desc* desc, int32_t index, const void* d_src, void* d_blob, void* stream) {
+  Dims d;
+  int rc = dims_from_desc(desc, &d);
+  if (rc) return rc;
+  if (!d_src || !d_blob) return SPECDEC_EINVAL;
+  if (index < 0 || index >= 3 + 9 * d.L) return SPECDEC_EINVAL;
+  if (d.wfmt != SPECDEC_W_BF16) return SPECDEC_EUNSUPPORTED;
+  return hip_status(launch_pack(d, index, d_src, d_blob, blob_layout(d), (hipStream_t)stream));
+}
+
+int specdec_model_create(const specdec_model_desc* desc, const void* d_blob, const specdec_model* share,
+                         specdec_model** out) {
+  Dims d;
+  int rc = dims_from_desc(desc, &d);
+  if (rc) return rc;
+  if (!d_blob || !out) return SPECDEC_EINVAL;
+  if (d.wfmt != SPECDEC_W_BF16) return SPECDEC_EUNSUPPORTED;
+  if (share && (share->d.H != d.H || share->d.V != d.V)) return SPECDEC_ESHAPE;
+  BlobLayout lay = blob_layout(d);
+  const char* b = static_cast<const char*>(d_blob);
+  specdec_model* m = new (std::nothrow) specdec_model;
+  if (!m) return SPECDEC_EINVAL;
+  m->d = d;
+  m->embed = share ? share->embed : reinterpret_cast<const bf16_bits*>(b + lay.embed);
+  m->final_norm = share ? share->final_norm : reinterpret_cast<const float*>(b + lay.final_norm);
+  m->lm_head = share ? share->lm_head : reinterpret_cast<const bf16x8_t*>(b + lay.lm_head);
+  m->layers.resize(d.L);
+  for (int l = 0; l < d.L; ++l) {
+    const LayerOffsets& o = lay.layer[l];
+    LayerPtrs& p = m->layers[l];
+    memset(&p, 0, sizeof(p));
+    p.attn_norm = reinterpret_cast<const float*>(b + o.attn_norm);
+    p.mlp_norm = reinterpret_cast<const float*>(b + o.mlp_norm);
+    p.wqkv = reinterpret_cast<const bf16x8_t*>(b + o.wqkv);
+    p.wo = reinterpret_cast<const bf16x8_t*>(b + o.wo);
+    p.wgu = reinterpret_cast<const bf16x8_t*>(b + o.wgu);
+    p.wdown = reinterpret_cast<const bf16x8_t*>(b + o.wdown);
+  }
+  *out = m;
+  return SPECDEC_OK;
+}
+
+void specdec_model_destroy(specdec_model* m) { delete m; }
+
+int specdec_cache_bytes(const specdec_model_desc* desc, int32_t max_len, size_t* bytes) {
+  Dims d;
+  int rc = dims_from_desc(desc, &d);
+  if (rc) return rc;
+  if (!bytes || max_len <= 0) return SPECDEC_EINVAL;
+  size_t kv = align256((size_t)d.L * 2 * d.nkv * max_len * d.hd * 2);
+  size_t rope = align256((size_t)max_len * (d.hd / 2) * 8);
+  *bytes = kv + rope;
+  return SPECDEC_OK;
+}
+
+int specdec_cache_create(const specdec_model_desc* desc, void* d_mem, size_t bytes, int32_t max_len, int32_t* d_len,
+                         specdec_cache** out) {
+  Dims d;
+  int rc = dims_from_desc(desc, &d);
+  if (rc) return rc;
+  size_t need;
+  rc = specdec_cache_bytes(desc, max_len, &need);
+  if (rc) return rc;
+  if (!d_mem || !d_len || !out) return SPECDEC_EINVAL;
+  if (bytes < need) return SPECDEC_ECAPACITY;
+  specdec_cache* c = new (std::nothrow) specdec_cache;
+  if (!c) return SPECDEC_EINVAL;
+  c->d = d;
+  c->kv = static_cast<bf16_bits*>(d_mem);
+  size_t kv = align256((size_t)d.L * 2 * d.nkv * max_len * d.hd * 2);
+  c->rope = reinterpret_cast<float2*>(static_cast<char*>(d_mem) + kv);
+  c->d_len = d_len;
+  c->max_len = max_len;
+  // RoPE table in double precision on the host: angle = pos * theta^(-2i/d)
+  const int half = d.hd / 2;
+  std::vector<float2> tab((size_t)max_len * half);
+  for (int i = 0; i < half; ++i) {
+    double inv = pow((double)d.theta, -2.0 * i / (double)d.hd);
+    for (int p = 0; p < max_len; ++p) {
+      double a = (double)p * inv;
+      tab[(size_t)p * half + i] = make_float2((float)cos(a), (float)sin(a));
+    }
+  }
+  hipError_t e = hipMemcpy(c->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(d_len, 0, sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    delete c;
+    return hip_status(e);
+  }
+  *out = c;
+  return SPECDEC_OK;
+}
+
+void specdec_cache_destroy(specdec_cache* c) { delete c; }
+
+int specdec_kv_trim(specdec_cache* c, int32_t new_len, int32_t* d_err, void* stream) {
+  if (!c || new_len < 0 || new_len > c->max_len) return SPECDEC_EINVAL;
+  return hip_status(launch_trim(c->d_len, new_len, nullptr, d_err, (hipStream_t)stream));
+}
+
+int specdec_workspace_bytes(const specdec_model_desc* desc, int32_t max_rows, int32_t max_len, size_t* bytes) {
+  Dims d;
+  int rc = dims_from_desc(desc, &d);
+  if (rc) return rc;
+  if (!bytes || max_rows <= 0 || max_len <= 0) return SPECDEC_EINVAL;
+  if (max_rows > SPECDEC_MAX_ROWS) return SPECDEC_ECAPACITY;
+  *bytes = ws_plan(d, max_rows, max_len).total;
+  return SPECDEC_OK;
+}
+
+int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream) {
+  if (!d_ws || ws_bytes < 256) return SPECDEC_EINVAL;
+  return hip_status(hipMemsetAsync(d_ws, 0, 256, (hipStream_t)stream));
+}
+
+static int check_fwd(const specdec_model* m, const specdec_cache* c, int32_t rows, size_t ws_bytes, WsPlan* plan) {
+  if (!m || !c) return SPECDEC_EINVAL;
+  if (rows < 1 || rows > SPECDEC_MAX_ROWS) return SPECDEC_ECAPACITY;
+  if (m->d.L != c->d.L || m->d.nkv != c->d.nkv || m->d.hd != c->d.hd) return SPECDEC_ESHAPE;
+  *plan = ws_plan(m->d, rows, c->max_len);
+  if (ws_bytes < plan->total) return SPECDEC_ECAPACITY;
+  return SPECDEC_OK;
+}
+
+int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t rows,
+                        float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+  WsPlan plan;
+  int rc = check_fwd(m, c, rows, ws_bytes, &plan);
+  if (rc) return rc;
+  if (!d_tokens || !d_ws) return SPECDEC_EINVAL;
+  FwdArgs a;
+  a.m = m; a.c = c; a.tokens = d_tokens; a.rows = rows;
+  a.logits = d_logits ? d_logits : reinterpret_cast<float*>(static_cast<char*>(d_ws) + plan.logits);
+  a.argmax = d_argmax; a.lse = d_lse; a.ws = static_cast<char*>(d_ws); a.plan = &plan;
+  a.stream = (hipStream_t)stream; a.gate = nullptr; a.skip_head = false;
+  return hip_status(launch_forward(a));
+}
+
+int specdec_prefill(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t n, int32_t chunk,
+                    float* d_last_logits, int32_t* d_last_argmax, float* d_last_lse, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  WsPlan plan;
+  int rc = check_fwd(m, c, 1, ws_bytes, &plan);
+  if (rc) return rc;
+  if (!d_tokens || !d_ws || n <= 0 || chunk <= 0) return SPECDEC_EINVAL;
+  if (n > c->max_len) return SPECDEC_ECAPACITY;
+  if (chunk > SPECDEC_MAX_ROWS) chunk = SPECDEC_MAX_ROWS;
+  char* ws = static_cast<char*>(d_ws);
+  for (int off = 0; off < n; off += chunk) {
+    int rows = n - off < chunk ? n - off : chunk;
+    bool last = off + rows >= n;
+    FwdArgs a;
+    a.m = m; a.c = c; a.tokens = d_tokens + off; a.rows = rows;
+    a.logits = reinterpret_cast<float*>(ws + plan.logits);
+    a.argmax = reinterpret_cast<int32_t*>(ws + plan.toks);
+    a.lse = reinterpret_cast<float*>(ws + plan.toks + SPECDEC_MAX_ROWS * 4);
+    a.ws = ws; a.plan = &plan; a.stream = (hipStream_t)stream; a.gate = nullptr;
+    a.skip_head = !last;
+    hipError_t e = launch_forward(a);
+    if (e == hipSuccess && last) e = launch_copy_last(a, d_last_logits, d_last_argmax, d_last_lse);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return SPECDEC_OK;
+}
+
+int specdec_check(const void* d_ws, int32_t* bits, void* stream) {
+  if (!d_ws) return SPECDEC_EINVAL;
+  int32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, d_ws, sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (bits) *bits = h;
+  return h ? SPECDEC_EDEVICE : SPECDEC_OK;
+}
+
+// ------------------------------------------------------------------ rounds
+
+int specdec_round_state_bytes(int32_t cap, size_t* bytes) {
+  if (!bytes || cap <= 0) return SPECDEC_EINVAL;
+  *bytes = sizeof(specdec_round_state) + (size_t)cap * 4;
+  return SPECDEC_OK;
+}
+
+int specdec_round_ws_bytes(const specdec_model_desc* target, int32_t k, size_t* bytes) {
+  Dims d;
+  int rc = dims_from_desc(target, &d);
+  if (rc) return rc;
+  if (!bytes || k < 1 || k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
+  *bytes = round_ws_plan(d.V, k).total;
+  return SPECDEC_OK;
+}
+
+int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
+  if (!desc || !out || !desc->target || !desc->target_cache || !desc->d_state || !desc->d_ws || !desc->d_round_ws)
+    return SPECDEC_EINVAL;
+  const specdec_round_desc& q = *desc;
+  if (q.k < 1 || q.k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
+  if (q.state_cap <= 0) return SPECDEC_EINVAL;
+  if (q.mode != SPECDEC_GREEDY && q.mode != SPECDEC_STOCHASTIC) return SPECDEC_EINVAL;
+  if (q.schedule != SPECDEC_SCHEDULE_A && q.schedule != SPECDEC_SCHEDULE_B) return SPECDEC_EINVAL;
+  if (q.draft_source < SPECDEC_DRAFT_TABLE || q.draft_source > SPECDEC_DRAFT_Q4_SELF) return SPECDEC_EINVAL;
+  const Dims& d = q.target->d;
+  const int rows = q.k + (q.schedule == SPECDEC_SCHEDULE_B ? 1 : 0);
+  if (rows > SPECDEC_MAX_ROWS) return SPECDEC_ECAPACITY;
+  if (q.schedule == SPECDEC_SCHEDULE_B && !q.bonus) return SPECDEC_EINVAL;
+  if (q.mode == SPECDEC_STOCHASTIC && (q.schedule != SPECDEC_SCHEDULE_A || q.draft_source != SPECDEC_DRAFT_NOISY_SELF))
+    return SPECDEC_EUNSUPPORTED;
+  if (q.mode == SPECDEC_GREEDY && q.draft_source == SPECDEC_DRAFT_NOISY_SELF) return SPECDEC_EINVAL;
+  if ((q.draft_source == SPECDEC_DRAFT_TABLE || q.draft_source == SPECDEC_DRAFT_MODEL) &&
+      (!q.d_draft_table || q.table_len <= 0))
+    return SPECDEC_EINVAL;
+  if (q.draft_source == SPECDEC_DRAFT_NOISY_SELF && (!q.d_noise || q.noise_rows <= 0)) return SPECDEC_EINVAL;
+  if (q.draft_source == SPECDEC_DRAFT_MODEL) {
+    if (!q.draft || !q.draft_cache || !q.d_draft_ws) return SPECDEC_EINVAL;
+    if (q.draft->d.V != d.V) return SPECDEC_ESHAPE;
+  }
+  if (q.draft_source == SPECDEC_DRAFT_Q4_SELF) {
+    if (!q.draft || q.draft_cache) return SPECDEC_EINVAL;
+    if (q.schedule != SPECDEC_SCHEDULE_A) return SPECDEC_EUNSUPPORTED;
+    if (q.draft->d.L != d.L || q.draft->d.H != d.H || q.draft->d.V != d.V || q.draft->d.nkv != d.nkv ||
+        q.draft->d.hd != d.hd)
+      return SPECDEC_ESHAPE;
+  }
+  specdec_round* r = new (std::nothrow) specdec_round;
+  if (!r) return SPECDEC_EINVAL;
+  r->desc = q;
+  r->prompt_len = 0;
+  r->tplan = ws_plan(d, rows, q.target_cache->max_len);
+  if (q.ws_bytes < r->tplan.total) { delete r; return SPECDEC_ECAPACITY; }
+  if (q.draft_source == SPECDEC_DRAFT_MODEL) {
+    r->dplan = ws_plan(q.draft->d, 1, q.draft_cache->max_len);
+    if (q.draft_ws_bytes < r->dplan.total) { delete r; return SPECDEC_ECAPACITY; }
+  }
+  RoundWsPlan rp = round_ws_plan(d.V, q.k);
+  if (q.round_ws_bytes < rp.total) { delete r; return SPECDEC_ECAPACITY; }
+  char* w = static_cast<char*>(q.d_round_ws);
+  RoundDev& v = r->dev;
+  memset(&v, 0, sizeof(v));
+  v.state = q.d_state;
+  v.flags = reinterpret_cast<int32_t*>(w + rp.flags);
+  v.block = reinterpret_cast<int32_t*>(w + rp.block);
+  v.repair_tok = reinterpret_cast<int32_t*>(w + rp.repair_tok);
+  v.rows_argmax = reinterpret_cast<int32_t*>(w + rp.rows_argmax);
+  v.rows_lse = reinterpret_cast<float*>(w + rp.rows_lse);
+  v.rows_logits = reinterpret_cast<float*>(w + rp.rows_logits);
+  v.saved_logits = reinterpret_cast<float*>(w + rp.saved_logits);
+  v.repair_argmax = reinterpret_cast<int32_t*>(w + rp.repair_argmax);
+  v.repair_lse = reinterpret_cast<float*>(w + rp.repair_lse);
+  v.q_logits = reinterpret_cast<float*>(w + rp.q_logits);
+  v.q_lse = reinterpret_cast<float*>(w + rp.q_lse);
+  v.z = reinterpret_cast<float*>(w + rp.z);
+  v.draft_logits = reinterpret_cast<float*>(w + rp.draft_logits);
+  v.draft_argmax = reinterpret_cast<int32_t*>(w + rp.draft_argmax);
+  v.snap_logits = reinterpret_cast<float*>(w + rp.snap_logits);
+  v.snap = reinterpret_cast<int32_t*>(w + rp.snap);
+  v.dbg = reinterpret_cast<float*>(w + rp.dbg);
+  v.t_len = q.target_cache->d_len;
+  v.d_len = q.draft_source == SPECDEC_DRAFT_MODEL ? q.draft_cache->d_len : nullptr;
+  v.err = static_cast<int32_t*>(q.d_ws);
+  v.table = q.d_draft_table;
+  v.table_len = q.table_len;
+  v.noise = q.d_noise;
+  v.noise_rows = q.noise_rows;
+  v.seed = q.philox_seed;
+  v.k = q.k; v.V = d.V; v.bonus = q.bonus ? 1 : 0; v.schedule = q.schedule; v.draft_source = q.draft_source;
+  v.mode = q.mode;
+  v.state_cap = q.state_cap;
+  *out = r;
+  return SPECDEC_OK;
+}
+
+void specdec_round_destroy(specdec_round* r) { delete r; }
+
+static hipError_t fwd(const specdec_round* r, bool draft, const int32_t* toks, int rows, float* logits,
+                      int32_t* argmax, float* lse, const int32_t* gate, hipStream_t s) {
+  const specdec_round_desc& q = r->desc;
+  FwdArgs a;
+  const bool own_draft = draft && q.draft_source == SPECDEC_DRAFT_MODEL;
+  a.m = draft ? q.draft : q.target;
+  a.c = own_draft ? q.draft_cache : q.target_cache;
+  a.tokens = toks; a.rows = rows; a.logits = logits; a.argmax = argmax; a.lse = lse;
+  a.ws = static_cast<char*>(own_draft ? q.d_draft_ws : q.d_ws);
+  a.plan = own_draft ? &r->dplan : &r->tplan;
+  a.stream = s; a.gate = gate; a.skip_head = false;
+  return launch_forward(a);
+}
+
+int specdec_round_prefill(specdec_round* r, const int32_t* d_prompt, int32_t n, int32_t chunk, void* stream) {
+  if (!r || !d_prompt || n <= 0 || chunk <= 0) return SPECDEC_EINVAL;
+  const specdec_round_desc& q = r->desc;
+  const bool B = q.schedule == SPECDEC_SCHEDULE_B;
+  const int rows = q.k + (B ? 1 : 0);
+  int need = n + 64 + 2 * rows;
+  if (need > q.target_cache->max_len) return SPECDEC_ECAPACITY;
+  if (B && n < 2) return SPECDEC_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const RoundDev& v = r->dev;
+  int32_t* err = static_cast<int32_t*>(q.d_ws);
+  hipError_t e = launch_trim(q.target_cache->d_len, 0, nullptr, err, s);
+  if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL) e = launch_trim(q.draft_cache->d_len, 0, nullptr, err, s);
+  if (e != hipSuccess) return hip_status(e);
+  int rc = specdec_prefill(q.target, q.target_cache, d_prompt, B ? n - 1 : n, chunk, v.saved_logits, v.repair_argmax,
+                           v.repair_lse, q.d_ws, q.ws_bytes, stream);
+  if (rc) return rc;
+  if (q.draft_source == SPECDEC_DRAFT_MODEL) {
+    rc = specdec_prefill(q.draft, q.draft_cache, d_prompt, n, chunk, v.draft_logits, v.draft_argmax, nullptr,
+                         q.d_draft_ws, q.draft_ws_bytes, stream);
+    if (rc) return rc;
+  }
+  r->prompt_len = n;
+  e = launch_snapshot(v, B ? d_prompt + n - 1 : nullptr, s);
+  if (e == hipSuccess) e = launch_reset(v, 0, s);
+  return hip_status(e);
+}
+
+int specdec_round_reset(specdec_round* r, int32_t n_target, void* stream) {
+  if (!r || n_target < 0) return SPECDEC_EINVAL;
+  if (r->prompt_len == 0) return SPECDEC_EINVAL;
+  const specdec_round_desc& q = r->desc;
+  if ((size_t)n_target + q.k + 1 > (size_t)q.state_cap) return SPECDEC_ECAPACITY;
+  int rows = q.k + (q.schedule == SPECDEC_SCHEDULE_B ? 1 : 0);
+  // every round commits at least one token; positions used stay below
+  // prompt + n_target + rows + 1
+  if (r->prompt_len + n_target + 2 * rows + 2 > q.target_cache->max_len) return SPECDEC_ECAPACITY;
+  return hip_status(launch_reset(r->dev, n_target, (hipStream_t)stream));
+}
+
+int specdec_verify_round(specdec_round* r, void* stream) {
+  if (!r) return SPECDEC_EINVAL;
+  if (r->prompt_len == 0) return SPECDEC_EINVAL;
+  const specdec_round_desc& q = r->desc;
+  const RoundDev& v = r->dev;
+  hipStream_t s = (hipStream_t)stream;
+  const bool B = q.schedule == SPECDEC_SCHEDULE_B;
+  const int k = q.k;
+  const int32_t* open = v.flags + kFlagOpen;
+  const int32_t* rep = v.flags + kFlagRepair;
+  hipError_t e = launch_round_start(v, s);
+  // ---- draft provision
+  if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL) {
+    for (int j = 0; j < k && e == hipSuccess; ++j)
+      e = fwd(r, true, v.block + (B ? 1 : 0) + j, 1, v.draft_logits, v.draft_argmax, nullptr, open, s);
+  } else if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_NOISY_SELF) {
+    e = launch_draft_sample(v, v.saved_logits, 0, s);
+    for (int j = 1; j < k && e == hipSuccess; ++j) {
+      e = fwd(r, false, v.block + j - 1, 1, v.z, nullptr, nullptr, open, s);
+      if (e == hipSuccess) e = launch_draft_sample(v, v.z, j, s);
+    }
+    if (e == hipSuccess && k > 1) e = launch_rewind(v, v.t_len, k - 1, s);
+  } else if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_Q4_SELF) {
+    for (int j = 1; j < k && e == hipSuccess; ++j)
+      e = fwd(r, true, v.block + j - 1, 1, v.draft_logits, v.block + j, nullptr, open, s);
+    if (e == hipSuccess && k > 1) e = launch_rewind(v, v.t_len, k - 1, s);
+  }
+  // ---- block verify
+  if (e == hipSuccess) e = fwd(r, false, v.block, k + (B ? 1 : 0), v.rows_logits, v.rows_argmax, v.rows_lse, open, s);
+  // ---- accept + trim
+  if (e == hipSuccess) e = q.mode == SPECDEC_STOCHASTIC ? launch_accept_stochastic(v, s) : launch_accept_greedy(v, s);
+  // ---- repair
+  if (e == hipSuccess && !B) {
+    e = fwd(r, false, v.repair_tok, 1, v.saved_logits, v.repair_argmax, v.repair_lse, rep, s);
+    if (e == hipSuccess) e = launch_repair_done(v, s);
+  }
+  if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL)
+    e = fwd(r, true, v.repair_tok, 1, v.draft_logits, v.draft_argmax, nullptr, rep, s);
+  return hip_status(e);
+}
+
+// Test hook: Philox4x64-10 words for n (counter, key) pairs (device arrays).
+int specdec_philox4x64(const uint64_t* d_ctr, const uint64_t* d_key, int32_t n, uint64_t* d_out, void* stream) {
+  if (!d_ctr || !d_key || !d_out || n <= 0) return SPECDEC_EINVAL;
+  return hip_status(launch_philox_words(d_ctr, d_key, n, d_out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Device-side layouts and helpers shared by the gfx950 kernels.
+//
+// Tile formats (all tiles are 1 KiB = 64 lanes x 16 bytes, the operand size
+// of one v_mfma_f32_16x16x32_bf16):
+//
+//  * Weight tile (A operand): 16 output rows x 32 inputs of a linear weight.
+//    Lane l holds 8 bf16 of row (l % 16), inputs 8*(l / 16) .. +7.  A matrix
+//    with N rows (N % 16 == 0) and K inputs (K % 32 == 0) is stored as
+//    [N/16 row groups][K/32 k-blocks][tile], so one row group streams as one
+//    contiguous run and every wave-wide 16-byte load is a contiguous 1 KiB.
+//
+//  * Activation tile (B operand): 32 inputs x 16 columns.  Column c < 8 holds
+//    the bf16 "hi" part of activation row 8*t + c, column c >= 8 its "lo"
+//    remainder (x = hi + lo to ~16 significant bits).  Lane l holds 8 bf16 of
+//    column (l % 16) at inputs 8*(l / 16) .. +7.  Layout
+//    [NT column tiles][K/32 k-blocks][tile]; row m lives in tile m / 8.
+//
+//  * MFMA result: lane l, register r holds C[4*(l/16) + r][l % 16].  The
+//    output for weight row i and activation row m is C[i][m%8] + C[i][m%8+8].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_bits;
+
+namespace sd {
+
+constexpr int kTileBytes = 1024;
+constexpr int kTileU16 = 512;       // bf16 elements per tile
+constexpr int kColsPerTile = 8;     // activation rows per column tile
+constexpr int kMaxRows = 32;        // rows per forward pass
+constexpr int kMaxNT = kMaxRows / kColsPerTile;
+
+__device__ __forceinline__ float bf2f(bf16_bits b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// float -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_bits f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_bits)((u >> 16) | 0x40u);
+  return (bf16_bits)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Position of activation (row m, input k) inside an activation tile buffer,
+// in bf16 units; the "lo" element sits 8 lanes (64 bf16) further.
+__device__ __forceinline__ size_t btile_index(int KB, int m, int k) {
+  int t = m >> 3, c = m & 7;
+  int kb = k >> 5, s = (k >> 3) & 3, e = k & 7;
+  return ((size_t)(t * KB + kb) * kTileU16) + (size_t)((s * 16 + c) * 8 + e);
+}
+
+__device__ __forceinline__ void btile_put(bf16_bits* tiles, int KB, int m, int k, float v) {
+  size_t i = btile_index(KB, m, k);
+  bf16_bits hi = f2bf(v);
+  bf16_bits lo = f2bf(v - bf2f(hi));
+  tiles[i] = hi;
+  tiles[i + 64] = lo;
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sticky device error bits.
+enum : int32_t {
+  kErrCapacity = 1,     // a forward would pass the cache capacity
+  kErrTrim = 2,         // trim above the current length
+  kErrNonFinite = 4,    // non-finite logits
+  kErrTable = 8,        // draft table / noise read past its end
+  kErrOutput = 16,      // committed-token buffer full
+};
+
+__device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+}  // namespace sd

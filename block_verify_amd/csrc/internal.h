@@ -1,0 +1,103 @@
+// Host-side internals shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/specdec.h"
+#include "device_common.h"
+
+namespace sd {
+
+struct Dims {
+  int L, H, nq, nkv, hd, F, V;
+  float theta, eps;
+  int wfmt;
+  int qdim() const { return nq * hd; }
+  int kvdim() const { return nkv * hd; }
+  int qkv_rows() const { return (nq + 2 * nkv) * hd; }
+  int group() const { return nq / nkv; }
+};
+
+int dims_from_desc(const specdec_model_desc* d, Dims* out);
+
+// Byte offsets of every packed tensor inside the weight blob.
+struct LayerOffsets {
+  size_t attn_norm, wqkv, wo, mlp_norm, wgu, wdown;
+};
+struct BlobLayout {
+  size_t embed, final_norm, lm_head, total;
+  std::vector<LayerOffsets> layer;
+};
+BlobLayout blob_layout(const Dims& d);
+
+struct LayerPtrs {
+  const float* attn_norm;
+  const float* mlp_norm;
+  const bf16x8_t* wqkv;   // tiles, RoPE-paired row groups
+  const bf16x8_t* wo;
+  const bf16x8_t* wgu;    // tiles, gate/up interleaved by 8 rows
+  const bf16x8_t* wdown;
+  // 4-bit substitute weights (weight_format == SPECDEC_W_Q4G64)
+  const uint8_t* q_wqkv;
+  const uint8_t* q_wo;
+  const uint8_t* q_wgu;
+  const uint8_t* q_wdown;
+};
+
+}  // namespace sd
+
+struct specdec_model {
+  sd::Dims d;
+  const bf16_bits* embed;
+  const float* final_norm;
+  const bf16x8_t* lm_head;
+  std::vector<sd::LayerPtrs> layers;
+};
+
+struct specdec_cache {
+  sd::Dims d;
+  bf16_bits* kv;      // [L][2][nkv][max_len][hd]
+  float2* rope;       // [max_len][hd/2] (cos, sin)
+  int32_t* d_len;
+  int max_len;
+  bf16_bits* k_layer(int l) const { return kv + (size_t)l * 2 * d.nkv * max_len * d.hd; }
+  bf16_bits* v_layer(int l) const { return k_layer(l) + (size_t)d.nkv * max_len * d.hd; }
+};
+
+namespace sd {
+
+constexpr int kAttnChunk = 64;
+
+// Workspace plan for one model.
+struct WsPlan {
+  size_t err, x, xb, ss, q, ob, hb, att_o, att_ml, lm_part, toks, logits, total;
+  int max_rows, nt, max_chunks, lm_wgs;
+};
+WsPlan ws_plan(const Dims& d, int max_rows, int max_len);
+
+// Kernel launchers (kernels_forward.hip).
+struct FwdArgs {
+  const specdec_model* m;
+  const specdec_cache* c;
+  const int32_t* tokens;
+  int rows;
+  float* logits;
+  int32_t* argmax;
+  float* lse;
+  char* ws;
+  const WsPlan* plan;
+  hipStream_t stream;
+  const int32_t* gate;   // optional device flag: when *gate == 0 every kernel returns at once
+  bool skip_head;        // prefill chunks before the last: no LM head, only the length advance
+};
+hipError_t launch_forward(const FwdArgs& a);
+hipError_t launch_pack(const Dims& d, int index, const void* src, void* blob, const BlobLayout& lay, hipStream_t s);
+hipError_t launch_trim(int32_t* d_len, int32_t new_len, const int32_t* d_base, int32_t* err, hipStream_t s);
+
+// Round kernels (kernels_round.hip).
+struct RoundDev;  // defined in api.cpp
+}  // namespace sd

@@ -1,0 +1,61 @@
+// Device-visible description of one speculative round (passed by value to
+// the round kernels) and the launchers of kernels_round.hip.
+#pragma once
+
+#include "internal.h"
+
+namespace sd {
+
+constexpr int kMaxK = SPECDEC_MAX_K;
+
+enum { kFlagOpen = 0, kFlagRepair = 1, kNumFlags = 4 };
+enum { kSnapTLen = 0, kSnapDLen = 1, kSnapArgmax = 2, kSnapLse = 3, kSnapLast = 4, kNumSnap = 8 };
+
+struct RoundDev {
+  specdec_round_state* state;
+  int32_t* flags;          // [kNumFlags]; gates of the round's forwards
+  int32_t* block;          // verify block tokens [k + 1]
+  int32_t* repair_tok;     // [1]
+  int32_t* rows_argmax;    // [k + 1]
+  float* rows_lse;         // [k + 1]
+  float* rows_logits;      // [k + 1][V]
+  float* saved_logits;     // [V] saved_next (schedule A)
+  int32_t* repair_argmax;  // [1]
+  float* repair_lse;       // [1]
+  float* q_logits;         // [k][V] noisy draft logits
+  float* q_lse;            // [k]
+  float* z;                // [V] logits of the noisy-draft steps
+  float* draft_logits;     // [V] scratch for draft-model steps
+  int32_t* draft_argmax;   // [1]
+  float* snap_logits;      // [V]
+  int32_t* snap;           // [kNumSnap]
+  float* dbg;              // [2 * kMaxK + 2] ratios / uniforms of the last stochastic round
+  int32_t* t_len;
+  int32_t* d_len;          // independent draft's cache length, or null
+  int32_t* err;
+  const int32_t* table;
+  int table_len;
+  const float* noise;
+  int noise_rows;
+  uint64_t seed;
+  int k, V, bonus, schedule, draft_source, mode, state_cap;
+};
+
+// Round scratch layout inside d_round_ws.
+struct RoundWsPlan {
+  size_t flags, block, repair_tok, rows_argmax, rows_lse, repair_argmax, repair_lse, q_lse, snap, dbg;
+  size_t rows_logits, saved_logits, q_logits, z, draft_logits, draft_argmax, snap_logits, total;
+};
+RoundWsPlan round_ws_plan(int V, int k);
+
+hipError_t launch_round_start(const RoundDev& r, hipStream_t s);
+hipError_t launch_accept_greedy(const RoundDev& r, hipStream_t s);
+hipError_t launch_repair_done(const RoundDev& r, hipStream_t s);
+hipError_t launch_rewind(const RoundDev& r, int32_t* len, int n, hipStream_t s);
+hipError_t launch_snapshot(const RoundDev& r, const int32_t* last, hipStream_t s);
+hipError_t launch_reset(const RoundDev& r, int32_t n_target, hipStream_t s);
+hipError_t launch_draft_sample(const RoundDev& r, const float* z, int j, hipStream_t s);
+hipError_t launch_accept_stochastic(const RoundDev& r, hipStream_t s);
+hipError_t launch_philox_words(const uint64_t* ctr, const uint64_t* key, int n, uint64_t* out, hipStream_t s);
+
+}  // namespace sd

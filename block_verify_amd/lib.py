@@ -1,0 +1,324 @@
+"""ctypes binding of libspecdec.so (the gfx950 block-verify path).
+
+Argument marshalling only: PyTorch provides device memory and the stream;
+every step of the path runs in the library's HIP kernels.  Importing this
+module raises if the library has not been built; nothing falls back to a
+CPU implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+from .shapes import ModelShape
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecdec.so")
+
+OK, EINVAL, ECAPACITY, ESHAPE, EHIP, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+DERR_CAPACITY, DERR_TRIM, DERR_NONFINITE, DERR_TABLE, DERR_OUTPUT = 1, 2, 4, 8, 16
+W_BF16, W_Q4G64 = 0, 1
+GREEDY, STOCHASTIC = 0, 1
+SCHEDULE_A, SCHEDULE_B = 0, 1
+DRAFT_TABLE, DRAFT_MODEL, DRAFT_NOISY_SELF, DRAFT_Q4_SELF = 0, 1, 2, 3
+MAX_ROWS = 32
+MAX_K = 16
+
+EXPORTED = [
+    "specdec_tensor_count", "specdec_weights_bytes", "specdec_weights_pack", "specdec_model_create",
+    "specdec_model_destroy", "specdec_cache_bytes", "specdec_cache_create", "specdec_cache_destroy",
+    "specdec_kv_trim", "specdec_workspace_bytes", "specdec_workspace_init", "specdec_decode_step",
+    "specdec_prefill", "specdec_round_state_bytes", "specdec_round_ws_bytes", "specdec_round_create",
+    "specdec_round_destroy", "specdec_round_prefill", "specdec_round_reset", "specdec_verify_round",
+    "specdec_check", "specdec_last_hip_error", "specdec_status_str", "specdec_philox4x64",
+]
+
+
+class SpecdecError(RuntimeError):
+    pass
+
+
+class ModelDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("vocab", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
+                ("weight_format", C.c_int32)]
+
+
+class RoundState(C.Structure):
+    _fields_ = [("n_committed", C.c_int32), ("round", C.c_int32), ("m_last", C.c_int32),
+                ("last_tok", C.c_int32), ("saved_argmax", C.c_int32), ("saved_lse", C.c_float),
+                ("accepted_total", C.c_int32), ("cap", C.c_int32), ("n_target", C.c_int32),
+                ("reserved", C.c_int32 * 7)]
+
+
+class RoundDesc(C.Structure):
+    _fields_ = [("target", C.c_void_p), ("target_cache", C.c_void_p), ("draft", C.c_void_p),
+                ("draft_cache", C.c_void_p), ("k", C.c_int32), ("mode", C.c_int32), ("bonus", C.c_int32),
+                ("schedule", C.c_int32), ("draft_source", C.c_int32), ("d_draft_table", C.c_void_p),
+                ("table_len", C.c_int32), ("d_noise", C.c_void_p), ("noise_rows", C.c_int32),
+                ("philox_seed", C.c_uint64), ("d_state", C.c_void_p), ("d_ws", C.c_void_p),
+                ("ws_bytes", C.c_size_t), ("d_draft_ws", C.c_void_p), ("draft_ws_bytes", C.c_size_t),
+                ("d_round_ws", C.c_void_p), ("round_ws_bytes", C.c_size_t), ("state_cap", C.c_int32)]
+
+
+def load_library(path: str = _LIB_PATH) -> C.CDLL:
+    if not os.path.exists(path):
+        raise SpecdecError(f"{path} is missing: build it with `python -m block_verify_amd.build`")
+    lib = C.CDLL(path)
+    vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    P = C.POINTER
+    sig = {
+        "specdec_tensor_count": (i32, [P(ModelDesc)]),
+        "specdec_weights_bytes": (C.c_int, [P(ModelDesc), P(sz)]),
+        "specdec_weights_pack": (C.c_int, [P(ModelDesc), i32, vp, vp, vp]),
+        "specdec_model_create": (C.c_int, [P(ModelDesc), vp, vp, P(vp)]),
+        "specdec_model_destroy": (None, [vp]),
+        "specdec_cache_bytes": (C.c_int, [P(ModelDesc), i32, P(sz)]),
+        "specdec_cache_create": (C.c_int, [P(ModelDesc), vp, sz, i32, vp, P(vp)]),
+        "specdec_cache_destroy": (None, [vp]),
+        "specdec_kv_trim": (C.c_int, [vp, i32, vp, vp]),
+        "specdec_workspace_bytes": (C.c_int, [P(ModelDesc), i32, i32, P(sz)]),
+        "specdec_workspace_init": (C.c_int, [vp, sz, vp]),
+        "specdec_decode_step": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+        "specdec_prefill": (C.c_int, [vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "specdec_round_state_bytes": (C.c_int, [i32, P(sz)]),
+        "specdec_round_ws_bytes": (C.c_int, [P(ModelDesc), i32, P(sz)]),
+        "specdec_round_create": (C.c_int, [P(RoundDesc), P(vp)]),
+        "specdec_round_destroy": (None, [vp]),
+        "specdec_round_prefill": (C.c_int, [vp, vp, i32, i32, vp]),
+        "specdec_round_reset": (C.c_int, [vp, i32, vp]),
+        "specdec_verify_round": (C.c_int, [vp, vp]),
+        "specdec_check": (C.c_int, [vp, P(i32), vp]),
+        "specdec_last_hip_error": (i32, []),
+        "specdec_status_str": (C.c_char_p, [C.c_int]),
+        "specdec_philox4x64": (C.c_int, [vp, vp, i32, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = load_library()
+    return _lib
+
+
+def check(rc: int, what: str = "") -> None:
+    if rc != OK:
+        msg = lib().specdec_status_str(rc).decode()
+        extra = f" (hipError {lib().specdec_last_hip_error()})" if rc == EHIP else ""
+        raise SpecdecError(f"{what}: {msg} [{rc}]{extra}")
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def desc_of(shape: ModelShape, weight_format: int = W_BF16) -> ModelDesc:
+    return ModelDesc(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                     shape.ffn, shape.vocab, shape.rope_theta, shape.rms_eps, weight_format)
+
+
+def _dev_bytes(n: int, device) -> torch.Tensor:
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+class Model:
+    """Packed bf16 decoder weights on the device + the library's model handle."""
+
+    def __init__(self, shape: ModelShape, tensors, device="cuda", stream=None):
+        self.shape = shape
+        self.desc = desc_of(shape)
+        L = lib()
+        nbytes = C.c_size_t()
+        check(L.specdec_weights_bytes(C.byref(self.desc), C.byref(nbytes)), "weights_bytes")
+        self.blob = _dev_bytes(nbytes.value, device)
+        s = _stream(stream)
+        for i, t in enumerate(tensors):
+            src = torch.from_numpy(np.ascontiguousarray(t).view(np.int16)).to(device)
+            check(L.specdec_weights_pack(C.byref(self.desc), i, src.data_ptr(), self.blob.data_ptr(), s), f"pack {i}")
+            torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+            del src
+        h = C.c_void_p()
+        check(L.specdec_model_create(C.byref(self.desc), self.blob.data_ptr(), None, C.byref(h)), "model_create")
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.specdec_model_destroy(self.handle)
+            self.handle = None
+
+
+class Cache:
+    """KV cache of max_len positions; the length lives in device memory."""
+
+    def __init__(self, shape: ModelShape, max_len: int, device="cuda"):
+        L = lib()
+        self.shape = shape
+        self.desc = desc_of(shape)
+        self.max_len = max_len
+        nbytes = C.c_size_t()
+        check(L.specdec_cache_bytes(C.byref(self.desc), max_len, C.byref(nbytes)), "cache_bytes")
+        self.mem = _dev_bytes(nbytes.value, device)
+        self.len = torch.zeros(1, dtype=torch.int32, device=device)
+        h = C.c_void_p()
+        check(L.specdec_cache_create(C.byref(self.desc), self.mem.data_ptr(), nbytes.value, max_len,
+                                     self.len.data_ptr(), C.byref(h)), "cache_create")
+        self.handle = h
+
+    def length(self) -> int:
+        return int(self.len.item())
+
+    def kv(self) -> torch.Tensor:
+        """bf16 bit view [L][2][n_kv][max_len][hd] (int16) of the cache."""
+        sh = self.shape
+        n = sh.n_layers * 2 * sh.n_kv_heads * self.max_len * sh.head_dim
+        return self.mem[: 2 * n].view(torch.int16).view(sh.n_layers, 2, sh.n_kv_heads, self.max_len, sh.head_dim)
+
+    def trim(self, new_len: int, ws: "Workspace", stream=None) -> None:
+        check(lib().specdec_kv_trim(self.handle, new_len, ws.mem.data_ptr(), _stream(stream)), "kv_trim")
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.specdec_cache_destroy(self.handle)
+            self.handle = None
+
+
+class Workspace:
+    def __init__(self, shape: ModelShape, max_len: int, max_rows: int = MAX_ROWS, device="cuda"):
+        L = lib()
+        nbytes = C.c_size_t()
+        d = desc_of(shape)
+        check(L.specdec_workspace_bytes(C.byref(d), max_rows, max_len, C.byref(nbytes)), "workspace_bytes")
+        self.nbytes = nbytes.value
+        self.mem = _dev_bytes(self.nbytes, device)
+        check(L.specdec_workspace_init(self.mem.data_ptr(), self.nbytes, _stream(None)), "workspace_init")
+
+    def error_bits(self, stream=None) -> int:
+        bits = C.c_int32()
+        lib().specdec_check(self.mem.data_ptr(), C.byref(bits), _stream(stream))
+        return bits.value
+
+
+def decode_step(model: Model, cache: Cache, tokens: torch.Tensor, ws: Workspace, logits=None, argmax=None,
+                lse=None, rows=None, stream=None) -> None:
+    rows = int(tokens.numel()) if rows is None else rows
+    check(lib().specdec_decode_step(model.handle, cache.handle, tokens.data_ptr(), rows, _ptr(logits),
+                                    _ptr(argmax), _ptr(lse), ws.mem.data_ptr(), ws.nbytes, _stream(stream)),
+          "decode_step")
+
+
+def prefill(model: Model, cache: Cache, tokens: torch.Tensor, ws: Workspace, chunk: int = MAX_ROWS,
+            logits=None, argmax=None, lse=None, stream=None) -> None:
+    check(lib().specdec_prefill(model.handle, cache.handle, tokens.data_ptr(), int(tokens.numel()), chunk,
+                                _ptr(logits), _ptr(argmax), _ptr(lse), ws.mem.data_ptr(), ws.nbytes,
+                                _stream(stream)), "prefill")
+
+
+def philox4x64(counters: np.ndarray, keys: np.ndarray, device="cuda") -> np.ndarray:
+    n = counters.shape[0]
+    c = torch.from_numpy(counters.astype(np.uint64).view(np.int64)).to(device)
+    k = torch.from_numpy(keys.astype(np.uint64).view(np.int64)).to(device)
+    out = torch.empty((n, 4), dtype=torch.int64, device=device)
+    check(lib().specdec_philox4x64(c.data_ptr(), k.data_ptr(), n, out.data_ptr(), _stream(None)), "philox")
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint64)
+
+
+class Round:
+    """One speculative decoding job: caches, state and the round handle."""
+
+    def __init__(self, target: Model, k: int, *, mode=GREEDY, bonus=True, schedule=SCHEDULE_A,
+                 draft_source=DRAFT_TABLE, table: np.ndarray | None = None, draft: Model | None = None,
+                 noise: np.ndarray | None = None, seed: int = 3, max_len: int, cap: int = 1024, device="cuda"):
+        L = lib()
+        self.target, self.draft, self.k = target, draft, k
+        self.schedule, self.mode, self.draft_source = schedule, mode, draft_source
+        sh = target.shape
+        self.tcache = Cache(sh, max_len, device)
+        self.ws = Workspace(sh, max_len, device=device)
+        self.dcache = self.dws = None
+        if draft_source == DRAFT_MODEL:
+            self.dcache = Cache(draft.shape, max_len, device)
+            self.dws = Workspace(draft.shape, max_len, device=device)
+        nb = C.c_size_t()
+        check(L.specdec_round_state_bytes(cap, C.byref(nb)), "state_bytes")
+        self.state = _dev_bytes(nb.value, device)
+        self.state.zero_()
+        check(L.specdec_round_ws_bytes(C.byref(target.desc), k, C.byref(nb)), "round_ws_bytes")
+        self.rws = _dev_bytes(nb.value, device)
+        self.rws.zero_()
+        self.table = torch.from_numpy(np.asarray(table, np.int32)).to(device) if table is not None else None
+        self.noise = torch.from_numpy(np.ascontiguousarray(noise, np.float32)).to(device) if noise is not None else None
+        d = RoundDesc()
+        d.target, d.target_cache = target.handle, self.tcache.handle
+        d.draft = draft.handle if draft is not None else None
+        d.draft_cache = self.dcache.handle if self.dcache is not None else None
+        d.k, d.mode, d.bonus, d.schedule, d.draft_source = k, mode, 1 if bonus else 0, schedule, draft_source
+        d.d_draft_table = _ptr(self.table)
+        d.table_len = int(self.table.numel()) if self.table is not None else 0
+        d.d_noise = _ptr(self.noise)
+        d.noise_rows = int(self.noise.shape[0]) if self.noise is not None else 0
+        d.philox_seed = seed
+        d.d_state = self.state.data_ptr()
+        d.d_ws, d.ws_bytes = self.ws.mem.data_ptr(), self.ws.nbytes
+        if self.dws is not None:
+            d.d_draft_ws, d.draft_ws_bytes = self.dws.mem.data_ptr(), self.dws.nbytes
+        d.d_round_ws, d.round_ws_bytes = self.rws.data_ptr(), self.rws.numel()
+        d.state_cap = cap
+        self.desc = d
+        h = C.c_void_p()
+        check(L.specdec_round_create(C.byref(d), C.byref(h)), "round_create")
+        self.handle = h
+        self.cap = cap
+
+    def prefill(self, prompt: np.ndarray, chunk: int = MAX_ROWS, stream=None) -> None:
+        self.prompt = torch.from_numpy(np.asarray(prompt, np.int32)).to(self.state.device)
+        check(lib().specdec_round_prefill(self.handle, self.prompt.data_ptr(), int(self.prompt.numel()), chunk,
+                                          _stream(stream)), "round_prefill")
+
+    def reset(self, n_target: int, stream=None) -> None:
+        check(lib().specdec_round_reset(self.handle, n_target, _stream(stream)), "round_reset")
+
+    def step(self, stream=None) -> None:
+        check(lib().specdec_verify_round(self.handle, _stream(stream)), "verify_round")
+
+    def read_state(self):
+        raw = self.state.cpu().numpy()
+        st = RoundState.from_buffer_copy(raw[:C.sizeof(RoundState)].tobytes())
+        toks = raw[C.sizeof(RoundState):].view(np.int32)
+        return st, toks[: min(st.n_committed, self.cap)].copy()
+
+    def run(self, n_new: int, stream=None, max_rounds: int = 100000):
+        """Reset to the post-prefill state and run rounds until n_new tokens are committed."""
+        self.reset(n_new, stream)
+        rounds = 0
+        while rounds < max_rounds:
+            self.step(stream)
+            rounds += 1
+            st, _ = self.read_state()
+            if st.n_committed >= n_new:
+                break
+        return self.read_state()
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.specdec_round_destroy(self.handle)
+            self.handle = None

@@ -1,0 +1,256 @@
+/* specdec.h - C ABI of the MI355X (gfx950) block-verify speculative decoding path.
+ *
+ * What the path computes is defined by these pages:
+ *  - "SpecDec-Context-Scaling 项目解读" (richardf123.github.io): section 2.2 (a
+ *    self-built forward serving prefill, decode and block verification; an
+ *    independent KV-cache API with trim and repair for the target and draft
+ *    caches), section 3 (the greedy round: k drafts, one block forward,
+ *    longest-prefix acceptance, replacement, bonus), section 3.1 (row
+ *    alignment: saved_next verifies d_1, rows[j-1] verifies d_(j+1)),
+ *    section 3.2 (cache length == committed tokens; trim to t+m, then repair
+ *    to t+m+1), section 2.1 (chunked prefill).
+ *  - the wmrh.cn speculative-decoding explainer, section 2.2, and
+ *    "mini-infer系统实战-13" (smarter.xin), modified rejection sampling section
+ *    (accept with min(1, p/q), resample from norm(max(0, p-q)), bonus on full
+ *    acceptance).
+ *  - "SubSpec" summary (jjl357.github.io), sections 4.1.1-4.1.3 (4-bit group-64
+ *    substitute draft sharing embedding, LM head and the KV cache).
+ *
+ * Conventions for every entry point:
+ *  - Pointers prefixed d_ are device pointers (hipMalloc or a framework's
+ *    device allocation).  The caller owns every buffer; the library keeps
+ *    non-owning references inside its handles and never frees them.  Buffers
+ *    must outlive the handles that reference them.
+ *  - After the *_create calls the library performs no device allocation.
+ *  - `stream` is a hipStream_t passed as void*.  Calls enqueue work on it and
+ *    return without synchronising unless stated.
+ *  - Return value: SPECDEC_OK (0) or a negative specdec_status.  Errors that
+ *    can be decided from host-visible values are returned synchronously and
+ *    nothing is enqueued.  Violations only the device can see (a trim above
+ *    the current length, a forward past the cache capacity, a draft table
+ *    read past its end, non-finite logits) set bits of a sticky device error
+ *    word (the SPECDEC_DERR_* bits) instead of faulting; the affected writes
+ *    are skipped.  specdec_check() reads and reports that word.
+ *  - The library never aborts, exits or prints.
+ *  - Handles are not thread-safe; use one stream per handle set.  Results
+ *    are bitwise deterministic for fixed inputs, and a row's results do not
+ *    depend on how many rows share its forward pass.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPECDEC_OK = 0,
+  SPECDEC_EINVAL = -1,      /* NULL pointer, bad enum, bad size */
+  SPECDEC_ECAPACITY = -2,   /* rows / length beyond what the buffers were sized for */
+  SPECDEC_ESHAPE = -3,      /* model dimensions the kernels do not support */
+  SPECDEC_EHIP = -4,        /* a HIP runtime call failed (see specdec_last_hip_error) */
+  SPECDEC_EDEVICE = -5,     /* the sticky device error word is non-zero */
+  SPECDEC_EUNSUPPORTED = -6 /* valid request this build does not implement */
+} specdec_status;
+
+/* Bits of the sticky device error word. */
+enum {
+  SPECDEC_DERR_CAPACITY = 1,   /* a forward would pass the cache capacity (writes skipped) */
+  SPECDEC_DERR_TRIM = 2,       /* trim above the current length (length unchanged) */
+  SPECDEC_DERR_NONFINITE = 4,  /* non-finite logits */
+  SPECDEC_DERR_TABLE = 8,      /* draft table or noise read past its end */
+  SPECDEC_DERR_OUTPUT = 16     /* committed-token buffer full (tokens dropped) */
+};
+
+enum { SPECDEC_W_BF16 = 0, SPECDEC_W_Q4G64 = 1 };
+enum { SPECDEC_GREEDY = 0, SPECDEC_STOCHASTIC = 1 };
+enum { SPECDEC_SCHEDULE_A = 0, SPECDEC_SCHEDULE_B = 1 };
+enum { SPECDEC_DRAFT_TABLE = 0, SPECDEC_DRAFT_MODEL = 1, SPECDEC_DRAFT_NOISY_SELF = 2, SPECDEC_DRAFT_Q4_SELF = 3 };
+
+/* Largest number of rows one forward pass takes (prefill runs in passes of
+ * at most this many rows). */
+#define SPECDEC_MAX_ROWS 32
+/* Largest number of drafts per round. */
+#define SPECDEC_MAX_K 16
+
+/* Decoder dimensions.  Pre-norm RMSNorm decoder with rotate-half RoPE,
+ * grouped-query attention (query head h reads kv head h / (n_q/n_kv)),
+ * SwiGLU MLP, untied LM head, no biases.  Supported: hidden, q_dim and ffn
+ * multiples of 32 (64 for q4), head_dim 64 or 128, n_q a multiple of n_kv,
+ * n_q / n_kv <= 8, vocab a multiple of 16. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rope_theta, rms_eps;
+  int32_t weight_format; /* SPECDEC_W_BF16, or SPECDEC_W_Q4G64 for 4-bit linears */
+} specdec_model_desc;
+
+typedef struct specdec_model specdec_model;
+typedef struct specdec_cache specdec_cache;
+typedef struct specdec_round specdec_round;
+
+/* ---------------------------------------------------------------- weights */
+
+/* Canonical tensor order, index i: 0 embed [V][H]; per layer l the indices
+ * 1+9l .. 9+9l are attn_norm [H], wq [n_q*hd][H], wk [n_kv*hd][H],
+ * wv [n_kv*hd][H], wo [H][n_q*hd], mlp_norm [H], wgate [F][H], wup [F][H],
+ * wdown [H][F]; then final_norm [H], lm_head [V][H].  Linear weights are
+ * [out][in] row-major. */
+int32_t specdec_tensor_count(const specdec_model_desc* desc);
+
+/* Bytes of the packed weight blob (the library's own HBM layout: MFMA-tile
+ * ordered linears, fp32 norm gains, row-major bf16 embedding). */
+int specdec_weights_bytes(const specdec_model_desc* desc, size_t* bytes);
+
+/* Pack canonical tensor `index` into the blob on `stream`.
+ * BF16 models: d_src is the row-major bf16 tensor (device memory).
+ * Q4G64 models: for linear tensors other than lm_head, d_src points to the
+ * packed codes uint8 [out][in/2] (even input in the low nibble) immediately
+ * followed by fp16 scale [out][in/64] and fp16 zero [out][in/64] (weight =
+ * (code - zero) * scale); other tensors are bf16 as above.  d_src may be
+ * freed after the stream has passed this call. */
+int specdec_weights_pack(const specdec_model_desc* desc, int32_t index, const void* d_src,
+                         void* d_blob, void* stream);
+
+/* Model handle over a packed blob.  `share` (may be NULL) names a model whose
+ * embedding, final norm and LM head this one uses instead of its own (the
+ * substitute draft); then those tensors need not be packed here. */
+int specdec_model_create(const specdec_model_desc* desc, const void* d_blob, const specdec_model* share,
+                         specdec_model** out);
+void specdec_model_destroy(specdec_model* m);
+
+/* ------------------------------------------------------------------ cache */
+
+/* Bytes of a KV cache of `max_len` positions: bf16 K and V
+ * [layer][K|V][kv head][max_len][head_dim] plus the RoPE table. */
+int specdec_cache_bytes(const specdec_model_desc* desc, int32_t max_len, size_t* bytes);
+
+/* Cache handle over `d_mem` (cache_bytes).  `d_len` is a caller-owned
+ * device int32 holding the current length (committed positions); the
+ * library reads and updates it on the device only.  This call writes the
+ * RoPE table (synchronous copy) and sets *d_len = 0. */
+int specdec_cache_create(const specdec_model_desc* desc, void* d_mem, size_t bytes, int32_t max_len,
+                         int32_t* d_len, specdec_cache** out);
+void specdec_cache_destroy(specdec_cache* c);
+
+/* Trim the cache to new_len positions (device-checked: new_len <= length,
+ * else SPECDEC_DERR_TRIM and the length is left as is).  No data moves. */
+int specdec_kv_trim(specdec_cache* c, int32_t new_len, int32_t* d_err, void* stream);
+
+/* -------------------------------------------------------------- workspace */
+
+/* Bytes of the scratch workspace one forward pass needs for up to max_rows
+ * rows against a cache of max_len positions.  The workspace also holds the
+ * sticky device error word at offset 0 (int32). */
+int specdec_workspace_bytes(const specdec_model_desc* desc, int32_t max_rows, int32_t max_len, size_t* bytes);
+
+/* Zero the workspace header (error word) on `stream`. */
+int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------- forwards */
+
+/* One forward pass of `rows` tokens (1..SPECDEC_MAX_ROWS) at positions
+ * length .. length+rows-1: appends their K/V, then length += rows.
+ * d_tokens int32 [rows] (device).  Outputs (any may be NULL): d_logits fp32
+ * [rows][vocab], d_argmax int32 [rows] (lowest index on ties), d_lse fp32
+ * [rows] (log-sum-exp of the row).  This is the decode step (rows = 1) and
+ * the block verify (rows = k or k+1). */
+int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t rows,
+                        float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
+                        void* stream);
+
+/* Prefill `n` tokens in passes of `chunk` rows (chunk clipped to
+ * SPECDEC_MAX_ROWS), starting at the current length.  Writes the last row's
+ * logits / argmax / lse (any may be NULL). */
+int specdec_prefill(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t n, int32_t chunk,
+                    float* d_last_logits, int32_t* d_last_argmax, float* d_last_lse, void* d_ws,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ round */
+
+/* Device-resident round state, followed in memory by int32 tokens[cap]
+ * (the committed tokens in order). */
+typedef struct {
+  int32_t n_committed;     /* tokens committed so far */
+  int32_t round;           /* rounds run */
+  int32_t m_last;          /* drafts accepted in the last round */
+  int32_t last_tok;        /* last committed token (repaired under A, pending under B) */
+  int32_t saved_argmax;    /* argmax of saved_next (schedule A) */
+  float saved_lse;         /* log-sum-exp of saved_next (schedule A) */
+  int32_t accepted_total;  /* sum of m over rounds */
+  int32_t cap;             /* capacity of the token array */
+  int32_t n_target;        /* rounds become no-ops once n_committed >= n_target */
+  int32_t reserved[7];
+} specdec_round_state;
+
+typedef struct {
+  const specdec_model* target;
+  specdec_cache* target_cache;
+  const specdec_model* draft;   /* DRAFT_MODEL: independent draft; DRAFT_Q4_SELF: substitute draft; else NULL */
+  specdec_cache* draft_cache;   /* DRAFT_MODEL only (own cache); NULL otherwise */
+  int32_t k;                    /* drafts per round, 1..SPECDEC_MAX_K (DRAFT_Q4_SELF: the depth D) */
+  int32_t mode;                 /* SPECDEC_GREEDY | SPECDEC_STOCHASTIC */
+  int32_t bonus;                /* 1: bonus token on full acceptance */
+  int32_t schedule;             /* SPECDEC_SCHEDULE_A | SPECDEC_SCHEDULE_B */
+  int32_t draft_source;         /* SPECDEC_DRAFT_* */
+  const int32_t* d_draft_table; /* TABLE / MODEL: drafts by generated index, int32 [table_len] */
+  int32_t table_len;
+  const float* d_noise;         /* NOISY_SELF: fp32 [noise_rows][vocab] logit noise by generated index */
+  int32_t noise_rows;
+  uint64_t philox_seed;         /* STOCHASTIC: Philox4x64-10 key word 0 */
+  specdec_round_state* d_state; /* device state + tokens (specdec_round_state_bytes) */
+  void* d_ws;                   /* target workspace (rows >= k+1) */
+  size_t ws_bytes;
+  void* d_draft_ws;             /* draft workspace (DRAFT_MODEL, DRAFT_Q4_SELF) */
+  size_t draft_ws_bytes;
+  void* d_round_ws;             /* round scratch (specdec_round_ws_bytes) */
+  size_t round_ws_bytes;
+  int32_t state_cap;            /* capacity of the state's token array (specdec_round_state_bytes(cap)) */
+} specdec_round_desc;
+
+int specdec_round_state_bytes(int32_t cap, size_t* bytes);
+int specdec_round_ws_bytes(const specdec_model_desc* target, int32_t k, size_t* bytes);
+
+/* Validate the descriptor and build a round handle (host memory only). */
+int specdec_round_create(const specdec_round_desc* desc, specdec_round** out);
+void specdec_round_destroy(specdec_round* r);
+
+/* Prefill `d_prompt` (int32 [n], device) into the round's caches in passes
+ * of `chunk` rows and snapshot the post-prefill state.  The caches are
+ * first trimmed to 0.  Schedule A prefills all n tokens into the target and
+ * keeps the last row as saved_next; schedule B prefills n-1 tokens and
+ * leaves prompt[n-1] pending.  An independent draft model prefills all n. */
+int specdec_round_prefill(specdec_round* r, const int32_t* d_prompt, int32_t n, int32_t chunk, void* stream);
+
+/* Return to the post-prefill snapshot: trim every cache back to its
+ * post-prefill length, restore saved_next / the pending token, zero the
+ * counters and set n_target (rounds stop committing once n_committed >=
+ * n_target).  Enqueued on `stream`; cheap (no forward). */
+int specdec_round_reset(specdec_round* r, int32_t n_target, void* stream);
+
+/* Enqueue one speculative round: draft provision, block verify, acceptance,
+ * trim of every cache to t+m and repair to t+m+1 (schedule A) or the
+ * pending-token form (schedule B).  No host synchronisation; once
+ * n_committed >= n_target the round's kernels return without work. */
+int specdec_verify_round(specdec_round* r, void* stream);
+
+/* Read the device error word of `d_ws` (synchronises `stream`): returns
+ * SPECDEC_OK or SPECDEC_EDEVICE and stores the bits in *bits (may be NULL). */
+int specdec_check(const void* d_ws, int32_t* bits, void* stream);
+
+/* The last hipError_t seen by a failing call on this thread. */
+int32_t specdec_last_hip_error(void);
+
+/* Philox4x64-10 output words for n (counter[4], key[2]) pairs: device
+ * arrays ctr uint64 [n][4], key uint64 [n][2], out uint64 [n][4].  The same
+ * generator draws the stochastic round's uniforms. */
+int specdec_philox4x64(const uint64_t* d_ctr, const uint64_t* d_key, int32_t n, uint64_t* d_out, void* stream);
+const char* specdec_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H */

@@ -1,0 +1,60 @@
+"""The C-ABI library loads on the host and exports every function include/specdec.h declares."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specdec.h")
+LIB = os.path.join(ROOT, "block_verify_amd", "libspecdec.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(specdec_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = _declared()
+    for n in ("specdec_prefill", "specdec_decode_step", "specdec_verify_round", "specdec_kv_trim"):
+        assert n in names
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_binding_covers_every_declared_symbol():
+    from block_verify_amd import lib as binding
+    assert sorted(binding.EXPORTED) == _declared()
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_host_validation_without_gpu():
+    """Argument checks that need no device: sizes, bad shapes, status strings."""
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import QWEN_1_5B, TINY
+    L = b.lib()
+    d = b.desc_of(QWEN_1_5B)
+    n = ctypes.c_size_t()
+    assert L.specdec_weights_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value >= QWEN_1_5B.weight_bytes_bf16()
+    assert L.specdec_tensor_count(ctypes.byref(d)) == len(QWEN_1_5B.tensor_specs())
+    assert L.specdec_workspace_bytes(ctypes.byref(d), 33, 4096, ctypes.byref(n)) == b.ECAPACITY
+    bad = b.desc_of(TINY)
+    bad.head_dim = 96
+    assert L.specdec_weights_bytes(ctypes.byref(bad), ctypes.byref(n)) == b.ESHAPE
+    bad = b.desc_of(TINY)
+    bad.n_q_heads = 3
+    assert L.specdec_weights_bytes(ctypes.byref(bad), ctypes.byref(n)) == b.ESHAPE
+    assert L.specdec_cache_bytes(ctypes.byref(b.desc_of(TINY)), 0, ctypes.byref(n)) == b.EINVAL
+    assert L.specdec_decode_step(None, None, None, 1, None, None, None, None, 0, None) == b.EINVAL
+    assert L.specdec_round_create(None, None) == b.EINVAL
+    assert L.specdec_status_str(b.EDEVICE) == b"device error flag set"
+    assert L.specdec_round_state_bytes(64, ctypes.byref(n)) == 0 and n.value == 64 + 64 * 4

@@ -1,0 +1,231 @@
+"""GPU parity on the tiny decoder: forward, cache, batch invariance, rounds, errors.
+
+Every case calls the HIP path through the C ABI (block_verify_amd.lib) and
+compares with the CPU oracle on the same seeded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (assert_logits_close, bf16_bits_to_f64, say, to_np, tokens_match_teacher_forced)
+
+pytestmark = pytest.mark.gpu
+
+P, N_NEW, K = 128, 16, 4
+
+
+@pytest.fixture(scope="module")
+def env():
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import TINY, SEED_TARGET
+    from block_verify_amd.synth import make_prompt, make_weights
+    from oracle.model import OracleWeights
+    say("tiny: building model")
+    w = make_weights(TINY, SEED_TARGET)
+    model = b.Model(TINY, w)
+    prompt = make_prompt(TINY.vocab, P)
+    return dict(b=b, shape=TINY, w=w, model=model, prompt=prompt, ow=OracleWeights(TINY, w))
+
+
+def _fresh(env, max_len=512):
+    b = env["b"]
+    cache = b.Cache(env["shape"], max_len)
+    ws = b.Workspace(env["shape"], max_len)
+    return cache, ws
+
+
+def _gpu_prefill(env, cache, ws, tokens, chunk=32):
+    b = env["b"]
+    V = env["shape"].vocab
+    t = torch.from_numpy(np.asarray(tokens, np.int32)).cuda()
+    logits = torch.empty(V, dtype=torch.float32, device="cuda")
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    lse = torch.empty(1, dtype=torch.float32, device="cuda")
+    b.prefill(env["model"], cache, t, ws, chunk=chunk, logits=logits, argmax=am, lse=lse)
+    return to_np(logits), int(to_np(am)[0]), float(to_np(lse)[0])
+
+
+def _gpu_forward(env, cache, ws, tokens):
+    b = env["b"]
+    V = env["shape"].vocab
+    M = len(tokens)
+    t = torch.from_numpy(np.asarray(tokens, np.int32)).cuda()
+    logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    am = torch.empty(M, dtype=torch.int32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    b.decode_step(env["model"], cache, t, ws, logits=logits, argmax=am, lse=lse)
+    return to_np(logits), to_np(am), to_np(lse)
+
+
+@pytest.mark.parametrize("chunk", [32, 7])
+def test_prefill_logits_and_cache(env, chunk):
+    from oracle.model import OracleCache, prefill
+    say(f"tiny prefill chunk={chunk}")
+    cache, ws = _fresh(env)
+    logits, am, lse = _gpu_prefill(env, cache, ws, env["prompt"], chunk=chunk)
+    assert cache.length() == P
+    oc = OracleCache(env["shape"], 512)
+    ol = prefill(env["ow"], oc, env["prompt"])
+    assert_logits_close(logits, ol, "prefill logits")
+    assert am == int(np.argmax(logits))
+    ref_lse = np.log(np.sum(np.exp(logits.astype(np.float64) - logits.max()))) + logits.max()
+    assert abs(lse - ref_lse) < 1e-4
+    kv = to_np(cache.kv())
+    for l in range(env["shape"].n_layers):
+        gk = bf16_bits_to_f64(kv[l, 0, :, :P])
+        gv = bf16_bits_to_f64(kv[l, 1, :, :P])
+        for g, o, nm in ((gk, oc.k[l][:, :P], "K"), (gv, oc.v[l][:, :P], "V")):
+            scale = np.abs(o).max()
+            err = np.abs(g - o).max()
+            say(f"layer {l} {nm}: max err {err:.3e} (scale {scale:.3f})")
+            assert err <= 1e-2 * scale
+    assert ws.error_bits() == 0
+
+
+@pytest.mark.parametrize("rows", [1, 2, 4, 5, 8, 9, 16, 17, 32])
+def test_block_forward_rows(env, rows):
+    from oracle.model import OracleCache, forward, prefill
+    say(f"tiny forward rows={rows}")
+    cache, ws = _fresh(env)
+    _gpu_prefill(env, cache, ws, env["prompt"])
+    toks = np.random.default_rng(rows).integers(0, env["shape"].vocab, rows)
+    logits, am, lse = _gpu_forward(env, cache, ws, toks)
+    assert cache.length() == P + rows
+    oc = OracleCache(env["shape"], 512)
+    prefill(env["ow"], oc, env["prompt"])
+    ol = forward(env["ow"], oc, toks)
+    assert_logits_close(logits, ol, f"rows={rows}")
+    assert np.array_equal(am, logits.argmax(axis=1))
+    assert ws.error_bits() == 0
+
+
+def test_batch_invariance_block_equals_single_steps(env):
+    """Rows of an M=5 block equal five M=1 steps bit for bit (logits and cache)."""
+    toks = np.array([5, 77, 4095, 0, 1234])
+    c1, w1 = _fresh(env)
+    c2, w2 = _fresh(env)
+    _gpu_prefill(env, c1, w1, env["prompt"])
+    _gpu_prefill(env, c2, w2, env["prompt"])
+    lb, ab, sb = _gpu_forward(env, c1, w1, toks)
+    singles = [_gpu_forward(env, c2, w2, toks[i:i + 1]) for i in range(5)]
+    ls = np.concatenate([s[0] for s in singles])
+    assert np.array_equal(lb.view(np.uint32), ls.view(np.uint32))
+    assert np.array_equal(to_np(c1.kv()), to_np(c2.kv()))
+    # prefill in different chunkings gives the same cache bits too
+    c3, w3 = _fresh(env)
+    _gpu_prefill(env, c3, w3, env["prompt"], chunk=13)
+    kv1 = to_np(c1.kv())[:, :, :, :P]
+    kv3 = to_np(c3.kv())[:, :, :, :P]
+    assert np.array_equal(kv1, kv3)
+
+
+def _gpu_ar(env, n, max_len=512):
+    """Greedy AR on the GPU: each step's argmax feeds the next step (device only)."""
+    b = env["b"]
+    cache, ws = _fresh(env, max_len)
+    V = env["shape"].vocab
+    toks = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    pt = torch.from_numpy(np.asarray(env["prompt"], np.int32)).cuda()
+    logits = torch.empty(V, dtype=torch.float32, device="cuda")
+    b.prefill(env["model"], cache, pt, ws, logits=logits, argmax=toks[0:1])
+    scratch = torch.empty(V, dtype=torch.float32, device="cuda")
+    for i in range(n - 1):
+        b.decode_step(env["model"], cache, toks[i:i + 1], ws, logits=scratch, argmax=toks[i + 1:i + 2])
+    return [int(x) for x in to_np(toks)[:n]]
+
+
+@pytest.fixture(scope="module")
+def gpu_ar(env):
+    return _gpu_ar(env, N_NEW + K + 1)
+
+
+def test_gpu_ar_matches_oracle_teacher_forced(env, gpu_ar):
+    from oracle.model import full_recompute_logits
+    seq = list(env["prompt"]) + gpu_ar
+    ol = full_recompute_logits(env["ow"], seq)
+    rows = ol[P - 1:P - 1 + len(gpu_ar)]
+    exempt = tokens_match_teacher_forced(gpu_ar, rows)
+    say(f"tiny AR: {len(gpu_ar)} tokens, {exempt} exempt by the top-2 margin rule")
+
+
+@pytest.mark.parametrize("schedule", [0, 1])
+@pytest.mark.parametrize("c", [0.0, 0.4, 1.0])
+def test_spec_rounds_equal_gpu_ar(env, gpu_ar, schedule, c):
+    from block_verify_amd.synth import make_draft_table
+    b = env["b"]
+    table = make_draft_table(np.array(gpu_ar), env["shape"].vocab, c)
+    r = b.Round(env["model"], K, schedule=schedule, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    for rep in range(2):
+        st, toks = r.run(N_NEW)
+        assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+        # the invariant: cache length == prompt + committed (minus the pending token under B)
+        assert r.tcache.length() == P + st.n_committed - (1 if schedule == 1 else 0)
+        assert r.ws.error_bits() == 0
+    say(f"schedule {'AB'[schedule]} c={c}: rounds {st.round} accepted {st.accepted_total}")
+    if c == 0.0:
+        assert st.accepted_total >= (st.round - 1) * K
+    if c == 1.0:
+        assert st.accepted_total == 0
+
+
+def test_spec_no_bonus(env, gpu_ar):
+    from block_verify_amd.synth import make_draft_table
+    b = env["b"]
+    table = make_draft_table(np.array(gpu_ar), env["shape"].vocab, 0.1)
+    r = b.Round(env["model"], K, bonus=False, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    st, toks = r.run(N_NEW)
+    assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+    assert r.tcache.length() == P + st.n_committed
+
+
+def test_spec_accept_matches_oracle_rule_on_gpu_argmax(env, gpu_ar):
+    """Accept decisions are exact on the GPU's own logits: replay the oracle rule per round."""
+    from block_verify_amd.synth import make_draft_table
+    from oracle.accept import greedy_accept
+    b = env["b"]
+    table = make_draft_table(np.array(gpu_ar), env["shape"].vocab, 0.4)
+    r = b.Round(env["model"], K, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    r.reset(N_NEW)
+    n0 = 0
+    while n0 < N_NEW:
+        r.step()
+        st, toks = r.read_state()
+        drafts = [int(x) for x in table[n0:n0 + K]]
+        v = [gpu_ar[n0 + j] for j in range(K + 1)]
+        m, com = greedy_accept(v, drafts, True)
+        assert st.m_last == m
+        assert list(toks[n0:n0 + m + 1]) == com
+        n0 = st.n_committed
+
+
+def test_trim_and_capacity_errors_are_flagged_not_faults(env):
+    b = env["b"]
+    cache, ws = _fresh(env, max_len=140)
+    _gpu_prefill(env, cache, ws, env["prompt"])
+    cache.trim(130, ws)   # above the length (128): flagged, length unchanged
+    assert ws.error_bits() & b.DERR_TRIM
+    assert cache.length() == P
+    ws2 = b.Workspace(env["shape"], 140)
+    toks = np.arange(16)
+    _gpu_forward(env, cache, ws2, toks)      # 128 + 16 > 140: flagged, cache writes skipped
+    assert ws2.error_bits() & b.DERR_CAPACITY
+    cache.trim(100, ws2)
+    assert cache.length() == 100
+
+
+def test_philox_matches_oracle_words():
+    from block_verify_amd import lib as b
+    from oracle.philox import philox4x64_10
+    rng = np.random.default_rng(0)
+    n = 4096
+    ctr = rng.integers(0, 2 ** 63, (n, 4), dtype=np.int64).astype(np.uint64) * np.uint64(2) + np.uint64(1)
+    ctr[:64, 1:] = 0
+    ctr[:64, 0] = np.arange(64, dtype=np.uint64)
+    key = rng.integers(0, 2 ** 63, (n, 2), dtype=np.int64).astype(np.uint64)
+    key[:64] = [3, 0]
+    got = b.philox4x64(ctr, key)
+    for i in list(range(64)) + list(range(64, n, 97)):
+        assert tuple(int(x) for x in got[i]) == philox4x64_10(ctr[i], key[i])
