@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Committed tok/s of block-verify speculative decoding on one MI355X.
+
+Workload (default): a Qwen2.5-1.5B-shaped random-init bf16 target at a
+2048-token context (prompt of 2048 seeded random ids, prefilled once), k = 4
+drafts per round from the synthetic table (the target's own greedy
+continuation with each position replaced with probability 0.46, seed 1),
+64 committed tokens per job.  One "step" is one job: reset to the
+post-prefill state, then rounds (draft provision, block verify, greedy
+acceptance, trim, repair) until 64 tokens are committed.  Inputs are
+resident in HBM before the timed region.
+
+Prints one JSON line.  `value` = committed tokens / second over the timed
+jobs (schedule B by default: the (k+1)-row verify pass; schedule A, the
+k-row verify plus a one-token repair forward, is reported beside it).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "committed tok/s, k=4, 1.5B-shape @2K/8K ctx; verify HBM GB/s vs 8 TB/s peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """A ring of hipEvent_t created through the HIP runtime (timing only)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), 0)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.arr[i] = ev.value
+        self.n = n
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), self.arr[a], self.arr[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(out.value)
+
+
+def verify_bytes(shape, T: int, M: int) -> int:
+    """Algorithmic HBM bytes of one forward of M rows at context T.
+
+    Weights read once (every linear incl. the LM head, the norm gains), the
+    K/V of the T cached positions and of the M new ones read by attention,
+    the M new K/V written, the M logits rows written, the M embedding rows.
+    """
+    w = shape.weight_bytes_bf16() - 2 * shape.vocab * shape.hidden   # embedding table is gathered, not streamed
+    kv_pos = shape.kv_bytes_per_token()
+    return w + kv_pos * (T + M) + kv_pos * M + 4 * shape.vocab * M + 2 * shape.hidden * M
+
+
+def gpu_ar(b, model, shape, prompt_t, n, max_len, torch):
+    """Greedy AR with the same kernels (M=1 steps chained on the device)."""
+    cache = b.Cache(shape, max_len)
+    ws = b.Workspace(shape, max_len)
+    toks = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(model, cache, prompt_t, ws, logits=logits, argmax=toks[0:1])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n - 1):
+        b.decode_step(model, cache, toks[i:i + 1], ws, logits=logits, argmax=toks[i + 1:i + 2])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    if ws.error_bits():
+        raise RuntimeError(f"AR: device error bits {ws.error_bits()}")
+    return [int(x) for x in toks[:n].cpu().numpy()], dt
+
+
+def run_spec(b, model, shape, prompt, table, k, schedule, steps, warmup, n_new, max_len, torch):
+    """Timed jobs replay the round's four captured HIP graphs; the library records
+    the per-term events (draft, verify, accept, repair) between them into a ring
+    large enough that every timed round keeps its own timestamps."""
+    nvar = (n_new + 1) * max(steps, 1)
+    ev = HipEvents(5 * nvar)
+    r = b.Round(model, k, schedule=schedule, table=table, max_len=max_len, events=ev.arr, n_events=5 * nvar)
+    r.prefill(prompt)
+    r.capture()
+    for _ in range(warmup):
+        r.run(n_new, graph=True)
+    torch.cuda.synchronize()
+    start_calls = r.calls()
+    t0 = time.perf_counter()
+    toks_all = []
+    rounds = 0
+    acc = 0
+    for _ in range(steps):
+        st, toks = r.run(n_new, graph=True)
+        rounds += st.round
+        acc += st.accepted_total
+        toks_all.append(list(toks[:n_new]))
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    end_calls = r.calls()
+    terms = {"draft": [], "verify": [], "accept": [], "repair": [], "round": []}
+    done_rounds = 0
+    for c in range(start_calls, end_calls):
+        base = (c % nvar) * 5
+        rd = ev.ms(base, base + 4)
+        if ev.ms(base + 1, base + 2) < 0.05:     # a launched round past the target returns at once
+            continue
+        done_rounds += 1
+        terms["draft"].append(ev.ms(base, base + 1))
+        terms["verify"].append(ev.ms(base + 1, base + 2))
+        terms["accept"].append(ev.ms(base + 2, base + 3))
+        terms["repair"].append(ev.ms(base + 3, base + 4))
+        terms["round"].append(rd)
+    if r.ws.error_bits():
+        raise RuntimeError(f"spec: device error bits {r.ws.error_bits()}")
+    return dict(seconds=dt, rounds=rounds, accepted=acc, tokens=toks_all, terms=terms,
+                prompt_len=len(prompt), t_len=r.tcache.length())
+
+
+def cpu_baseline(shape, weights, k, tau, budget_s=15.0, context=2048):
+    """Time the oracle's schedule-B round (k+1-row verify forward + greedy accept + trim).
+
+    Bounded sample: the oracle's cache holds `context` positions of seeded
+    random K/V (the forward's cost does not depend on their values); the
+    oracle's tokens/second = tau (tokens per round, measured on the GPU job)
+    / oracle seconds per round.
+    """
+    from oracle.accept import greedy_accept, argmax_lowest
+    from oracle.model import OracleCache, OracleWeights, forward
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    w = OracleWeights(shape, weights)
+    cache = OracleCache(shape, context + 4 * (k + 1) + 8)
+    rng = np.random.default_rng(5)
+    for l in range(shape.n_layers):
+        cache.k[l][:, :context] = rng.standard_normal((shape.n_kv_heads, context, shape.head_dim))
+        cache.v[l][:, :context] = rng.standard_normal((shape.n_kv_heads, context, shape.head_dim))
+    cache.length = context
+    toks = rng.integers(0, shape.vocab, k + 1)
+
+    def one_round():
+        t = cache.length
+        rows = forward(w, cache, toks)
+        v = [argmax_lowest(rr) for rr in rows]
+        m, com = greedy_accept(v, list(toks[1:]), True)
+        cache.trim(t)
+
+    t0 = time.perf_counter()
+    one_round()             # first round also upcasts the weights (not timed)
+    log(f"cpu baseline: warm-up round {time.perf_counter() - t0:.1f} s")
+    n, t0 = 0, time.perf_counter()
+    while True:
+        one_round()
+        n += 1
+        el = time.perf_counter() - t0
+        if el > budget_s or n >= 50:
+            break
+    per_round = el / n
+    return {"value": tau / per_round, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{n} oracle schedule-B rounds (verify forward of {k + 1} rows, float64, at a "
+                       f"{context}-position cache of seeded random K/V + greedy accept + trim), "
+                       f"{per_round:.3f} s/round; tok/s = {tau:.3f} tokens/round (GPU job) / s per round")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--schedule", choices=["A", "B"], default="B")
+    ap.add_argument("--context", type=int, default=2048)
+    ap.add_argument("--n-new", type=int, default=64)
+    ap.add_argument("--corrupt", type=float, default=0.46)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import QWEN_1_5B as S, SEED_TARGET
+    from block_verify_amd.synth import make_draft_table, make_prompt, make_weights
+
+    k = 4
+    P = args.context
+    max_len = P + args.n_new + 4 * (k + 2) + 64
+    t0 = time.perf_counter()
+    weights = make_weights(S, SEED_TARGET)
+    model = b.Model(S, weights)
+    torch.cuda.synchronize()
+    log(f"model ready in {time.perf_counter() - t0:.1f} s")
+    prompt = make_prompt(S.vocab, P)
+    prompt_t = torch.from_numpy(prompt).cuda()
+
+    ar_toks, ar_s = gpu_ar(b, model, S, prompt_t, args.n_new + k + 2, max_len, torch)
+    ar_tok_s = (args.n_new + k + 1) / ar_s
+    log(f"AR: {ar_tok_s:.1f} tok/s")
+    table = make_draft_table(np.array(ar_toks), S.vocab, args.corrupt)
+
+    res = {}
+    for sched in ("A", "B"):
+        res[sched] = run_spec(b, model, S, prompt, table, k, 0 if sched == "A" else 1, args.steps, args.warmup,
+                              args.n_new, max_len, torch)
+        for toks in res[sched]["tokens"]:
+            if toks != ar_toks[:args.n_new]:
+                raise RuntimeError(f"schedule {sched}: committed tokens differ from the GPU AR decode")
+        log(f"schedule {sched}: {args.n_new * args.steps / res[sched]['seconds']:.1f} tok/s, "
+            f"{res[sched]['rounds'] / args.steps:.1f} rounds/job")
+
+    main_r = res[args.schedule]
+    value = args.n_new * args.steps / main_r["seconds"]
+    terms = {s: {t: float(np.mean(v)) for t, v in res[s]["terms"].items()} for s in res}
+    rows = k + (1 if args.schedule == "B" else 0)
+    vb = verify_bytes(S, P + args.n_new // 2, rows)
+    v_ms = float(np.mean(main_r["terms"]["verify"]))
+    achieved = vb / (v_ms * 1e-3) / 1e9
+    rounds_per_job = main_r["rounds"] / args.steps
+    tau = args.n_new / rounds_per_job
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(main_r["seconds"] * 1e3 / args.steps, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights, random prompt ids, corrupted greedy-continuation drafts)",
+        "config": {"workload": f"1.5B-shape target, {P}-token context, k={k}, {args.n_new} committed tokens, "
+                               f"table drafts corrupt p={args.corrupt}, greedy, schedule {args.schedule}",
+                   "context": P, "k": k, "n_new": args.n_new, "schedule": args.schedule},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": f"verify forward ({rows} rows), {vb} algorithmic bytes, {v_ms * 1e3:.1f} us avg"},
+        "terms_ms": terms,
+        "schedule_A_tok_s": round(args.n_new * args.steps / res["A"]["seconds"], 2),
+        "schedule_B_tok_s": round(args.n_new * args.steps / res["B"]["seconds"], 2),
+        "ar_tok_s": round(ar_tok_s, 2),
+        "R_spec_over_ar": round(value / ar_tok_s, 3),
+        "rounds_per_job": round(rounds_per_job, 2),
+        "acceptance_per_drafted": round(main_r["accepted"] / (k * main_r["rounds"]), 4),
+        "tokens_per_round": round(tau, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(S, weights, k, tau, args.cpu_budget, P)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,15 +69,18 @@ WsPlan ws_plan(const Dims& d, int max_rows, int max_len) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   const size_t R = kMaxRows;
-  p.err = take(256);
+  p.err = 0;
+  p.cnt = 256;
+  off = kWsHeader;
   p.x = take(R * d.H * 4);
   p.xb = take((size_t)kMaxNT * d.H * 32);
   p.ss = take(R * (d.H / 16) * 4);
-  p.q = take(R * d.qdim() * 4);
+  p.qb = take((size_t)d.nkv * (kMaxRows * 8 / 16) * (d.hd / 32) * 2 * 1024);
   p.ob = take((size_t)kMaxNT * d.qdim() * 32);
   p.hb = take((size_t)kMaxNT * d.F * 32);
   p.att_o = take((size_t)d.nkv * p.max_chunks * (R * 8) * d.hd * 4);
   p.att_ml = take((size_t)d.nkv * p.max_chunks * (R * 8) * 2 * 4);
+  p.part = take((size_t)kMaxSplit * kMaxRows * d.H * 4);
   p.lm_part = take(R * p.lm_wgs * 3 * 4);
   p.toks = take(R * 4 * 2);
   p.logits = take(R * (size_t)d.V * 4);
@@ -124,6 +127,10 @@ struct specdec_round {
   RoundDev dev;
   WsPlan tplan, dplan;
   int prompt_len;
+  long calls;
+  hipStream_t cap_stream;
+  std::vector<hipGraph_t> graphs;
+  std::vector<hipGraphExec_t> execs;
 };
 
 extern "C" {
@@ -207,7 +214,9 @@ int specdec_cache_bytes(const specdec_model_desc* desc, int32_t max_len, size_t*
   int rc = dims_from_desc(desc, &d);
   if (rc) return rc;
   if (!bytes || max_len <= 0) return SPECDEC_EINVAL;
-  size_t kv = align256((size_t)d.L * 2 * d.nkv * max_len * d.hd * 2);
+  if (max_len > 65536) return SPECDEC_ECAPACITY;
+  const size_t lp = ((size_t)max_len + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
+  size_t kv = align256((size_t)d.L * 2 * d.nkv * lp * d.hd * 2);
   size_t rope = align256((size_t)max_len * (d.hd / 2) * 8);
   *bytes = kv + rope;
   return SPECDEC_OK;
@@ -227,10 +236,12 @@ int specdec_cache_create(const specdec_model_desc* desc, void* d_mem, size_t byt
   if (!c) return SPECDEC_EINVAL;
   c->d = d;
   c->kv = static_cast<bf16_bits*>(d_mem);
-  size_t kv = align256((size_t)d.L * 2 * d.nkv * max_len * d.hd * 2);
+  const size_t lpad = ((size_t)max_len + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
+  size_t kv = align256((size_t)d.L * 2 * d.nkv * lpad * d.hd * 2);
   c->rope = reinterpret_cast<float2*>(static_cast<char*>(d_mem) + kv);
   c->d_len = d_len;
   c->max_len = max_len;
+  c->lp = (max_len + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
   // RoPE table in double precision on the host: angle = pos * theta^(-2i/d)
   const int half = d.hd / 2;
   std::vector<float2> tab((size_t)max_len * half);
@@ -270,8 +281,8 @@ int specdec_workspace_bytes(const specdec_model_desc* desc, int32_t max_rows, in
 }
 
 int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream) {
-  if (!d_ws || ws_bytes < 256) return SPECDEC_EINVAL;
-  return hip_status(hipMemsetAsync(d_ws, 0, 256, (hipStream_t)stream));
+  if (!d_ws || ws_bytes < (size_t)kWsHeader) return SPECDEC_EINVAL;
+  return hip_status(hipMemsetAsync(d_ws, 0, kWsHeader, (hipStream_t)stream));
 }
 
 static int check_fwd(const specdec_model* m, const specdec_cache* c, int32_t rows, size_t ws_bytes, WsPlan* plan) {
@@ -386,6 +397,9 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   if (!r) return SPECDEC_EINVAL;
   r->desc = q;
   r->prompt_len = 0;
+  r->calls = 0;
+  r->cap_stream = nullptr;
+  if (q.events && q.n_events < 5) { delete r; return SPECDEC_EINVAL; }
   r->tplan = ws_plan(d, rows, q.target_cache->max_len);
   if (q.ws_bytes < r->tplan.total) { delete r; return SPECDEC_ECAPACITY; }
   if (q.draft_source == SPECDEC_DRAFT_MODEL) {
@@ -430,7 +444,13 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   return SPECDEC_OK;
 }
 
-void specdec_round_destroy(specdec_round* r) { delete r; }
+void specdec_round_destroy(specdec_round* r) {
+  if (!r) return;
+  for (auto x : r->execs) (void)hipGraphExecDestroy(x);
+  for (auto g : r->graphs) (void)hipGraphDestroy(g);
+  if (r->cap_stream) (void)hipStreamDestroy(r->cap_stream);
+  delete r;
+}
 
 static hipError_t fwd(const specdec_round* r, bool draft, const int32_t* toks, int rows, float* logits,
                       int32_t* argmax, float* lse, const int32_t* gate, hipStream_t s) {
@@ -486,45 +506,122 @@ int specdec_round_reset(specdec_round* r, int32_t n_target, void* stream) {
   return hip_status(launch_reset(r->dev, n_target, (hipStream_t)stream));
 }
 
+// A round is four segments: 0 round start + draft provision, 1 block verify,
+// 2 acceptance + trim, 3 repair.  Per-term events sit between segments.
+static hipError_t enqueue_segment(specdec_round* r, hipStream_t s, int seg);
+
+static hipError_t record_mark(specdec_round* r, hipStream_t s, long call, int i) {
+  const specdec_round_desc& q = r->desc;
+  const int ring = q.events ? (q.n_events / 5) * 5 : 0;
+  if (!ring) return hipSuccess;
+  const int eb = (int)((call * 5) % ring);
+  return hipEventRecord((hipEvent_t)q.events[eb + i], s);
+}
+
+static hipError_t enqueue_round(specdec_round* r, hipStream_t s) {
+  const long call = r->calls++;
+  hipError_t e = hipSuccess;
+  for (int seg = 0; seg < 4 && e == hipSuccess; ++seg) {
+    e = record_mark(r, s, call, seg);
+    if (e == hipSuccess) e = enqueue_segment(r, s, seg);
+  }
+  if (e == hipSuccess) e = record_mark(r, s, call, 4);
+  return e;
+}
+
 int specdec_verify_round(specdec_round* r, void* stream) {
   if (!r) return SPECDEC_EINVAL;
   if (r->prompt_len == 0) return SPECDEC_EINVAL;
+  return hip_status(enqueue_round(r, (hipStream_t)stream));
+}
+
+int specdec_round_graph(specdec_round* r) {
+  if (!r) return SPECDEC_EINVAL;
+  if (r->prompt_len == 0) return SPECDEC_EINVAL;
+  hipError_t e = hipSuccess;
+  if (!r->cap_stream) e = hipStreamCreateWithFlags(&r->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_status(e);
+  for (auto x : r->execs) (void)hipGraphExecDestroy(x);
+  for (auto g : r->graphs) (void)hipGraphDestroy(g);
+  r->execs.clear();
+  r->graphs.clear();
+  for (int seg = 0; seg < 4; ++seg) {
+    e = hipStreamBeginCapture(r->cap_stream, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) break;
+    hipError_t e2 = enqueue_segment(r, r->cap_stream, seg);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(r->cap_stream, &g);
+    if (e2 != hipSuccess) e = e2;
+    if (e != hipSuccess) { if (g) (void)hipGraphDestroy(g); break; }
+    hipGraphExec_t x = nullptr;
+    e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) { (void)hipGraphDestroy(g); break; }
+    r->graphs.push_back(g);
+    r->execs.push_back(x);
+  }
+  if (e != hipSuccess) {
+    for (auto x : r->execs) (void)hipGraphExecDestroy(x);
+    for (auto g : r->graphs) (void)hipGraphDestroy(g);
+    r->execs.clear();
+    r->graphs.clear();
+  }
+  return hip_status(e);
+}
+
+int specdec_round_graph_launch(specdec_round* r, int32_t n_rounds, void* stream) {
+  if (!r || r->execs.size() != 4 || n_rounds < 0) return SPECDEC_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  for (int i = 0; i < n_rounds; ++i) {
+    const long call = r->calls++;
+    hipError_t e = hipSuccess;
+    for (int seg = 0; seg < 4 && e == hipSuccess; ++seg) {
+      e = record_mark(r, s, call, seg);
+      if (e == hipSuccess) e = hipGraphLaunch(r->execs[(size_t)seg], s);
+    }
+    if (e == hipSuccess) e = record_mark(r, s, call, 4);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return SPECDEC_OK;
+}
+
+static hipError_t enqueue_segment(specdec_round* r, hipStream_t s, int seg) {
   const specdec_round_desc& q = r->desc;
   const RoundDev& v = r->dev;
-  hipStream_t s = (hipStream_t)stream;
   const bool B = q.schedule == SPECDEC_SCHEDULE_B;
   const int k = q.k;
   const int32_t* open = v.flags + kFlagOpen;
   const int32_t* rep = v.flags + kFlagRepair;
-  hipError_t e = launch_round_start(v, s);
-  // ---- draft provision
-  if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL) {
-    for (int j = 0; j < k && e == hipSuccess; ++j)
-      e = fwd(r, true, v.block + (B ? 1 : 0) + j, 1, v.draft_logits, v.draft_argmax, nullptr, open, s);
-  } else if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_NOISY_SELF) {
-    e = launch_draft_sample(v, v.saved_logits, 0, s);
-    for (int j = 1; j < k && e == hipSuccess; ++j) {
-      e = fwd(r, false, v.block + j - 1, 1, v.z, nullptr, nullptr, open, s);
-      if (e == hipSuccess) e = launch_draft_sample(v, v.z, j, s);
+  hipError_t e = hipSuccess;
+  if (seg == 0) {
+    e = launch_round_start(v, s);
+    if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL) {
+      for (int j = 0; j < k && e == hipSuccess; ++j)
+        e = fwd(r, true, v.block + (B ? 1 : 0) + j, 1, v.draft_logits, v.draft_argmax, nullptr, open, s);
+    } else if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_NOISY_SELF) {
+      e = launch_draft_sample(v, v.saved_logits, 0, s);
+      for (int j = 1; j < k && e == hipSuccess; ++j) {
+        e = fwd(r, false, v.block + j - 1, 1, v.z, nullptr, nullptr, open, s);
+        if (e == hipSuccess) e = launch_draft_sample(v, v.z, j, s);
+      }
+      if (e == hipSuccess && k > 1) e = launch_rewind(v, v.t_len, k - 1, s);
+    } else if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_Q4_SELF) {
+      for (int j = 1; j < k && e == hipSuccess; ++j)
+        e = fwd(r, true, v.block + j - 1, 1, v.draft_logits, v.block + j, nullptr, open, s);
+      if (e == hipSuccess && k > 1) e = launch_rewind(v, v.t_len, k - 1, s);
     }
-    if (e == hipSuccess && k > 1) e = launch_rewind(v, v.t_len, k - 1, s);
-  } else if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_Q4_SELF) {
-    for (int j = 1; j < k && e == hipSuccess; ++j)
-      e = fwd(r, true, v.block + j - 1, 1, v.draft_logits, v.block + j, nullptr, open, s);
-    if (e == hipSuccess && k > 1) e = launch_rewind(v, v.t_len, k - 1, s);
+  } else if (seg == 1) {
+    e = fwd(r, false, v.block, k + (B ? 1 : 0), v.rows_logits, v.rows_argmax, v.rows_lse, open, s);
+  } else if (seg == 2) {
+    e = q.mode == SPECDEC_STOCHASTIC ? launch_accept_stochastic(v, s) : launch_accept_greedy(v, s);
+  } else {
+    if (!B) {
+      e = fwd(r, false, v.repair_tok, 1, v.saved_logits, v.repair_argmax, v.repair_lse, rep, s);
+      if (e == hipSuccess) e = launch_repair_done(v, s);
+    }
+    if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL)
+      e = fwd(r, true, v.repair_tok, 1, v.draft_logits, v.draft_argmax, nullptr, rep, s);
   }
-  // ---- block verify
-  if (e == hipSuccess) e = fwd(r, false, v.block, k + (B ? 1 : 0), v.rows_logits, v.rows_argmax, v.rows_lse, open, s);
-  // ---- accept + trim
-  if (e == hipSuccess) e = q.mode == SPECDEC_STOCHASTIC ? launch_accept_stochastic(v, s) : launch_accept_greedy(v, s);
-  // ---- repair
-  if (e == hipSuccess && !B) {
-    e = fwd(r, false, v.repair_tok, 1, v.saved_logits, v.repair_argmax, v.repair_lse, rep, s);
-    if (e == hipSuccess) e = launch_repair_done(v, s);
-  }
-  if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL)
-    e = fwd(r, true, v.repair_tok, 1, v.draft_logits, v.draft_argmax, nullptr, rep, s);
-  return hip_status(e);
+  return e;
 }
 
 // Test hook: Philox4x64-10 words for n (counter, key) pairs (device arrays).

@@ -38,11 +38,9 @@ __device__ __forceinline__ float bf2f(bf16_bits b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// float -> bf16, round to nearest even (NaN stays NaN).
+// float -> bf16, round to nearest even (the native gfx950 conversion).
 __device__ __forceinline__ bf16_bits f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_bits)((u >> 16) | 0x40u);
-  return (bf16_bits)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  return __builtin_bit_cast(bf16_bits, (__bf16)f);
 }
 
 // Position of activation (row m, input k) inside an activation tile buffer,
@@ -61,16 +59,65 @@ __device__ __forceinline__ void btile_put(bf16_bits* tiles, int KB, int m, int k
   tiles[i + 64] = lo;
 }
 
+// Cross-lane moves within 16-lane rows (DPP); control words of the GFX9
+// DPP encoding: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_ror:8 = 0x128,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Value of lane (l ^ 8): swaps the hi and lo halves of an MFMA result row.
+__device__ __forceinline__ float swap8(float v) { return dpp_f<0x128>(v); }
+
+// Wave-wide sum / max: a fixed tree inside each 16-lane row, then the four
+// row results in lane order.  Every lane gets the same value.
 __device__ __forceinline__ float warp_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return ((readlane_f(v, 0) + readlane_f(v, 16)) + readlane_f(v, 32)) + readlane_f(v, 48);
 }
 
 __device__ __forceinline__ float warp_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+// Wave-wide (max, lowest index of the max).
+__device__ __forceinline__ void warp_argmax(float& v, int& idx) {
+#define SD_ARGMAX_STEP(CTRL)                                        \
+  {                                                                 \
+    float ov = dpp_f<CTRL>(v);                                      \
+    int oi = dpp_i<CTRL>(idx);                                      \
+    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }      \
+  }
+  SD_ARGMAX_STEP(0xB1)
+  SD_ARGMAX_STEP(0x4E)
+  SD_ARGMAX_STEP(0x141)
+  SD_ARGMAX_STEP(0x140)
+#undef SD_ARGMAX_STEP
+  float bv = readlane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(idx, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  for (int r = 1; r < 4; ++r) {
+    float ov = readlane_f(v, 16 * r);
+    int oi = __builtin_amdgcn_readlane(idx, 16 * r);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  v = bv;
+  idx = bi;
 }
 
 // Sticky device error bits.

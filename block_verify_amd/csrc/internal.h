@@ -58,23 +58,29 @@ struct specdec_model {
   std::vector<sd::LayerPtrs> layers;
 };
 
+// K is [nkv][lp][hd] per layer; V is kept transposed, [nkv][hd][lp], so the
+// attention's P*V operand reads 8 consecutive keys of one head dim as 16
+// contiguous bytes.  lp = max_len rounded up to the 64-key attention chunk.
 struct specdec_cache {
   sd::Dims d;
-  bf16_bits* kv;      // [L][2][nkv][max_len][hd]
+  bf16_bits* kv;      // [L][K|V][...]
   float2* rope;       // [max_len][hd/2] (cos, sin)
   int32_t* d_len;
   int max_len;
-  bf16_bits* k_layer(int l) const { return kv + (size_t)l * 2 * d.nkv * max_len * d.hd; }
-  bf16_bits* v_layer(int l) const { return k_layer(l) + (size_t)d.nkv * max_len * d.hd; }
+  int lp;
+  bf16_bits* k_layer(int l) const { return kv + (size_t)l * 2 * d.nkv * lp * d.hd; }
+  bf16_bits* v_layer(int l) const { return k_layer(l) + (size_t)d.nkv * lp * d.hd; }
 };
 
 namespace sd {
 
 constexpr int kAttnChunk = 64;
+constexpr int kWsHeader = 65536;   // error word + split-K arrival counters (zeroed once)
+constexpr int kMaxSplit = 4;
 
 // Workspace plan for one model.
 struct WsPlan {
-  size_t err, x, xb, ss, q, ob, hb, att_o, att_ml, lm_part, toks, logits, total;
+  size_t err, cnt, x, xb, ss, qb, ob, hb, att_o, att_ml, part, lm_part, toks, logits, total;
   int max_rows, nt, max_chunks, lm_wgs;
 };
 WsPlan ws_plan(const Dims& d, int max_rows, int max_len);

@@ -22,7 +22,12 @@
 
 namespace sd {
 
-enum class Epi { QKV, RESID, SWIGLU, LMHEAD };
+enum class Epi { QKV, RESID, SWIGLU, LMHEAD, PARTIAL };
+
+// K splits of the down projection (fixed per matrix, so a row's summation
+// order never depends on the row count).
+constexpr int kDownSplit = 4;
+
 
 hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStream_t s);
 
@@ -150,46 +155,39 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Weight-streaming MFMA GEMV.
 // ---------------------------------------------------------------------------
-template <int NT>
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Streams the weight tiles of one row group over k-blocks [kb0, kb1) through
+// MFMA.  Tiles travel as 32-bit integer vectors (bit-cast to bf16 only at the
+// MFMA) so the guarded unroll never needs 16-bit lane merges; kb0/kb1 are
+// wave-uniform, so the guards are scalar branches.
+template <int NT, int U>
 __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, const bf16x8_t* __restrict__ B, int KB,
                                             int kb0, int kb1, int lane, f32x4_t (&acc)[NT]) {
-  const bf16x8_t* a = A + (size_t)kb0 * 64 + lane;
-  const bf16x8_t* b = B + (size_t)kb0 * 64 + lane;
+  const i32x4_t* a = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
+  const i32x4_t* b = reinterpret_cast<const i32x4_t*>(B) + (size_t)kb0 * 64 + lane;
   const size_t tstride = (size_t)KB * 64;
   const int n = kb1 - kb0;
-  constexpr int U = (NT <= 2) ? 8 : 4;
-  int i = 0;
-  for (; i + U <= n; i += U) {
-    bf16x8_t av[U];
-    bf16x8_t bv[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) av[u] = __builtin_nontemporal_load(a + (size_t)(i + u) * 64);
+  // up to U weight tiles in flight per wave; the activation tiles are L2-resident
+  for (int i = 0; i < n; i += U) {
+    i32x4_t av[U];
+    i32x4_t bv[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) bv[u][t] = b[t * tstride + (size_t)(i + u) * 64];
+      if (i + u < n) av[u] = __builtin_nontemporal_load(a + (size_t)(i + u) * 64);
 #pragma unroll
     for (int u = 0; u < U; ++u)
+      if (i + u < n)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][t], acc[t], 0, 0, 0);
-  }
-  for (; i < n; ++i) {
-    bf16x8_t av = __builtin_nontemporal_load(a + (size_t)i * 64);
+        for (int t = 0; t < NT; ++t) bv[u][t] = b[t * tstride + (size_t)(i + u) * 64];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      bf16x8_t bv = b[t * tstride + (size_t)i * 64];
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[t], 0, 0, 0);
-    }
+    for (int u = 0; u < U; ++u)
+      if (i + u < n)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
+                                                          __builtin_bit_cast(bf16x8_t, bv[u][t]), acc[t], 0, 0, 0);
   }
-}
-
-// r_m = 1 / sqrt(mean(x_m^2) + eps) from the per-16-feature partial sums.
-// One wave per row; the reduction tree is fixed by the feature layout.
-__device__ __forceinline__ float rms_scale_wave(const float* __restrict__ ss, int m, int NP, int H, float eps, int lane) {
-  float s = 0.f;
-  for (int g = lane; g < NP; g += 64) s += ss[(size_t)m * NP + g];
-  s = warp_sum(s);
-  return 1.0f / sqrtf(s / (float)H + eps);
 }
 
 struct GemvParams {
@@ -205,12 +203,13 @@ struct GemvParams {
   int H;
   float eps;
   // QKV
-  float* q_out;
+  bf16_bits* qb;         // query operand tiles per kv head
   bf16_bits* k_cache;
   bf16_bits* v_cache;
   const float2* rope;
   const int32_t* d_len;
-  int max_len;
+  int max_len;           // cache capacity (positions)
+  int kv_stride;         // padded positions per head (K rows; V^T row length)
   int nq, nkv, hd;
   // RESID
   float* x;
@@ -224,53 +223,97 @@ struct GemvParams {
   float* logits;
   int V;
   float* lm_part;        // [rows][gridDim.x][3]
+  // PARTIAL (split-K): [nsplit][kMaxRows][H] partial outputs
+  float* part;
+  int nsplit;
 };
 
-template <int NT, int WG_ROWS, int WK, Epi E>
+// Query operand tiles: per kv head, query rows r = m * G + g (g = query head
+// within the group), 16 rows per tile, the bf16 hi and lo parts of q / sqrt(d)
+// in separate tiles: [tile][k-block over the head dim][hi|lo][64 lanes][8].
+// Lane l of a tile holds row 16 * tile + (l % 16), dims 32 * kb + 8 * (l / 16) .. +7.
+constexpr int kQTiles = kMaxRows * 8 / 16;   // up to 8 * kMaxRows query rows
+__device__ __forceinline__ size_t qtile_head(int h, int hd) { return (size_t)h * kQTiles * (hd / 32) * 2 * kTileU16; }
+__device__ __forceinline__ void qtile_put(bf16_bits* qh, int KBH, int row, int dim, float v) {
+  const int tq = row >> 4, j = row & 15, kb = dim >> 5, sg = (dim >> 3) & 3, e = dim & 7;
+  const size_t base = ((size_t)(tq * KBH + kb) * 2) * kTileU16 + (size_t)((sg * 16 + j) * 8 + e);
+  const bf16_bits hi = f2bf(v);
+  qh[base] = hi;
+  qh[base + kTileU16] = f2bf(v - bf2f(hi));
+}
+
+template <int NT, int WG_ROWS, int WK, int U, Epi E>
 __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
   if (p.gate && *p.gate == 0) return;
   constexpr int NW = WG_ROWS * WK;
   constexpr int NC = NT * 8;        // activation rows covered
-  __shared__ float red[NW][16][NT * 16 + 1];
+  constexpr int RPW = (kMaxRows + NW - 1) / NW;
+  __shared__ float red[NW][16][NC + 1];
   __shared__ float fin[WG_ROWS][16][NC + 1];
   __shared__ float rsc[kMaxRows];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // wave index as a provably uniform value: the k-range guards below become
+  // scalar branches instead of EXEC-masked regions around MFMA operands
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = w / WK, ks = w % WK;
-  const int g = blockIdx.x * WG_ROWS + rg;
+  const int nsplit = (E == Epi::PARTIAL) ? p.nsplit : 1;
+  const int sidx = (E == Epi::PARTIAL) ? (int)(blockIdx.x % nsplit) : 0;
+  const int g = (E == Epi::PARTIAL) ? (int)(blockIdx.x / nsplit) : (int)(blockIdx.x * WG_ROWS + rg);
   const int M = p.rows;
+  const int NP = p.H >> 4;
+
+  // sums of squares of the normalised input, issued before the weight stream
+  constexpr bool kNorm = (E == Epi::QKV || E == Epi::SWIGLU || E == Epi::LMHEAD);
+  float ssv[RPW][4];
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int m = w + j * NW;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int gg = lane + 64 * u;
+        ssv[j][u] = (m < M && gg < NP) ? p.ss_in[(size_t)m * NP + gg] : 0.f;
+      }
+    }
+  }
 
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (g < p.n_groups) {
-    const int kb0 = (int)(((long)ks * p.KB) / WK), kb1 = (int)(((long)(ks + 1) * p.KB) / WK);
-    mfma_stream<NT>(p.A + (size_t)g * p.KB * 64, p.B, p.KB, kb0, kb1, lane, acc);
+    const int s0 = (int)(((long)sidx * p.KB) / nsplit), s1 = (int)(((long)(sidx + 1) * p.KB) / nsplit);
+    const int kb0 = s0 + (int)(((long)ks * (s1 - s0)) / WK), kb1 = s0 + (int)(((long)(ks + 1) * (s1 - s0)) / WK);
+    mfma_stream<NT, U>(p.A + (size_t)g * p.KB * 64, p.B, p.KB, kb0, kb1, lane, acc);
   }
-  // row scales for normalised inputs (overlaps other waves' streaming)
-  if constexpr (E != Epi::RESID) {
-    for (int m = w; m < M; m += NW) {
-      float r = rms_scale_wave(p.ss_in, m, p.H >> 4, p.H, p.eps, lane);
-      if (lane == 0) rsc[m] = r;
+  // r_m = 1 / sqrt(mean(x_m^2) + eps); fixed reduction order per row
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int m = w + j * NW;
+      if (m < M) {
+        float sq = ((ssv[j][0] + ssv[j][1]) + ssv[j][2]) + ssv[j][3];
+        sq = warp_sum(sq);
+        if (lane == 0) rsc[m] = 1.0f / sqrtf(sq / (float)p.H + p.eps);
+      }
     }
   }
+  // hi + lo (columns c and c+8) in registers, then the waves' partials in LDS
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[w][4 * (lane >> 4) + r][t * 16 + (lane & 15)] = acc[t][r];
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[t][r] + swap8(acc[t][r]);
+      if ((lane & 15) < 8) red[w][4 * (lane >> 4) + r][t * 8 + (lane & 15)] = v;
+    }
   __syncthreads();
-  // fixed-order reduction over the k-split waves, then hi + lo
+  // fixed-order reduction over the k-split waves
   for (int idx = threadIdx.x; idx < WG_ROWS * 16 * NC; idx += blockDim.x) {
     int rr = idx / (16 * NC), rem = idx % (16 * NC), i = rem / NC, m = rem % NC;
-    int t = m >> 3, c = m & 7;
-    float hi = 0.f, lo = 0.f;
+    float v = 0.f;
 #pragma unroll
-    for (int s = 0; s < WK; ++s) {
-      hi += red[rr * WK + s][i][t * 16 + c];
-      lo += red[rr * WK + s][i][t * 16 + 8 + c];
-    }
-    fin[rr][i][m] = hi + lo;
+    for (int s2 = 0; s2 < WK; ++s2) v += red[rr * WK + s2][i][m];
+    fin[rr][i][m] = v;
   }
   __syncthreads();
 
@@ -297,12 +340,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
             if (v > best || (v == best && idx < bidx)) { best = v; bidx = idx; }
           }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          float ob = __shfl_xor(best, o, 64);
-          int oi = __shfl_xor(bidx, o, 64);
-          if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
-        }
+        warp_argmax(best, bidx);
         float se = 0.f;
         for (int e = lane; e < 16 * WG_ROWS; e += 64) {
           int rr = e >> 4, i = e & 15, gg = blockIdx.x * WG_ROWS + rr;
@@ -342,11 +380,14 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
         float o1 = y1 * cs.x - y2 * cs.y;
         float o2 = y2 * cs.x + y1 * cs.y;
         if (!is_k) {
-          float* q = p.q_out + (size_t)m * p.nq * p.hd + head * p.hd;
-          q[d1] = o1;
-          q[d1 + half] = o2;
+          const int G = p.nq / p.nkv;
+          const float qs = 1.0f / sqrtf((float)p.hd);
+          bf16_bits* qh = p.qb + qtile_head(head / G, p.hd);
+          const int rq = m * G + head % G;
+          qtile_put(qh, p.hd >> 5, rq, d1, o1 * qs);
+          qtile_put(qh, p.hd >> 5, rq, d1 + half, o2 * qs);
         } else {
-          bf16_bits* kc = p.k_cache + ((size_t)head * p.max_len + pos) * p.hd;
+          bf16_bits* kc = p.k_cache + ((size_t)head * p.kv_stride + pos) * p.hd;
           kc[d1] = f2bf(o1);
           kc[d1 + half] = f2bf(o2);
         }
@@ -358,7 +399,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
         int i = idx & 15, m = idx >> 4;
         int pos = pos0 + m;
         if (pos >= p.max_len) continue;
-        p.v_cache[((size_t)head * p.max_len + pos) * p.hd + d0 + i] = f2bf(f[i][m] * rsc[m]);
+        p.v_cache[((size_t)head * p.hd + d0 + i) * p.kv_stride + pos] = f2bf(f[i][m] * rsc[m]);
       }
     }
   } else if constexpr (E == Epi::SWIGLU) {
@@ -369,6 +410,13 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
       float gt = f[i][m] * r, up = f[i + 8][m] * r;
       float h = gt / (1.0f + __expf(-gt)) * up;
       btile_put(p.hb_out, KBo, m, 8 * g + i, h);
+    }
+  } else if constexpr (E == Epi::PARTIAL) {
+    // this split's 16 outputs x M rows, reduced in split order by resid_reduce_kernel
+    float* dst = p.part + (size_t)sidx * kMaxRows * p.H;
+    for (int idx = lane; idx < 16 * M; idx += 64) {
+      const int i = idx & 15, m = idx >> 4;
+      dst[(size_t)m * p.H + 16 * g + i] = f[i][m];
     }
   } else {  // RESID
     const int KBo = p.H >> 5, NP = p.H >> 4;
@@ -392,116 +440,264 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K causal attention over the cache (one workgroup per kv head and
-// 64-key chunk) and the fixed-order merge of the chunk partials.
+// Causal grouped-query attention over the cache, split by 64-key chunks whose
+// boundaries are fixed by absolute key index, then a fixed-order merge of the
+// chunk partials per output.
+//
+// Chunk partial: one wave per (kv head, chunk).  All operand tiles are loaded
+// up front: K rows (operand A of S^T = K Q^T; 8 consecutive head dims per
+// lane), V^T rows (operand A of O^T = V^T P^T; the cache keeps V transposed so
+// 8 consecutive keys of one head dim are 16 contiguous bytes) and the query
+// tiles.  The bf16 hi/lo split of q and of P runs along the MFMA k dimension
+// (two MFMAs into one accumulator), so no cross-lane combine is needed.  Per
+// 16-row query tile: scores, causal mask, row max / sum of exp over the chunk,
+// P^T through a small LDS tile, O^T on MFMA.  Keys past the current length
+// are masked in the scores and zeroed in V^T.
 // ---------------------------------------------------------------------------
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void pack_hilo8(const float (&v)[8], i32x4_t& hi_out, i32x4_t& lo_out) {
+  u16x8_t h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16_bits hb = f2bf(v[e]);
+    h[e] = hb;
+    l[e] = f2bf(v[e] - bf2f(hb));
+  }
+  hi_out = __builtin_bit_cast(i32x4_t, h);
+  lo_out = __builtin_bit_cast(i32x4_t, l);
+}
+
+__device__ __forceinline__ f32x4_t mfma_i(const i32x4_t& a, const i32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+                                                 0, 0);
+}
+
+constexpr int kAttnQPrefetch = 2;   // query tiles (of 16 rows) held in registers
+
 template <int HD>
-__global__ __launch_bounds__(256) void attn_partial_kernel(const float* __restrict__ q, const bf16_bits* __restrict__ Kc,
-                                                           const bf16_bits* __restrict__ Vc, const int32_t* __restrict__ d_len,
-                                                           int rows, int max_len, int nq, int nkv,
-                                                           float* __restrict__ o_part, float* __restrict__ ml_part,
-                                                           int max_chunks, const int32_t* gate) {
+__global__ __launch_bounds__(64) void attn_chunk_kernel(const bf16_bits* __restrict__ qb, const bf16_bits* __restrict__ Kc,
+                                                        const bf16_bits* __restrict__ Vt, const int32_t* __restrict__ d_len,
+                                                        int rows, int max_len, int lp, int G, float* __restrict__ o_part,
+                                                        float* __restrict__ ml_part, int max_chunks, const int32_t* gate) {
   if (gate && *gate == 0) return;
-  constexpr int C = kAttnChunk;
-  constexpr int DL = HD / 64;   // head dims per lane
-  __shared__ float Kt[HD][C + 1];
-  __shared__ float Vs[C][HD + 1];
-  __shared__ float qs[4][HD];
-  const int c = blockIdx.x, h = blockIdx.y;
+  constexpr int C = kAttnChunk;   // 64 keys
+  constexpr int KBH = HD / 32;    // k-blocks over the head dimension
+  constexpr int DT = HD / 16;     // 16-dim output tiles
+  __shared__ __attribute__((aligned(16))) float Pl[16][C + 4];
+  const int c = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int len = *d_len;
   int T = len + rows;
   if (T > max_len) T = max_len;
   const int key0 = c * C;
   if (key0 >= T) return;
-  const int nkeys = min(C, T - key0);
-  const int G = nq / nkv;
-  const bf16_bits* kb = Kc + ((size_t)h * max_len + key0) * HD;
-  const bf16_bits* vb = Vc + ((size_t)h * max_len + key0) * HD;
-  for (int e = threadIdx.x; e < C * (HD / 8); e += blockDim.x) {
-    int j = e / (HD / 8), d8 = (e % (HD / 8)) * 8;
-    uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-    if (j < nkeys) {
-      kv4 = *reinterpret_cast<const uint4*>(kb + (size_t)j * HD + d8);
-      vv4 = *reinterpret_cast<const uint4*>(vb + (size_t)j * HD + d8);
-    }
-    const bf16_bits* k16 = reinterpret_cast<const bf16_bits*>(&kv4);
-    const bf16_bits* v16 = reinterpret_cast<const bf16_bits*>(&vv4);
+  const int R = rows * G, NTq = (R + 15) / 16;
+  const int col = lane & 15, grp = lane >> 4;
+  const size_t rstride = (size_t)kMaxRows * 8;
+
+  const i32x4_t* qh = reinterpret_cast<const i32x4_t*>(qb + qtile_head(h, HD));
+  i32x4_t qv[kAttnQPrefetch][KBH][2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      Kt[d8 + u][j] = bf2f(k16[u]);
-      Vs[j][d8 + u] = bf2f(v16[u]);
+  for (int t = 0; t < kAttnQPrefetch; ++t)
+    if (t < NTq)
+#pragma unroll
+      for (int kb = 0; kb < KBH; ++kb)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) qv[t][kb][hl] = qh[(((size_t)t * KBH + kb) * 2 + hl) * 64 + lane];
+
+  const bf16_bits* kbase = Kc + (size_t)h * lp * HD;
+  i32x4_t ka[4][KBH];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    int krow = key0 + 16 * kt + col;
+    if (krow > T - 1) krow = T - 1;
+#pragma unroll
+    for (int kb = 0; kb < KBH; ++kb)
+      ka[kt][kb] = *reinterpret_cast<const i32x4_t*>(kbase + (size_t)krow * HD + kb * 32 + 8 * grp);
+  }
+  const bf16_bits* vbase = Vt + (size_t)h * HD * lp;
+  i32x4_t va[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+      va[dt][kb2] = *reinterpret_cast<const i32x4_t*>(vbase + (size_t)(16 * dt + col) * lp + key0 + 32 * kb2 + 8 * grp);
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    const int nvalid = T - (key0 + 32 * kb2 + 8 * grp);
+    if (nvalid < 8) {
+      i32x4_t mask;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        mask[j] = (2 * j < nvalid ? 0x0000FFFF : 0) | (2 * j + 1 < nvalid ? (int32_t)0xFFFF0000u : 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) va[dt][kb2] &= mask;
     }
   }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const float scale = 1.0f / sqrtf((float)HD);
-  const int R = rows * G;
-  for (int r = w; r < R; r += 4) {
-    const int m = r / G, hq = h * G + r % G;
-    const float* qr = q + (size_t)m * nq * HD + (size_t)hq * HD;
+
+  float* ob = o_part + ((size_t)h * max_chunks + c) * rstride * HD;
+  float* mb = ml_part + ((size_t)h * max_chunks + c) * rstride * 2;
+  for (int t = 0; t < NTq; ++t) {
+    i32x4_t qt[KBH][2];
+    if (t < kAttnQPrefetch) {
 #pragma unroll
-    for (int u = 0; u < DL; ++u) qs[w][lane + 64 * u] = qr[lane + 64 * u];
-    __builtin_amdgcn_wave_barrier();
+      for (int kb = 0; kb < KBH; ++kb) { qt[kb][0] = qv[t & 1][kb][0]; qt[kb][1] = qv[t & 1][kb][1]; }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KBH; ++kb)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) qt[kb][hl] = qh[(((size_t)t * KBH + kb) * 2 + hl) * 64 + lane];
+    }
+    // S^T tile per 16 keys: lane (col = query row, grp) holds keys 4 * grp + r
+    const int row = 16 * t + col;
+    const int m = row / G;
+    const bool rvalid = row < R;
+    float sv[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KBH; ++kb) {
+        acc = mfma_i(ka[kt][kb], qt[kb][0], acc);
+        acc = mfma_i(ka[kt][kb], qt[kb][1], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kidx = key0 + 16 * kt + 4 * grp + r;
+        const bool ok = rvalid && kidx < T && kidx <= len + m;
+        sv[kt][r] = ok ? acc[r] : -INFINITY;
+        mx = fmaxf(mx, sv[kt][r]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = (mx == -INFINITY) ? 0.f : __expf(sv[kt][r] - mx);
+        sv[kt][r] = pv;
+        sum += pv;
+      }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Pl[col][16 * kt + 4 * grp + r] = sv[kt][r];
+    if (grp == 0 && rvalid) { mb[row * 2] = mx; mb[row * 2 + 1] = sum; }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    float s = 0.f;
-#pragma unroll 16
-    for (int d = 0; d < HD; ++d) s = fmaf(qs[w][d], Kt[d][lane], s);
-    s *= scale;
-    const bool valid = (lane < nkeys) && (key0 + lane <= len + m);
-    s = valid ? s : -INFINITY;
-    const float mx = warp_max(s);
-    float* op = o_part + (((size_t)h * max_chunks + c) * (kMaxRows * 8) + r) * HD;
-    float* mlp = ml_part + (((size_t)h * max_chunks + c) * (kMaxRows * 8) + r) * 2;
-    if (mx == -INFINITY) {
-      if (lane == 0) { mlp[0] = -INFINITY; mlp[1] = 0.f; }
-      continue;
-    }
-    const float pj = valid ? __expf(s - mx) : 0.f;
-    const float l = warp_sum(pj);
-    float o[DL];
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // operand B: P^T (keys x query rows), hi and lo parts along k
+    i32x4_t pb[2][2];
 #pragma unroll
-    for (int u = 0; u < DL; ++u) o[u] = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < C; ++j) {
-      float pjj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j));
-#pragma unroll
-      for (int u = 0; u < DL; ++u) o[u] = fmaf(pjj, Vs[j][lane + 64 * u], o[u]);
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const float4* src = reinterpret_cast<const float4*>(&Pl[col][32 * kb2 + 8 * grp]);
+      const float4 p0 = src[0], p1 = src[1];
+      const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      pack_hilo8(pv8, pb[kb2][0], pb[kb2][1]);
     }
 #pragma unroll
-    for (int u = 0; u < DL; ++u) op[lane + 64 * u] = o[u];
-    if (lane == 0) { mlp[0] = mx; mlp[1] = l; }
-    __builtin_amdgcn_wave_barrier();
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        acc = mfma_i(va[dt][kb2], pb[kb2][0], acc);
+        acc = mfma_i(va[dt][kb2], pb[kb2][1], acc);
+      }
+      // lane (col = query row, grp) holds O[row][16 dt + 4 grp + r]
+      if (rvalid)
+        *reinterpret_cast<float4*>(ob + (size_t)row * HD + 16 * dt + 4 * grp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __builtin_amdgcn_s_barrier();
   }
 }
 
-// One workgroup per (row, q head); thread d owns head dim d.  Chunks merge
-// in index order.  Writes the attention output as activation tiles.
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part,
-                                                        const int32_t* __restrict__ d_len, int rows, int max_len, int nq,
-                                                        int nkv, int hd, int max_chunks, bf16_bits* __restrict__ ob,
-                                                        const int32_t* gate) {
+// Merge: one workgroup per (row, query head), thread d owns head dim d.  The
+// partial loads of a batch of chunks are issued first; the chunk statistics
+// go to LDS and every thread forms the same weights and normaliser in chunk
+// order; the sum over chunks runs in chunk order.
+constexpr int kMaxMergeChunks = 1024;
+
+template <int HD>
+__global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part,
+                                                       const int32_t* __restrict__ d_len, int rows, int max_len, int nq,
+                                                       int nkv, int max_chunks, bf16_bits* __restrict__ ob,
+                                                       const int32_t* gate) {
   if (gate && *gate == 0) return;
+  __shared__ float sm[kMaxMergeChunks], sw[kMaxMergeChunks], sl[kMaxMergeChunks];
   const int m = blockIdx.x / nq, hq = blockIdx.x % nq;
   const int G = nq / nkv, h = hq / G, r = m * G + hq % G;
   int pos = *d_len + m;
   if (pos >= max_len) pos = max_len - 1;
   const int nch = pos / kAttnChunk + 1;
-  const float* ml = ml_part + ((size_t)h * max_chunks * (kMaxRows * 8) + r) * 2;
-  const size_t cstride = (size_t)kMaxRows * 8;
-  float mx = -INFINITY;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, ml[c * cstride * 2]);
+  const size_t rstride = (size_t)kMaxRows * 8;
+  const float* ml = ml_part + ((size_t)h * max_chunks * rstride + r) * 2;
   const int d = threadIdx.x;
-  if (d >= hd) return;
-  float L = 0.f, acc = 0.f;
-  const float* op = o_part + ((size_t)h * max_chunks * cstride + r) * hd + d;
-#pragma unroll 4
-  for (int c = 0; c < nch; ++c) {
-    float mc = ml[c * cstride * 2];
-    float wgt = (mc == -INFINITY) ? 0.f : __expf(mc - mx);
-    L = fmaf(wgt, ml[c * cstride * 2 + 1], L);
-    acc = fmaf(wgt, op[c * cstride * hd], acc);
+  const float* op = o_part + ((size_t)h * max_chunks * rstride + r) * HD + d;
+  const size_t cst = rstride * HD;
+  constexpr int BATCH = 48;
+  float ov[BATCH];
+#pragma unroll
+  for (int u = 0; u < BATCH; ++u) ov[u] = (u < nch) ? op[(size_t)u * cst] : 0.f;
+  for (int c = d; c < nch; c += HD) {
+    sm[c] = ml[(size_t)c * rstride * 2];
+    sl[c] = ml[(size_t)c * rstride * 2 + 1];
   }
-  btile_put(ob, (nq * hd) >> 5, m, hq * hd + d, acc / L);
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, sm[c]);
+  for (int c = d; c < nch; c += HD) sw[c] = (sm[c] == -INFINITY) ? 0.f : __expf(sm[c] - mx);
+  __syncthreads();
+  float L = 0.f;
+  for (int c = 0; c < nch; ++c) L = fmaf(sw[c], sl[c], L);
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < BATCH; ++u)
+    if (u < nch) acc = fmaf(sw[u], ov[u], acc);
+  for (int c0 = BATCH; c0 < nch; c0 += BATCH) {
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) ov[u] = (c0 + u < nch) ? op[(size_t)(c0 + u) * cst] : 0.f;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+      if (c0 + u < nch) acc = fmaf(sw[c0 + u], ov[u], acc);
+  }
+  btile_put(ob, (nq * HD) >> 5, m, hq * HD + d, acc / L);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K finish of the down projection: x += sum of the splits (split
+// order), then the next norm's operand tiles of x * gain and the sums of
+// squares per 16 features.  One workgroup of 256 threads covers 256 features
+// of one row; thread i of a 16-thread group owns feature 16 * group + i.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void resid_reduce_kernel(const float* __restrict__ part, int nsplit, int H, int rows,
+                                                           float* __restrict__ x, const float* __restrict__ gain,
+                                                           bf16_bits* __restrict__ xb, float* __restrict__ ss,
+                                                           const int32_t* gate) {
+  if (gate && *gate == 0) return;
+  __shared__ float sq[256];
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  float xn = 0.f;
+  if (n < H) {
+    float y = 0.f;
+    for (int s2 = 0; s2 < nsplit; ++s2) y += part[((size_t)s2 * kMaxRows + m) * H + n];
+    xn = x[(size_t)m * H + n] + y;
+    x[(size_t)m * H + n] = xn;
+    btile_put(xb, H >> 5, m, n, xn * gain[n]);
+  }
+  sq[threadIdx.x] = xn;
+  __syncthreads();
+  if ((threadIdx.x & 15) == 0 && n < H) {
+    float s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s2 = fmaf(sq[threadIdx.x + i], sq[threadIdx.x + i], s2);
+    ss[(size_t)m * (H >> 4) + (n >> 4)] = s2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -569,47 +765,54 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   float* x = reinterpret_cast<float*>(ws + pl.x);
   bf16_bits* xb = reinterpret_cast<bf16_bits*>(ws + pl.xb);
   float* ss = reinterpret_cast<float*>(ws + pl.ss);
-  float* q = reinterpret_cast<float*>(ws + pl.q);
+  bf16_bits* qb = reinterpret_cast<bf16_bits*>(ws + pl.qb);
   bf16_bits* ob = reinterpret_cast<bf16_bits*>(ws + pl.ob);
   bf16_bits* hb = reinterpret_cast<bf16_bits*>(ws + pl.hb);
   float* att_o = reinterpret_cast<float*>(ws + pl.att_o);
   float* att_ml = reinterpret_cast<float*>(ws + pl.att_ml);
   hipStream_t s = a.stream;
 
-  // fused RMSNorm -> QKV -> RoPE -> K/V append
+  // fused RMSNorm -> QKV -> RoPE -> K/V append (query rows into operand tiles)
   GemvParams p = base;
   p.A = L.wqkv; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.qkv_rows() / 16;
-  p.ss_in = ss; p.q_out = q; p.k_cache = a.c->k_layer(l); p.v_cache = a.c->v_layer(l);
-  gemv_kernel<NT, 1, 4, Epi::QKV><<<p.n_groups, 256, 0, s>>>(p);
+  p.ss_in = ss; p.qb = qb; p.k_cache = a.c->k_layer(l); p.v_cache = a.c->v_layer(l);
+  gemv_kernel<NT, 1, 16, 4, Epi::QKV><<<p.n_groups, 1024, 0, s>>>(p);
 
-  // attention
+  // attention: chunk partials, then the merge into the O-projection operand tiles
   dim3 ag(pl.max_chunks, d.nkv);
-  if (d.hd == 128)
-    attn_partial_kernel<128><<<ag, 256, 0, s>>>(q, a.c->k_layer(l), a.c->v_layer(l), a.c->d_len, a.rows, a.c->max_len,
-                                                 d.nq, d.nkv, att_o, att_ml, pl.max_chunks, a.gate);
-  else
-    attn_partial_kernel<64><<<ag, 256, 0, s>>>(q, a.c->k_layer(l), a.c->v_layer(l), a.c->d_len, a.rows, a.c->max_len,
-                                                d.nq, d.nkv, att_o, att_ml, pl.max_chunks, a.gate);
-  attn_merge_kernel<<<a.rows * d.nq, 128, 0, s>>>(att_o, att_ml, a.c->d_len, a.rows, a.c->max_len, d.nq, d.nkv, d.hd,
-                                                  pl.max_chunks, ob, a.gate);
+  if (d.hd == 128) {
+    attn_chunk_kernel<128><<<ag, 64, 0, s>>>(qb, a.c->k_layer(l), a.c->v_layer(l), a.c->d_len, a.rows, a.c->max_len,
+                                              a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, a.gate);
+    attn_merge_kernel<128><<<a.rows * d.nq, 128, 0, s>>>(att_o, att_ml, a.c->d_len, a.rows, a.c->max_len, d.nq, d.nkv,
+                                                         pl.max_chunks, ob, a.gate);
+  } else {
+    attn_chunk_kernel<64><<<ag, 64, 0, s>>>(qb, a.c->k_layer(l), a.c->v_layer(l), a.c->d_len, a.rows, a.c->max_len,
+                                             a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, a.gate);
+    attn_merge_kernel<64><<<a.rows * d.nq, 64, 0, s>>>(att_o, att_ml, a.c->d_len, a.rows, a.c->max_len, d.nq, d.nkv,
+                                                       pl.max_chunks, ob, a.gate);
+  }
 
   // O projection + residual; next input is the MLP norm
   p = base;
   p.A = L.wo; p.B = reinterpret_cast<const bf16x8_t*>(ob); p.KB = d.qdim() / 32; p.n_groups = d.H / 16;
   p.x = x; p.gain_next = L.mlp_norm; p.xb_out = xb; p.ss_out = ss;
-  gemv_kernel<NT, 1, 4, Epi::RESID><<<p.n_groups, 256, 0, s>>>(p);
+  gemv_kernel<NT, 1, 16, 4, Epi::RESID><<<p.n_groups, 1024, 0, s>>>(p);
 
   // RMSNorm -> gate/up -> SwiGLU
   p = base;
   p.A = L.wgu; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.F / 8;
   p.ss_in = ss; p.hb_out = hb;
-  gemv_kernel<NT, 1, 4, Epi::SWIGLU><<<p.n_groups, 256, 0, s>>>(p);
+  gemv_kernel<NT, 1, 4, 12, Epi::SWIGLU><<<p.n_groups, 256, 0, s>>>(p);
 
   // down projection + residual; next input is the next layer's (or final) norm
   p = base;
   p.A = L.wdown; p.B = reinterpret_cast<const bf16x8_t*>(hb); p.KB = d.F / 32; p.n_groups = d.H / 16;
   p.x = x; p.gain_next = (l + 1 < d.L) ? a.m->layers[l + 1].attn_norm : a.m->final_norm; p.xb_out = xb; p.ss_out = ss;
-  gemv_kernel<NT, 1, 8, Epi::RESID><<<p.n_groups, 512, 0, s>>>(p);
+  p.part = reinterpret_cast<float*>(ws + pl.part);
+  p.nsplit = kDownSplit;
+  gemv_kernel<NT, 1, 8, 8, Epi::PARTIAL><<<p.n_groups * kDownSplit, 512, 0, s>>>(p);
+  resid_reduce_kernel<<<dim3((d.H + 255) / 256, a.rows), 256, 0, s>>>(p.part, kDownSplit, d.H, a.rows, x, p.gain_next, xb,
+                                                                     ss, a.gate);
 }
 
 template <int NT>
@@ -627,7 +830,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
                                       a.c->d_len, a.c->max_len, err, a.gate);
   GemvParams base = {};
   base.rows = a.rows; base.gate = a.gate; base.err = err; base.H = d.H; base.eps = d.eps;
-  base.rope = a.c->rope; base.d_len = a.c->d_len; base.max_len = a.c->max_len;
+  base.rope = a.c->rope; base.d_len = a.c->d_len; base.max_len = a.c->max_len; base.kv_stride = a.c->lp;
   base.nq = d.nq; base.nkv = d.nkv; base.hd = d.hd; base.F = d.F; base.V = d.V;
   for (int l = 0; l < d.L; ++l) launch_gemvs_layer<NT>(a, l, base);
 
@@ -639,7 +842,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
   p.lm_part = lm_part;
   constexpr int LMR = 4;
   int wgs = (p.n_groups + LMR - 1) / LMR;
-  gemv_kernel<NT, LMR, 1, Epi::LMHEAD><<<wgs, 64 * LMR, 0, s>>>(p);
+  gemv_kernel<NT, LMR, 1, 12, Epi::LMHEAD><<<wgs, 64 * LMR, 0, s>>>(p);
   lm_reduce_kernel<<<a.rows, 256, 0, s>>>(lm_part, wgs, a.rows, a.argmax, a.lse, a.c->d_len, err, a.gate);
   return hipGetLastError();
 }

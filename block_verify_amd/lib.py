@@ -33,6 +33,7 @@ EXPORTED = [
     "specdec_prefill", "specdec_round_state_bytes", "specdec_round_ws_bytes", "specdec_round_create",
     "specdec_round_destroy", "specdec_round_prefill", "specdec_round_reset", "specdec_verify_round",
     "specdec_check", "specdec_last_hip_error", "specdec_status_str", "specdec_philox4x64",
+    "specdec_round_graph", "specdec_round_graph_launch",
 ]
 
 
@@ -61,7 +62,8 @@ class RoundDesc(C.Structure):
                 ("table_len", C.c_int32), ("d_noise", C.c_void_p), ("noise_rows", C.c_int32),
                 ("philox_seed", C.c_uint64), ("d_state", C.c_void_p), ("d_ws", C.c_void_p),
                 ("ws_bytes", C.c_size_t), ("d_draft_ws", C.c_void_p), ("draft_ws_bytes", C.c_size_t),
-                ("d_round_ws", C.c_void_p), ("round_ws_bytes", C.c_size_t), ("state_cap", C.c_int32)]
+                ("d_round_ws", C.c_void_p), ("round_ws_bytes", C.c_size_t), ("state_cap", C.c_int32),
+                ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int32)]
 
 
 def load_library(path: str = _LIB_PATH) -> C.CDLL:
@@ -95,6 +97,8 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
         "specdec_last_hip_error": (i32, []),
         "specdec_status_str": (C.c_char_p, [C.c_int]),
         "specdec_philox4x64": (C.c_int, [vp, vp, i32, vp, vp]),
+        "specdec_round_graph": (C.c_int, [vp]),
+        "specdec_round_graph_launch": (C.c_int, [vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -186,11 +190,19 @@ class Cache:
     def length(self) -> int:
         return int(self.len.item())
 
-    def kv(self) -> torch.Tensor:
-        """bf16 bit view [L][2][n_kv][max_len][hd] (int16) of the cache."""
+    def kv(self):
+        """bf16 bit views (int16) of the cache: K [L][n_kv][max_len][hd] and V [L][n_kv][max_len][hd].
+
+        V is stored transposed ([n_kv][hd][lp] per layer); the view returned
+        here is transposed back (a strided view, no copy).
+        """
         sh = self.shape
-        n = sh.n_layers * 2 * sh.n_kv_heads * self.max_len * sh.head_dim
-        return self.mem[: 2 * n].view(torch.int16).view(sh.n_layers, 2, sh.n_kv_heads, self.max_len, sh.head_dim)
+        lp = (self.max_len + 63) // 64 * 64
+        per = sh.n_kv_heads * lp * sh.head_dim
+        raw = self.mem[: 2 * sh.n_layers * 2 * per].view(torch.int16).view(sh.n_layers, 2, per)
+        k = raw[:, 0].view(sh.n_layers, sh.n_kv_heads, lp, sh.head_dim)[:, :, : self.max_len]
+        v = raw[:, 1].view(sh.n_layers, sh.n_kv_heads, sh.head_dim, lp).transpose(2, 3)[:, :, : self.max_len]
+        return k, v
 
     def trim(self, new_len: int, ws: "Workspace", stream=None) -> None:
         check(lib().specdec_kv_trim(self.handle, new_len, ws.mem.data_ptr(), _stream(stream)), "kv_trim")
@@ -247,7 +259,8 @@ class Round:
 
     def __init__(self, target: Model, k: int, *, mode=GREEDY, bonus=True, schedule=SCHEDULE_A,
                  draft_source=DRAFT_TABLE, table: np.ndarray | None = None, draft: Model | None = None,
-                 noise: np.ndarray | None = None, seed: int = 3, max_len: int, cap: int = 1024, device="cuda"):
+                 noise: np.ndarray | None = None, seed: int = 3, max_len: int, cap: int = 1024, device="cuda",
+                 events=None, n_events: int = 0):
         L = lib()
         self.target, self.draft, self.k = target, draft, k
         self.schedule, self.mode, self.draft_source = schedule, mode, draft_source
@@ -283,6 +296,11 @@ class Round:
             d.d_draft_ws, d.draft_ws_bytes = self.dws.mem.data_ptr(), self.dws.nbytes
         d.d_round_ws, d.round_ws_bytes = self.rws.data_ptr(), self.rws.numel()
         d.state_cap = cap
+        if events is not None:
+            d.events = C.cast(events, C.POINTER(C.c_void_p))
+            d.n_events = n_events
+        self._events = events
+        self._calls = 0
         self.desc = d
         h = C.c_void_p()
         check(L.specdec_round_create(C.byref(d), C.byref(h)), "round_create")
@@ -299,6 +317,11 @@ class Round:
 
     def step(self, stream=None) -> None:
         check(lib().specdec_verify_round(self.handle, _stream(stream)), "verify_round")
+        self._calls += 1
+
+    def calls(self) -> int:
+        """Rounds enqueued so far (the index the library uses for its event ring)."""
+        return self._calls
 
     def read_state(self):
         raw = self.state.cpu().numpy()
@@ -306,16 +329,32 @@ class Round:
         toks = raw[C.sizeof(RoundState):].view(np.int32)
         return st, toks[: min(st.n_committed, self.cap)].copy()
 
-    def run(self, n_new: int, stream=None, max_rounds: int = 100000):
-        """Reset to the post-prefill state and run rounds until n_new tokens are committed."""
+    def capture(self) -> None:
+        """Capture the round as four HIP graphs (replayed by run(graph=True))."""
+        check(lib().specdec_round_graph(self.handle), "round_graph")
+
+    def committed(self) -> int:
+        return int(self.state[:4].view(torch.int32).item())
+
+    def run(self, n_new: int, stream=None, graph: bool = False, max_rounds: int = 100000):
+        """Reset to the post-prefill state and run rounds until n_new tokens are committed.
+
+        Each host check launches ceil((n_new - n) / (k + 1)) rounds first: a
+        round commits at most k + 1 tokens, so every one of them is needed
+        (rounds past the target would return at once on the device anyway).
+        """
         self.reset(n_new, stream)
-        rounds = 0
-        while rounds < max_rounds:
-            self.step(stream)
-            rounds += 1
-            st, _ = self.read_state()
-            if st.n_committed >= n_new:
-                break
+        rounds, n = 0, 0
+        while rounds < max_rounds and n < n_new:
+            batch = max(1, -(-(n_new - n) // (self.k + 1)))
+            if graph:
+                check(lib().specdec_round_graph_launch(self.handle, batch, _stream(stream)), "round_graph_launch")
+                self._calls += batch
+            else:
+                for _ in range(batch):
+                    self.step(stream)
+            rounds += batch
+            n = self.committed()
         return self.read_state()
 
     def __del__(self):

@@ -123,8 +123,11 @@ void specdec_model_destroy(specdec_model* m);
 
 /* ------------------------------------------------------------------ cache */
 
-/* Bytes of a KV cache of `max_len` positions: bf16 K and V
- * [layer][K|V][kv head][max_len][head_dim] plus the RoPE table. */
+/* Bytes of a KV cache of `max_len` positions (at most 65536).  With
+ * lp = max_len rounded up to 64, each layer holds bf16 K as
+ * [kv head][lp][head_dim] followed by bf16 V transposed as
+ * [kv head][head_dim][lp]; then the fp32 RoPE table [max_len][head_dim/2]
+ * of (cos, sin). */
 int specdec_cache_bytes(const specdec_model_desc* desc, int32_t max_len, size_t* bytes);
 
 /* Cache handle over `d_mem` (cache_bytes).  `d_len` is a caller-owned
@@ -208,6 +211,10 @@ typedef struct {
   void* d_round_ws;             /* round scratch (specdec_round_ws_bytes) */
   size_t round_ws_bytes;
   int32_t state_cap;            /* capacity of the state's token array (specdec_round_state_bytes(cap)) */
+  void* const* events;          /* optional hipEvent_t ring for per-term timing, or NULL */
+  int32_t n_events;             /* ring size (>= 5); each round records 5 events in order:
+                                   start, after draft provision, after verify, after accept,
+                                   after repair; round i uses entries 5*i .. 5*i+4 modulo the ring */
 } specdec_round_desc;
 
 int specdec_round_state_bytes(int32_t cap, size_t* bytes);
@@ -235,6 +242,19 @@ int specdec_round_reset(specdec_round* r, int32_t n_target, void* stream);
  * pending-token form (schedule B).  No host synchronisation; once
  * n_committed >= n_target the round's kernels return without work. */
 int specdec_verify_round(specdec_round* r, void* stream);
+
+/* Capture the round (exactly the work of specdec_verify_round) as four HIP
+ * graphs owned by the round handle: round start + draft provision, block
+ * verify, acceptance + trim, repair.  Every dynamic value a round uses
+ * (lengths, tokens, counters) lives in device memory, so one set of graphs
+ * serves every position.  Captures on an internal stream; no device memory
+ * is allocated. */
+int specdec_round_graph(specdec_round* r);
+
+/* Enqueue `n_rounds` rounds on `stream` as replays of the four graphs.  The
+ * per-term events of the ring (if configured) are recorded between the
+ * graphs, exactly as specdec_verify_round records them. */
+int specdec_round_graph_launch(specdec_round* r, int32_t n_rounds, void* stream);
 
 /* Read the device error word of `d_ws` (synchronises `stream`): returns
  * SPECDEC_OK or SPECDEC_EDEVICE and stores the bits in *bits (may be NULL). */

@@ -1,0 +1,148 @@
+"""GPU parity at the full 1.5B shape and 2048-token context (the benchmark's workload).
+
+The oracle runs its own float64 prefill of the same 2048 seeded prompt ids on
+the host (tens of seconds), then the same verify blocks; sampled K/V entries
+of the cache; the full 64-token job under schedules A and B against the GPU's
+own greedy decode (bit for bit) and against the oracle (teacher-forced, exact
+except where the oracle's top-2 margin is below 0.1).
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import MARGIN, assert_logits_close, bf16_bits_to_f64, oracle_margin, say, to_np
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+P, N_NEW, K, C = 2048, 64, 4, 0.46
+
+
+@pytest.fixture(scope="module")
+def big():
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import QWEN_1_5B, SEED_TARGET
+    from block_verify_amd.synth import make_prompt, make_weights
+    from oracle.model import OracleCache, OracleWeights, prefill
+    S = QWEN_1_5B
+    t0 = time.time()
+    w = make_weights(S, SEED_TARGET)
+    model = b.Model(S, w)
+    prompt = make_prompt(S.vocab, P)
+    say(f"1.5B: weights + pack {time.time() - t0:.1f} s")
+    max_len = P + 256
+    cache = b.Cache(S, max_len)
+    ws = b.Workspace(S, max_len)
+    saved = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(model, cache, torch.from_numpy(prompt).cuda(), ws, logits=saved)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    ow = OracleWeights(S, w)
+    oc = OracleCache(S, max_len)
+    o_saved = prefill(ow, oc, prompt)
+    say(f"1.5B: oracle float64 prefill of {P} tokens {time.time() - t0:.1f} s")
+    return dict(b=b, S=S, w=w, model=model, prompt=prompt, cache=cache, ws=ws, saved=to_np(saved),
+                ow=ow, oc=oc, o_saved=o_saved, max_len=max_len)
+
+
+def test_prefill_saved_next_logits(big):
+    assert big["cache"].length() == P
+    assert_logits_close(big["saved"], big["o_saved"], "1.5B saved_next")
+    assert big["ws"].error_bits() == 0
+
+
+def test_kv_cache_sampled_entries(big):
+    S = big["S"]
+    kk, vv = big["cache"].kv()
+    rng = np.random.default_rng(0)
+    for l in rng.choice(S.n_layers, 6, replace=False):
+        pos = rng.choice(P, 64, replace=False)
+        pt = torch.from_numpy(pos).cuda()
+        g = bf16_bits_to_f64(np.stack([to_np(kk[int(l)][:, pt, :]), to_np(vv[int(l)][:, pt, :])]))
+        ok = np.stack([big["oc"].k[l][:, pos], big["oc"].v[l][:, pos]])
+        scale = np.abs(ok).max()
+        err = np.abs(g - ok).max()
+        say(f"layer {l}: K/V max err {err:.3e} of scale {scale:.3f}")
+        assert err <= 1e-2 * scale
+
+
+@pytest.mark.parametrize("rows", [1, 4, 5, 9])
+def test_verify_block_logits(big, rows):
+    from oracle.model import forward
+    b, S = big["b"], big["S"]
+    toks = np.random.default_rng(100 + rows).integers(0, S.vocab, rows)
+    logits = torch.empty((rows, S.vocab), dtype=torch.float32, device="cuda")
+    am = torch.empty(rows, dtype=torch.int32, device="cuda")
+    b.decode_step(big["model"], big["cache"], torch.from_numpy(toks.astype(np.int32)).cuda(), big["ws"],
+                  logits=logits, argmax=am)
+    assert big["cache"].length() == P + rows
+    big["cache"].trim(P, big["ws"])
+    oc = big["oc"].clone()
+    ol = forward(big["ow"], oc, toks)
+    g = to_np(logits)
+    assert_logits_close(g, ol, f"1.5B verify rows={rows}")
+    gam = to_np(am)
+    assert np.array_equal(gam, g.argmax(axis=1))
+    for i in range(rows):
+        if oracle_margin(ol[i]) >= MARGIN:
+            assert gam[i] == int(np.argmax(ol[i]))
+    assert big["ws"].error_bits() == 0
+
+
+def test_batch_invariance_full_size(big):
+    b, S = big["b"], big["S"]
+    toks = torch.from_numpy(np.array([11, 222, 3333, 44444, 151935], np.int32)).cuda()
+    lb = torch.empty((5, S.vocab), dtype=torch.float32, device="cuda")
+    b.decode_step(big["model"], big["cache"], toks, big["ws"], logits=lb)
+    big["cache"].trim(P, big["ws"])
+    ls = torch.empty((5, S.vocab), dtype=torch.float32, device="cuda")
+    for i in range(5):
+        b.decode_step(big["model"], big["cache"], toks[i:i + 1], big["ws"], logits=ls[i])
+    big["cache"].trim(P, big["ws"])
+    assert torch.equal(lb.view(torch.int32), ls.view(torch.int32))
+
+
+@pytest.fixture(scope="module")
+def ar_tokens(big):
+    b, S = big["b"], big["S"]
+    n = N_NEW + K + 2
+    toks = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    toks[0] = int(np.argmax(big["saved"]))
+    scratch = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    for i in range(n - 1):
+        b.decode_step(big["model"], big["cache"], toks[i:i + 1], big["ws"], logits=scratch, argmax=toks[i + 1:i + 2])
+    big["cache"].trim(P, big["ws"])
+    return [int(x) for x in to_np(toks)[:n]]
+
+
+def test_gpu_ar_against_oracle_teacher_forced(big, ar_tokens):
+    from oracle.model import forward
+    oc = big["oc"].clone()
+    toks = ar_tokens[:N_NEW]
+    rows = np.concatenate([big["o_saved"][None], forward(big["ow"], oc, toks[:-1])])
+    exempt = 0
+    for i, t in enumerate(toks):
+        a = int(np.argmax(rows[i]))
+        if a != t:
+            assert oracle_margin(rows[i]) < MARGIN, f"token {i}: gpu {t} oracle {a} margin {oracle_margin(rows[i])}"
+            exempt += 1
+    say(f"1.5B AR vs oracle: {N_NEW} tokens, {exempt} differ where the oracle top-2 margin < {MARGIN}")
+
+
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_spec_job_equals_gpu_ar(big, ar_tokens, schedule):
+    from block_verify_amd.synth import make_draft_table
+    b, S = big["b"], big["S"]
+    table = make_draft_table(np.array(ar_tokens), S.vocab, C)
+    r = b.Round(big["model"], K, schedule=schedule, table=table, max_len=big["max_len"])
+    r.prefill(big["prompt"])
+    st, toks = r.run(N_NEW)
+    assert list(toks[:N_NEW]) == ar_tokens[:N_NEW]
+    assert r.tcache.length() == P + st.n_committed - (1 if schedule == 1 else 0)
+    assert r.ws.error_bits() == 0
+    examined = 0
+    n0 = 0
+    # accepted drafts per round follow the table's corruption pattern exactly
+    say(f"schedule {'AB'[schedule]}: {st.round} rounds, {st.accepted_total} drafts accepted")
+    assert st.round >= N_NEW // (K + 1)

@@ -70,10 +70,11 @@ def test_prefill_logits_and_cache(env, chunk):
     assert am == int(np.argmax(logits))
     ref_lse = np.log(np.sum(np.exp(logits.astype(np.float64) - logits.max()))) + logits.max()
     assert abs(lse - ref_lse) < 1e-4
-    kv = to_np(cache.kv())
+    kk, vv = cache.kv()
+    kk, vv = to_np(kk.contiguous()), to_np(vv.contiguous())
     for l in range(env["shape"].n_layers):
-        gk = bf16_bits_to_f64(kv[l, 0, :, :P])
-        gv = bf16_bits_to_f64(kv[l, 1, :, :P])
+        gk = bf16_bits_to_f64(kk[l, :, :P])
+        gv = bf16_bits_to_f64(vv[l, :, :P])
         for g, o, nm in ((gk, oc.k[l][:, :P], "K"), (gv, oc.v[l][:, :P], "V")):
             scale = np.abs(o).max()
             err = np.abs(g - o).max()
@@ -110,13 +111,15 @@ def test_batch_invariance_block_equals_single_steps(env):
     singles = [_gpu_forward(env, c2, w2, toks[i:i + 1]) for i in range(5)]
     ls = np.concatenate([s[0] for s in singles])
     assert np.array_equal(lb.view(np.uint32), ls.view(np.uint32))
-    assert np.array_equal(to_np(c1.kv()), to_np(c2.kv()))
+    assert np.array_equal(ab, np.concatenate([s[1] for s in singles]))
+    n = P + len(toks)   # positions past the length were never written
+    for a, b_ in zip(c1.kv(), c2.kv()):
+        assert torch.equal(a[:, :, :n], b_[:, :, :n])
     # prefill in different chunkings gives the same cache bits too
     c3, w3 = _fresh(env)
     _gpu_prefill(env, c3, w3, env["prompt"], chunk=13)
-    kv1 = to_np(c1.kv())[:, :, :, :P]
-    kv3 = to_np(c3.kv())[:, :, :, :P]
-    assert np.array_equal(kv1, kv3)
+    for a, b_ in zip(c1.kv(), c3.kv()):
+        assert torch.equal(a[:, :, :P], b_[:, :, :P])
 
 
 def _gpu_ar(env, n, max_len=512):
@@ -167,6 +170,25 @@ def test_spec_rounds_equal_gpu_ar(env, gpu_ar, schedule, c):
         assert st.accepted_total >= (st.round - 1) * K
     if c == 1.0:
         assert st.accepted_total == 0
+
+
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_graph_replay_commits_the_same_tokens(env, gpu_ar, schedule):
+    """One captured round replayed as a HIP graph: same tokens, same cache length, several jobs in a row."""
+    from block_verify_amd.synth import make_draft_table
+    b = env["b"]
+    table = make_draft_table(np.array(gpu_ar), env["shape"].vocab, 0.4)
+    r = b.Round(env["model"], K, schedule=schedule, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    r.capture()
+    for rep in range(3):
+        st, toks = r.run(N_NEW, graph=True)
+        assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+        assert r.tcache.length() == P + st.n_committed - (1 if schedule == 1 else 0)
+        # eager rounds interleaved with graph replays stay consistent
+        st2, toks2 = r.run(N_NEW)
+        assert list(toks2[:N_NEW]) == gpu_ar[:N_NEW]
+    assert r.ws.error_bits() == 0
 
 
 def test_spec_no_bonus(env, gpu_ar):
