@@ -135,6 +135,59 @@ def run_spec(b, model, shape, prompt, table, k, schedule, steps, warmup, n_new, 
                 prompt_len=len(prompt), t_len=r.tcache.length())
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "verify_forward_1.5b_2k_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per 5-row verify forward at a 2048-token context, from the committed
+    FETCH_SIZE / WRITE_SIZE summary; None once a kernel source it lists has changed."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    val = None
+    for line in text.splitlines():
+        f = line.split()
+        if len(f) == 3 and f[0] == "traffic_bytes_per_forward":
+            val = int(f[2])
+        elif len(f) == 3 and f[0] == "sha256":
+            with open(os.path.join(ROOT, f[1]), "rb") as fh:
+                if hashlib.sha256(fh.read()).hexdigest() != f[2]:
+                    return None
+    return val
+
+
+def profile_forwards(b, model, shape, prompt_t, rows, n, max_len, torch):
+    """Verify forwards at the prompt's context (trimmed back after each), timed with
+    hipEvents, then a plain 256 MiB device-to-device copy (calibrates traffic counters)."""
+    cache = b.Cache(shape, max_len)
+    ws = b.Workspace(shape, max_len)
+    logits = torch.empty((rows, shape.vocab), dtype=torch.float32, device="cuda")
+    b.prefill(model, cache, prompt_t, ws, logits=logits[0])
+    P = int(prompt_t.numel())
+    toks = torch.arange(rows, dtype=torch.int32, device="cuda") * 977 + 13
+    ev = HipEvents(2 * n)
+    hip = ev.hip
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(n):
+        hip.hipEventRecord(ev.arr[2 * i], stream)
+        b.decode_step(model, cache, toks, ws, logits=logits)
+        hip.hipEventRecord(ev.arr[2 * i + 1], stream)
+        cache.trim(P, ws)
+    torch.cuda.synchronize()
+    us = [1e3 * ev.ms(2 * i, 2 * i + 1) for i in range(n)]
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    vb = verify_bytes(shape, P, rows)
+    print(json.dumps({"mode": "forward-only", "rows": rows, "context": P, "forwards": n,
+                      "us_per_forward_median": float(np.median(us)), "algorithmic_bytes": vb,
+                      "copy_bytes": 256 << 20, "error_bits": ws.error_bits()}), flush=True)
+
+
 def cpu_baseline(shape, weights, k, tau, budget_s=15.0, context=2048):
     """Time the oracle's schedule-B round (k+1-row verify forward + greedy accept + trim).
 
@@ -193,6 +246,9 @@ def main():
     ap.add_argument("--n-new", type=int, default=64)
     ap.add_argument("--corrupt", type=float, default=0.46)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward-only", type=int, default=0,
+                    help="profiling mode: after the prefill run this many verify forwards of k+1 rows "
+                         "(no jobs), then one 256 MiB device copy of known size for counter calibration")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -216,6 +272,9 @@ def main():
     prompt = make_prompt(S.vocab, P)
     prompt_t = torch.from_numpy(prompt).cuda()
 
+    if args.forward_only:
+        profile_forwards(b, model, S, prompt_t, k + 1, args.forward_only, max_len, torch)
+        return
     ar_toks, ar_s = gpu_ar(b, model, S, prompt_t, args.n_new + k + 2, max_len, torch)
     ar_tok_s = (args.n_new + k + 1) / ar_s
     log(f"AR: {ar_tok_s:.1f} tok/s")
@@ -238,6 +297,7 @@ def main():
     vb = verify_bytes(S, P + args.n_new // 2, rows)
     v_ms = float(np.mean(main_r["terms"]["verify"]))
     achieved = vb / (v_ms * 1e-3) / 1e9
+    traffic = measured_traffic() if (P == 2048 and rows == 5 and k == 4) else None
     rounds_per_job = main_r["rounds"] / args.steps
     tau = args.n_new / rounds_per_job
     out = {
@@ -249,7 +309,7 @@ def main():
                                f"table drafts corrupt p={args.corrupt}, greedy, schedule {args.schedule}",
                    "context": P, "k": k, "n_new": args.n_new, "schedule": args.schedule},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": f"verify forward ({rows} rows), {vb} algorithmic bytes, {v_ms * 1e3:.1f} us avg"},
         "terms_ms": terms,
         "schedule_A_tok_s": round(args.n_new * args.steps / res["A"]["seconds"], 2),

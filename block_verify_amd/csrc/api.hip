@@ -624,6 +624,21 @@ static hipError_t enqueue_segment(specdec_round* r, hipStream_t s, int seg) {
   return e;
 }
 
+int specdec_round_debug_view(const specdec_round* r, int32_t which, void** d_ptr, size_t* bytes) {
+  if (!r || !d_ptr || !bytes) return SPECDEC_EINVAL;
+  const RoundDev& v = r->dev;
+  const size_t V = (size_t)v.V;
+  switch (which) {
+    case 0: *d_ptr = v.saved_logits; *bytes = V * 4; break;
+    case 1: *d_ptr = v.rows_logits; *bytes = (size_t)(v.k + 1) * V * 4; break;
+    case 2: *d_ptr = v.q_logits; *bytes = (size_t)v.k * V * 4; break;
+    case 3: *d_ptr = v.block; *bytes = (size_t)(v.k + 1) * 4; break;
+    case 4: *d_ptr = v.dbg; *bytes = (2 * kMaxK + 2) * 4; break;
+    default: return SPECDEC_EINVAL;
+  }
+  return SPECDEC_OK;
+}
+
 // Test hook: Philox4x64-10 words for n (counter, key) pairs (device arrays).
 int specdec_philox4x64(const uint64_t* d_ctr, const uint64_t* d_key, int32_t n, uint64_t* d_out, void* stream) {
   if (!d_ctr || !d_key || !d_out || n <= 0) return SPECDEC_EINVAL;

@@ -33,7 +33,7 @@ EXPORTED = [
     "specdec_prefill", "specdec_round_state_bytes", "specdec_round_ws_bytes", "specdec_round_create",
     "specdec_round_destroy", "specdec_round_prefill", "specdec_round_reset", "specdec_verify_round",
     "specdec_check", "specdec_last_hip_error", "specdec_status_str", "specdec_philox4x64",
-    "specdec_round_graph", "specdec_round_graph_launch",
+    "specdec_round_graph", "specdec_round_graph_launch", "specdec_round_debug_view",
 ]
 
 
@@ -99,6 +99,7 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
         "specdec_philox4x64": (C.c_int, [vp, vp, i32, vp, vp]),
         "specdec_round_graph": (C.c_int, [vp]),
         "specdec_round_graph_launch": (C.c_int, [vp, i32, vp]),
+        "specdec_round_debug_view": (C.c_int, [vp, i32, P(vp), P(sz)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -322,6 +323,15 @@ class Round:
     def calls(self) -> int:
         """Rounds enqueued so far (the index the library uses for its event ring)."""
         return self._calls
+
+    def debug_view(self, which: int, dtype=torch.float32) -> torch.Tensor:
+        """A torch view (no copy) of an internal round buffer (see specdec_round_debug_view)."""
+        ptr, nb = C.c_void_p(), C.c_size_t()
+        check(lib().specdec_round_debug_view(self.handle, which, C.byref(ptr), C.byref(nb)), "debug_view")
+        base = self.rws.data_ptr()
+        off = ptr.value - base
+        assert 0 <= off and off + nb.value <= self.rws.numel()
+        return self.rws[off:off + nb.value].view(dtype)
 
     def read_state(self):
         raw = self.state.cpu().numpy()

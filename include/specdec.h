@@ -256,6 +256,14 @@ int specdec_round_graph(specdec_round* r);
  * graphs, exactly as specdec_verify_round records them. */
 int specdec_round_graph_launch(specdec_round* r, int32_t n_rounds, void* stream);
 
+/* Device views of a round's internal buffers, for inspection by tests:
+ * which = 0 saved_next logits fp32 [V] (schedule A; overwritten by the repair),
+ * 1 verify logits fp32 [k+1][V], 2 noisy draft logits z + noise fp32 [k][V],
+ * 3 verify block tokens int32 [k+1], 4 the last stochastic round's
+ * (ratio, u_accept) pairs fp32 [2*SPECDEC_MAX_K] then (u_resample, m).
+ * Returns the pointer and the byte size; nothing is copied. */
+int specdec_round_debug_view(const specdec_round* r, int32_t which, void** d_ptr, size_t* bytes);
+
 /* Read the device error word of `d_ws` (synchronises `stream`): returns
  * SPECDEC_OK or SPECDEC_EDEVICE and stores the bits in *bits (may be NULL). */
 int specdec_check(const void* d_ws, int32_t* bits, void* stream);
