@@ -63,3 +63,64 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b).astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# Stochastic rounds: the GPU's decisions against the oracle's rule on the GPU's
+# own logits.  Probabilities on the GPU are float32 (expf of logit - lse), the
+# oracle's float64, so a decision whose uniform lies within BOUNDARY of the
+# threshold (accept test) or of a CDF step (inverse-CDF sample, relative to the
+# total mass) may legitimately differ; such cases are counted, not failed.
+BOUNDARY = 1e-6
+
+
+def softmax64(x):
+    x = np.asarray(x, np.float64)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def near_cdf_step(weights, u, i):
+    """True when u * total lies within BOUNDARY * total of the CDF steps around index i."""
+    c = np.cumsum(np.asarray(weights, np.float64))
+    t = u * c[-1]
+    lo = c[i - 1] if i > 0 else 0.0
+    return min(abs(t - lo), abs(t - c[min(i, len(c) - 1)])) < BOUNDARY * c[-1]
+
+
+def check_stochastic_round(saved, rows, qz, drafts, m_gpu, com_gpu, seed, rnd):
+    """Replay one schedule-A round of modified rejection sampling in the oracle.
+
+    saved: target logits before the round ([V]); rows: the k verify rows;
+    qz: the k noisy draft logits the GPU drew from; drafts: the GPU's k draft
+    tokens; m_gpu / com_gpu: the GPU's accepted count and committed tokens.
+    Returns the number of boundary exemptions (0 or more); raises on a
+    decision that differs away from a boundary.
+    """
+    from oracle import accept as acc
+    from oracle import philox
+    k = len(drafts)
+    exempt = 0
+    q_rows = [softmax64(qz[j]) for j in range(k)]
+    for j in range(k):
+        u = philox.uniform(seed, rnd, j, philox.STREAM_DRAFT)
+        d = acc.sample_inverse_cdf(q_rows[j], u)
+        if d != int(drafts[j]):
+            assert near_cdf_step(q_rows[j], u, int(drafts[j])), f"round {rnd} draft {j}: gpu {drafts[j]} oracle {d}"
+            exempt += 1
+    p_rows = [softmax64(saved)] + [softmax64(r) for r in rows]
+    ua = [philox.uniform(seed, rnd, j, philox.STREAM_ACCEPT) for j in range(k)]
+    ur = philox.uniform(seed, rnd, 0, philox.STREAM_RESAMPLE)
+    m, com, info = acc.stochastic_accept(p_rows, q_rows, [int(x) for x in drafts], ua, ur)
+    if m == m_gpu and list(com) == [int(x) for x in com_gpu]:
+        return exempt
+    near_accept = any(abs(ua[j] - info["ratios"][j]) < BOUNDARY for j in range(len(info["ratios"])))
+    if m == m_gpu:
+        j = m
+        src = acc.residual(p_rows[j], q_rows[j]) if j < k else p_rows[k]
+        if j < k and src.sum() <= acc.RESIDUAL_EPS:
+            src = p_rows[j]
+        near_sample = near_cdf_step(src, ur, int(com_gpu[-1]))
+    else:
+        near_sample = False
+    assert near_accept or near_sample, f"round {rnd}: gpu m={m_gpu} {list(com_gpu)} oracle m={m} {com}"
+    return exempt + 1

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import MARGIN, assert_logits_close, bf16_bits_to_f64, oracle_margin, say, to_np
+from gpu_helpers import (MARGIN, assert_logits_close, bf16_bits_to_f64, check_stochastic_round, oracle_margin, say,
+                         to_np)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -146,3 +147,56 @@ def test_spec_job_equals_gpu_ar(big, ar_tokens, schedule):
     # accepted drafts per round follow the table's corruption pattern exactly
     say(f"schedule {'AB'[schedule]}: {st.round} rounds, {st.accepted_total} drafts accepted")
     assert st.round >= N_NEW // (K + 1)
+
+
+P4 = 4096
+
+
+def test_stochastic_4k_rounds_match_oracle(big):
+    """Modified rejection sampling at a 4096-token context (noisy self-draft, Philox seed 3):
+    the first rounds' verify rows and saved_next against the oracle's float64 forward,
+    every round's draft samples and decisions against the oracle rule on the GPU's logits."""
+    import torch
+    from block_verify_amd.synth import make_noise, make_prompt
+    from oracle.model import OracleCache, forward, prefill
+    b, S = big["b"], big["S"]
+    V, seed = S.vocab, 3
+    prompt = make_prompt(S.vocab, P4)
+    noise = make_noise(N_NEW + 2 * K + 2, V)
+    r = b.Round(big["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=seed,
+                max_len=P4 + 256)
+    r.prefill(prompt)
+    r.reset(N_NEW)
+    t0 = time.time()
+    oc = OracleCache(S, P4 + 256)
+    o_saved = prefill(big["ow"], oc, prompt)
+    say(f"4K: oracle float64 prefill {time.time() - t0:.1f} s")
+    exempt, n0, ms, checked = 0, 0, [], 0
+    while n0 < N_NEW:
+        saved = to_np(r.debug_view(0)).copy()
+        st0, _ = r.read_state()
+        teacher = st0.round < 3
+        if teacher:
+            assert_logits_close(saved, o_saved, f"4K round {st0.round} saved_next")
+        r.step()
+        st, toks = r.read_state()
+        rows = to_np(r.debug_view(1)).reshape(K + 1, V)[:K].copy()
+        qz = to_np(r.debug_view(2)).reshape(K, V).copy()
+        drafts = to_np(r.debug_view(3, torch.int32))[:K].copy()
+        assert np.array_equal(qz[0], (saved + noise[n0]).astype(np.float32))
+        for j in range(1, K):
+            assert np.array_equal(qz[j], (rows[j - 1] + noise[n0 + j]).astype(np.float32))
+        com = toks[n0:st.n_committed]
+        if teacher:
+            ol = forward(big["ow"], oc.clone(), [int(x) for x in drafts])
+            assert_logits_close(rows, ol, f"4K round {st0.round} verify rows")
+            o_saved = forward(big["ow"], oc, [int(x) for x in com])[-1]
+            checked += 1
+        exempt += check_stochastic_round(saved, rows, qz, drafts, st.m_last, com, seed, st0.round)
+        assert r.tcache.length() == P4 + st.n_committed
+        ms.append(st.m_last)
+        n0 = st.n_committed
+    assert r.ws.error_bits() == 0
+    say(f"4K stochastic: {len(ms)} rounds, accepted {ms}, {exempt} boundary exemptions, "
+        f"{checked} rounds teacher-forced against the oracle")
+    assert exempt <= 2

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (assert_logits_close, bf16_bits_to_f64, say, to_np, tokens_match_teacher_forced)
+from gpu_helpers import (assert_logits_close, bf16_bits_to_f64, check_stochastic_round, say, to_np,
+                         tokens_match_teacher_forced)
 
 pytestmark = pytest.mark.gpu
 
@@ -251,3 +252,103 @@ def test_philox_matches_oracle_words():
     got = b.philox4x64(ctr, key)
     for i in list(range(64)) + list(range(64, n, 97)):
         assert tuple(int(x) for x in got[i]) == philox4x64_10(ctr[i], key[i])
+
+
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_draft_model_rounds_keep_both_caches(env, gpu_ar, schedule):
+    """A separate draft model with its own cache: k draft steps per round (tokens from the
+    table), both caches trimmed to t+m and repaired; the draft cache ends up holding the
+    draft model's K/V of prompt + committed tokens."""
+    from block_verify_amd.shapes import SEED_DRAFT
+    from block_verify_amd.synth import make_draft_table, make_weights
+    from oracle.model import OracleCache, OracleWeights, prefill
+    b, S = env["b"], env["shape"]
+    dw = make_weights(S, SEED_DRAFT)
+    draft = b.Model(S, dw)
+    table = make_draft_table(np.array(gpu_ar), S.vocab, 0.4)
+    r = b.Round(env["model"], K, schedule=schedule, draft_source=b.DRAFT_MODEL, draft=draft, table=table,
+                max_len=512)
+    r.prefill(env["prompt"])
+    for rep in range(2):
+        st, toks = r.run(N_NEW)
+        assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+        assert r.tcache.length() == P + st.n_committed - (1 if schedule == 1 else 0)
+        assert r.dcache.length() == P + st.n_committed
+        assert r.ws.error_bits() == 0 and r.dws.error_bits() == 0
+    seq = list(env["prompt"]) + [int(x) for x in toks[:st.n_committed]]
+    ow = OracleWeights(S, dw)
+    oc = OracleCache(S, len(seq) + 8)
+    prefill(ow, oc, seq)
+    kk, vv = r.dcache.kv()
+    n = len(seq)
+    for l in range(S.n_layers):
+        g = bf16_bits_to_f64(np.stack([to_np(kk[l][:, :n]), to_np(vv[l][:, :n])]))
+        o = np.stack([oc.k[l][:, :n], oc.v[l][:, :n]])
+        err = np.abs(g - o).max()
+        say(f"draft cache layer {l}: max err {err:.3e} of {np.abs(o).max():.3f}")
+        assert err <= 1e-2 * np.abs(o).max()
+
+
+def test_stochastic_rounds_match_oracle_decisions(env):
+    """Modified rejection sampling with the noisy self-draft (schedule A): per round, the
+    noisy draft logits, the verify rows, the draft samples and the accept/resample/bonus
+    decisions against the oracle on the GPU's own logits."""
+    from block_verify_amd.synth import make_noise
+    from oracle.model import OracleCache, forward, prefill
+    b, S = env["b"], env["shape"]
+    V, seed = S.vocab, 3
+    noise = make_noise(N_NEW + 2 * K + 2, V)
+    r = b.Round(env["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=seed,
+                max_len=512)
+    r.prefill(env["prompt"])
+    r.reset(N_NEW)
+    oc = OracleCache(S, 512)
+    o_saved = prefill(env["ow"], oc, env["prompt"])
+    exempt, n0, stops = 0, 0, []
+    while n0 < N_NEW:
+        saved = to_np(r.debug_view(0)).copy()
+        st0, _ = r.read_state()
+        assert_logits_close(saved, o_saved, f"round {st0.round} saved_next")
+        r.step()
+        st, toks = r.read_state()
+        rows = to_np(r.debug_view(1)).reshape(K + 1, V)[:K].copy()
+        qz = to_np(r.debug_view(2)).reshape(K, V).copy()
+        drafts = to_np(r.debug_view(3, torch.int32))[:K].copy()
+        # q_1 from saved_next, q_(j+1) from the M=1 step on d_j: equal bit for bit to verify row j plus noise
+        assert np.array_equal(qz[0], (saved + noise[n0]).astype(np.float32))
+        for j in range(1, K):
+            assert np.array_equal(qz[j], (rows[j - 1] + noise[n0 + j]).astype(np.float32))
+        ol = forward(env["ow"], oc.clone(), [int(x) for x in drafts])
+        assert_logits_close(rows, ol, f"round {st0.round} verify rows")
+        com = toks[n0:st.n_committed]
+        assert len(com) == st.m_last + 1
+        exempt += check_stochastic_round(saved, rows, qz, drafts, st.m_last, com, seed, st0.round)
+        assert r.tcache.length() == P + st.n_committed
+        stops.append(st.m_last)
+        o_saved = forward(env["ow"], oc, [int(x) for x in com])[-1]
+        n0 = st.n_committed
+    assert r.ws.error_bits() == 0
+    say(f"stochastic: {len(stops)} rounds, accepted per round {stops}, {exempt} boundary exemptions")
+    assert exempt <= 1
+
+
+def test_stochastic_job_is_deterministic_eager_and_graph(env):
+    from block_verify_amd.synth import make_noise
+    b, S = env["b"], env["shape"]
+    noise = make_noise(N_NEW + 2 * K + 2, S.vocab)
+    r = b.Round(env["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=3,
+                max_len=512)
+    r.prefill(env["prompt"])
+    st, ref = r.run(N_NEW)
+    r.capture()
+    for rep in range(2):
+        st2, toks = r.run(N_NEW, graph=True)
+        assert list(toks) == list(ref) and st2.round == st.round
+        st3, toks3 = r.run(N_NEW)
+        assert list(toks3) == list(ref)
+    r2 = b.Round(env["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=4,
+                 max_len=512)
+    r2.prefill(env["prompt"])
+    _, other = r2.run(N_NEW)
+    assert list(other[:N_NEW]) != list(ref[:N_NEW])
+    assert r.ws.error_bits() == 0
