@@ -34,6 +34,14 @@ int dims_from_desc(const specdec_model_desc* d, Dims* o) {
   if (x.nq % x.nkv != 0 || x.nq / x.nkv > 8) return SPECDEC_ESHAPE;
   if (x.H % 32 || x.F % 32 || x.qdim() % 32 || x.V % 16 || x.H % 16) return SPECDEC_ESHAPE;
   if (x.H > 8192 || x.V > (1 << 24)) return SPECDEC_ESHAPE;
+  if (x.wfmt == SPECDEC_W_Q4G64) {
+    if (x.H % 64 || x.qdim() % 64 || x.F % 64) return SPECDEC_ESHAPE;
+    // the 4-bit kernel stages up to kQ4MaxRows activation rows of its input range in LDS
+    const size_t lim = 48 * 1024;
+    if (q4_lds_bytes(kQ4MaxRows, x.H, 1) > lim || q4_lds_bytes(kQ4MaxRows, x.qdim(), 1) > lim ||
+        q4_lds_bytes(kQ4MaxRows, x.F, kMaxSplit) > lim)
+      return SPECDEC_ESHAPE;
+  }
   *o = x;
   return SPECDEC_OK;
 }
@@ -44,14 +52,27 @@ BlobLayout blob_layout(const Dims& d) {
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   b.embed = take((size_t)d.V * d.H * 2);
   b.layer.resize(d.L);
+  const bool q4 = d.wfmt == SPECDEC_W_Q4G64;
   for (int l = 0; l < d.L; ++l) {
     LayerOffsets& o = b.layer[l];
     o.attn_norm = take((size_t)d.H * 4);
-    o.wqkv = take((size_t)d.qkv_rows() * d.H * 2);
-    o.wo = take((size_t)d.H * d.qdim() * 2);
     o.mlp_norm = take((size_t)d.H * 4);
-    o.wgu = take((size_t)2 * d.F * d.H * 2);
-    o.wdown = take((size_t)d.H * d.F * 2);
+    if (q4) {
+      o.wqkv = take(q4_code_bytes(d.qkv_rows(), d.H));
+      o.s_wqkv = take(q4_scale_bytes(d.qkv_rows(), d.H));
+      o.wo = take(q4_code_bytes(d.H, d.qdim()));
+      o.s_wo = take(q4_scale_bytes(d.H, d.qdim()));
+      o.wgu = take(q4_code_bytes(2 * d.F, d.H));
+      o.s_wgu = take(q4_scale_bytes(2 * d.F, d.H));
+      o.wdown = take(q4_code_bytes(d.H, d.F));
+      o.s_wdown = take(q4_scale_bytes(d.H, d.F));
+    } else {
+      o.wqkv = take((size_t)d.qkv_rows() * d.H * 2);
+      o.wo = take((size_t)d.H * d.qdim() * 2);
+      o.wgu = take((size_t)2 * d.F * d.H * 2);
+      o.wdown = take((size_t)d.H * d.F * 2);
+      o.s_wqkv = o.s_wo = o.s_wgu = o.s_wdown = 0;
+    }
   }
   b.final_norm = take((size_t)d.H * 4);
   b.lm_head = take((size_t)d.V * d.H * 2);
@@ -160,7 +181,6 @@ int specdec_weights_bytes(const specdec_model_desc* desc, size_t* bytes) {
   int rc = dims_from_desc(desc, &d);
   if (rc) return rc;
   if (!bytes) return SPECDEC_EINVAL;
-  if (d.wfmt != SPECDEC_W_BF16) return SPECDEC_EUNSUPPORTED;
   *bytes = blob_layout(d).total;
   return SPECDEC_OK;
 }
@@ -171,8 +191,29 @@ int specdec_weights_pack(const specdec_model_desc* desc, int32_t index, const vo
   if (rc) return rc;
   if (!d_src || !d_blob) return SPECDEC_EINVAL;
   if (index < 0 || index >= 3 + 9 * d.L) return SPECDEC_EINVAL;
-  if (d.wfmt != SPECDEC_W_BF16) return SPECDEC_EUNSUPPORTED;
-  return hip_status(launch_pack(d, index, d_src, d_blob, blob_layout(d), (hipStream_t)stream));
+  const BlobLayout lay = blob_layout(d);
+  if (d.wfmt == SPECDEC_W_Q4G64 && index > 0 && index < 1 + 9 * d.L) {
+    const int l = (index - 1) / 9, which = (index - 1) % 9;
+    const LayerOffsets& o = lay.layer[l];
+    uint8_t* blob = static_cast<uint8_t*>(d_blob);
+    const int qg = d.qdim() / 16, kg = d.kvdim() / 16;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    switch (which) {
+      case 1: e = launch_pack_q4(d_src, d.qdim(), d.H, PACK_ROPE, d.hd, 0, blob + o.wqkv, blob + o.s_wqkv, st); break;
+      case 2: e = launch_pack_q4(d_src, d.kvdim(), d.H, PACK_ROPE, d.hd, qg, blob + o.wqkv, blob + o.s_wqkv, st); break;
+      case 3:
+        e = launch_pack_q4(d_src, d.kvdim(), d.H, PACK_PLAIN, d.hd, qg + kg, blob + o.wqkv, blob + o.s_wqkv, st);
+        break;
+      case 4: e = launch_pack_q4(d_src, d.H, d.qdim(), PACK_PLAIN, d.hd, 0, blob + o.wo, blob + o.s_wo, st); break;
+      case 6: e = launch_pack_q4(d_src, d.F, d.H, PACK_GATE, d.hd, 0, blob + o.wgu, blob + o.s_wgu, st); break;
+      case 7: e = launch_pack_q4(d_src, d.F, d.H, PACK_UP, d.hd, 0, blob + o.wgu, blob + o.s_wgu, st); break;
+      case 8: e = launch_pack_q4(d_src, d.H, d.F, PACK_PLAIN, d.hd, 0, blob + o.wdown, blob + o.s_wdown, st); break;
+      default: return hip_status(launch_pack(d, index, d_src, d_blob, lay, st));   // norms stay fp32 gains
+    }
+    return hip_status(e);
+  }
+  return hip_status(launch_pack(d, index, d_src, d_blob, lay, (hipStream_t)stream));
 }
 
 int specdec_model_create(const specdec_model_desc* desc, const void* d_blob, const specdec_model* share,
@@ -181,7 +222,6 @@ int specdec_model_create(const specdec_model_desc* desc, const void* d_blob, con
   int rc = dims_from_desc(desc, &d);
   if (rc) return rc;
   if (!d_blob || !out) return SPECDEC_EINVAL;
-  if (d.wfmt != SPECDEC_W_BF16) return SPECDEC_EUNSUPPORTED;
   if (share && (share->d.H != d.H || share->d.V != d.V)) return SPECDEC_ESHAPE;
   BlobLayout lay = blob_layout(d);
   const char* b = static_cast<const char*>(d_blob);
@@ -202,6 +242,13 @@ int specdec_model_create(const specdec_model_desc* desc, const void* d_blob, con
     p.wo = reinterpret_cast<const bf16x8_t*>(b + o.wo);
     p.wgu = reinterpret_cast<const bf16x8_t*>(b + o.wgu);
     p.wdown = reinterpret_cast<const bf16x8_t*>(b + o.wdown);
+    if (d.wfmt == SPECDEC_W_Q4G64) {
+      const uint8_t* ub = reinterpret_cast<const uint8_t*>(b);
+      p.q_wqkv = ub + o.wqkv; p.s_wqkv = ub + o.s_wqkv;
+      p.q_wo = ub + o.wo; p.s_wo = ub + o.s_wo;
+      p.q_wgu = ub + o.wgu; p.s_wgu = ub + o.s_wgu;
+      p.q_wdown = ub + o.wdown; p.s_wdown = ub + o.s_wdown;
+    }
   }
   *out = m;
   return SPECDEC_OK;
@@ -288,6 +335,7 @@ int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream) {
 static int check_fwd(const specdec_model* m, const specdec_cache* c, int32_t rows, size_t ws_bytes, WsPlan* plan) {
   if (!m || !c) return SPECDEC_EINVAL;
   if (rows < 1 || rows > SPECDEC_MAX_ROWS) return SPECDEC_ECAPACITY;
+  if (m->d.wfmt == SPECDEC_W_Q4G64 && rows > kQ4MaxRows) return SPECDEC_ECAPACITY;
   if (m->d.L != c->d.L || m->d.nkv != c->d.nkv || m->d.hd != c->d.hd) return SPECDEC_ESHAPE;
   *plan = ws_plan(m->d, rows, c->max_len);
   if (ws_bytes < plan->total) return SPECDEC_ECAPACITY;
@@ -317,6 +365,7 @@ int specdec_prefill(const specdec_model* m, specdec_cache* c, const int32_t* d_t
   if (!d_tokens || !d_ws || n <= 0 || chunk <= 0) return SPECDEC_EINVAL;
   if (n > c->max_len) return SPECDEC_ECAPACITY;
   if (chunk > SPECDEC_MAX_ROWS) chunk = SPECDEC_MAX_ROWS;
+  if (m->d.wfmt == SPECDEC_W_Q4G64 && chunk > kQ4MaxRows) chunk = kQ4MaxRows;
   char* ws = static_cast<char*>(d_ws);
   for (int off = 0; off < n; off += chunk) {
     int rows = n - off < chunk ? n - off : chunk;
@@ -389,8 +438,8 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   if (q.draft_source == SPECDEC_DRAFT_Q4_SELF) {
     if (!q.draft || q.draft_cache) return SPECDEC_EINVAL;
     if (q.schedule != SPECDEC_SCHEDULE_A) return SPECDEC_EUNSUPPORTED;
-    if (q.draft->d.L != d.L || q.draft->d.H != d.H || q.draft->d.V != d.V || q.draft->d.nkv != d.nkv ||
-        q.draft->d.hd != d.hd)
+    const Dims& e = q.draft->d;
+    if (e.L != d.L || e.H != d.H || e.V != d.V || e.nkv != d.nkv || e.nq != d.nq || e.hd != d.hd || e.F != d.F)
       return SPECDEC_ESHAPE;
   }
   specdec_round* r = new (std::nothrow) specdec_round;

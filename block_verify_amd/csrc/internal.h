@@ -27,6 +27,7 @@ int dims_from_desc(const specdec_model_desc* d, Dims* out);
 // Byte offsets of every packed tensor inside the weight blob.
 struct LayerOffsets {
   size_t attn_norm, wqkv, wo, mlp_norm, wgu, wdown;
+  size_t s_wqkv, s_wo, s_wgu, s_wdown;   // 4-bit models: (scale, zero) arrays
 };
 struct BlobLayout {
   size_t embed, final_norm, lm_head, total;
@@ -41,11 +42,16 @@ struct LayerPtrs {
   const bf16x8_t* wo;
   const bf16x8_t* wgu;    // tiles, gate/up interleaved by 8 rows
   const bf16x8_t* wdown;
-  // 4-bit substitute weights (weight_format == SPECDEC_W_Q4G64)
+  // 4-bit substitute weights (weight_format == SPECDEC_W_Q4G64): codes and
+  // (scale, zero) pairs of each linear, in the 4-bit kernel's block order
   const uint8_t* q_wqkv;
   const uint8_t* q_wo;
   const uint8_t* q_wgu;
   const uint8_t* q_wdown;
+  const uint8_t* s_wqkv;
+  const uint8_t* s_wo;
+  const uint8_t* s_wgu;
+  const uint8_t* s_wdown;
 };
 
 }  // namespace sd
@@ -101,6 +107,25 @@ struct FwdArgs {
   bool skip_head;        // prefill chunks before the last: no LM head, only the length advance
 };
 hipError_t launch_forward(const FwdArgs& a);
+
+// Row order of the packed linears.  Output row r of a weight goes to row
+// group g, slot i (16 slots per group): PLAIN keeps the order; ROPE puts the
+// rotate-half partners (d, d + hd/2) of a head in slots i and i + 8 of one
+// group; GATE / UP interleave 8 gate rows and the 8 matching up rows.
+enum PackKind { PACK_PLAIN = 0, PACK_ROPE = 1, PACK_GATE = 2, PACK_UP = 3 };
+
+// 4-bit group-64 linears (kernels_q4.hip).  Rows per pass of a 4-bit model.
+constexpr int kQ4MaxRows = 4;
+// Packed sizes of one 4-bit linear with N outputs and K inputs.
+inline size_t q4_code_bytes(int N, int K) { return (size_t)N * ((K + 127) / 128) * 64; }
+inline size_t q4_scale_bytes(int N, int K) { return (size_t)N * ((K + 127) / 128) * 8; }
+enum class Q4Linear { QKV, O, GATE_UP, DOWN };
+struct GemvParams;
+hipError_t launch_q4_linear(Q4Linear which, const GemvParams& p, const uint8_t* codes, const uint8_t* scales, int K,
+                            hipStream_t s);
+hipError_t launch_pack_q4(const void* src, int rows, int K, int kind, int hd, int group_base, uint8_t* codes,
+                          uint8_t* scales, hipStream_t s);
+size_t q4_lds_bytes(int rows, int K, int nsplit);
 hipError_t launch_pack(const Dims& d, int index, const void* src, void* blob, const BlobLayout& lay, hipStream_t s);
 hipError_t launch_trim(int32_t* d_len, int32_t new_len, const int32_t* d_base, int32_t* err, hipStream_t s);
 

@@ -16,13 +16,11 @@
 // of the fp32 activations.  Row results never depend on which other rows
 // share the pass: every reduction runs in an order fixed by the row's own
 // data layout, never by the row count.
-#include "internal.h"
+#include "gemv_common.h"
 
 #include <math.h>
 
 namespace sd {
-
-enum class Epi { QKV, RESID, SWIGLU, LMHEAD, PARTIAL };
 
 // K splits of the down projection (fixed per matrix, so a row's summation
 // order never depends on the row count).
@@ -34,8 +32,6 @@ hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStre
 // ---------------------------------------------------------------------------
 // Packing (setup): row-major bf16 -> MFMA weight tiles.
 // ---------------------------------------------------------------------------
-enum PackKind { PACK_PLAIN = 0, PACK_ROPE = 1, PACK_GATE = 2, PACK_UP = 3 };
-
 __global__ void pack_linear_kernel(const bf16_bits* __restrict__ src, int rows, int K, int kind, int hd,
                                    int group_base, bf16_bits* __restrict__ dst) {
   const int kc_per_row = K >> 3;
@@ -45,18 +41,7 @@ __global__ void pack_linear_kernel(const bf16_bits* __restrict__ src, int rows, 
     int r = (int)(idx / kc_per_row);
     int k = (int)(idx % kc_per_row) * 8;
     int g, i;
-    if (kind == PACK_PLAIN) {
-      g = r >> 4; i = r & 15;
-    } else if (kind == PACK_ROPE) {
-      int head = r / hd, d = r % hd, half = hd >> 1;
-      int per_head = hd >> 4;
-      if (d < half) { g = head * per_head + (d >> 3); i = d & 7; }
-      else { g = head * per_head + ((d - half) >> 3); i = 8 + ((d - half) & 7); }
-    } else if (kind == PACK_GATE) {
-      g = r >> 3; i = r & 7;
-    } else {
-      g = r >> 3; i = 8 + (r & 7);
-    }
+    pack_row_slot(kind, r, hd, g, i);
     const int KB = K >> 5;
     const int kb = k >> 5, s = (k >> 3) & 3;
     size_t d = (((size_t)(group_base + g) * KB + kb) * 64 + (s * 16 + i)) * 8;
@@ -190,58 +175,6 @@ __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, cons
   }
 }
 
-struct GemvParams {
-  const bf16x8_t* A;     // weight tiles
-  const bf16x8_t* B;     // activation tiles
-  int KB;                // k-blocks of 32 inputs
-  int n_groups;          // 16-row output groups
-  int rows;              // activation rows M
-  const int32_t* gate;
-  int32_t* err;
-  // norm (QKV, SWIGLU, LMHEAD): r from ss partials
-  const float* ss_in;
-  int H;
-  float eps;
-  // QKV
-  bf16_bits* qb;         // query operand tiles per kv head
-  bf16_bits* k_cache;
-  bf16_bits* v_cache;
-  const float2* rope;
-  const int32_t* d_len;
-  int max_len;           // cache capacity (positions)
-  int kv_stride;         // padded positions per head (K rows; V^T row length)
-  int nq, nkv, hd;
-  // RESID
-  float* x;
-  const float* gain_next;
-  bf16_bits* xb_out;
-  float* ss_out;
-  // SWIGLU
-  bf16_bits* hb_out;
-  int F;
-  // LMHEAD
-  float* logits;
-  int V;
-  float* lm_part;        // [rows][gridDim.x][3]
-  // PARTIAL (split-K): [nsplit][kMaxRows][H] partial outputs
-  float* part;
-  int nsplit;
-};
-
-// Query operand tiles: per kv head, query rows r = m * G + g (g = query head
-// within the group), 16 rows per tile, the bf16 hi and lo parts of q / sqrt(d)
-// in separate tiles: [tile][k-block over the head dim][hi|lo][64 lanes][8].
-// Lane l of a tile holds row 16 * tile + (l % 16), dims 32 * kb + 8 * (l / 16) .. +7.
-constexpr int kQTiles = kMaxRows * 8 / 16;   // up to 8 * kMaxRows query rows
-__device__ __forceinline__ size_t qtile_head(int h, int hd) { return (size_t)h * kQTiles * (hd / 32) * 2 * kTileU16; }
-__device__ __forceinline__ void qtile_put(bf16_bits* qh, int KBH, int row, int dim, float v) {
-  const int tq = row >> 4, j = row & 15, kb = dim >> 5, sg = (dim >> 3) & 3, e = dim & 7;
-  const size_t base = ((size_t)(tq * KBH + kb) * 2) * kTileU16 + (size_t)((sg * 16 + j) * 8 + e);
-  const bf16_bits hi = f2bf(v);
-  qh[base] = hi;
-  qh[base + kTileU16] = f2bf(v - bf2f(hi));
-}
-
 template <int NT, int WG_ROWS, int WK, int U, Epi E>
 __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
   if (p.gate && *p.gate == 0) return;
@@ -261,22 +194,11 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
   const int sidx = (E == Epi::PARTIAL) ? (int)(blockIdx.x % nsplit) : 0;
   const int g = (E == Epi::PARTIAL) ? (int)(blockIdx.x / nsplit) : (int)(blockIdx.x * WG_ROWS + rg);
   const int M = p.rows;
-  const int NP = p.H >> 4;
 
   // sums of squares of the normalised input, issued before the weight stream
   constexpr bool kNorm = (E == Epi::QKV || E == Epi::SWIGLU || E == Epi::LMHEAD);
   float ssv[RPW][4];
-  if constexpr (kNorm) {
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int m = w + j * NW;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int gg = lane + 64 * u;
-        ssv[j][u] = (m < M && gg < NP) ? p.ss_in[(size_t)m * NP + gg] : 0.f;
-      }
-    }
-  }
+  if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
 
   f32x4_t acc[NT];
 #pragma unroll
@@ -286,18 +208,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
     const int kb0 = s0 + (int)(((long)ks * (s1 - s0)) / WK), kb1 = s0 + (int)(((long)(ks + 1) * (s1 - s0)) / WK);
     mfma_stream<NT, U>(p.A + (size_t)g * p.KB * 64, p.B, p.KB, kb0, kb1, lane, acc);
   }
-  // r_m = 1 / sqrt(mean(x_m^2) + eps); fixed reduction order per row
-  if constexpr (kNorm) {
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int m = w + j * NW;
-      if (m < M) {
-        float sq = ((ssv[j][0] + ssv[j][1]) + ssv[j][2]) + ssv[j][3];
-        sq = warp_sum(sq);
-        if (lane == 0) rsc[m] = 1.0f / sqrtf(sq / (float)p.H + p.eps);
-      }
-    }
-  }
+  if constexpr (kNorm) norm_finish<RPW, NW>(p, w, lane, M, ssv, rsc);
   // hi + lo (columns c and c+8) in registers, then the waves' partials in LDS
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -317,126 +228,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
   }
   __syncthreads();
 
-  if constexpr (E == Epi::LMHEAD) {
-    // logits and this workgroup's (max, argmax, sum exp) per row
-    for (int idx = threadIdx.x; idx < WG_ROWS * 16 * M; idx += blockDim.x) {
-      int rr = idx / (16 * M), rem = idx % (16 * M), m = rem / 16, i = rem % 16;
-      int gg = blockIdx.x * WG_ROWS + rr;
-      float v = fin[rr][i][m] * rsc[m];
-      fin[rr][i][m] = v;
-      if (gg < p.n_groups) p.logits[(size_t)m * p.V + 16 * gg + i] = v;
-    }
-    __syncthreads();
-    if (w == 0) {
-      for (int m = 0; m < M; ++m) {
-        // lane owns entries lane and lane + 64 of the workgroup's 16 * WG_ROWS
-        float best = -INFINITY;
-        int bidx = 0x7fffffff;
-        for (int e = lane; e < 16 * WG_ROWS; e += 64) {
-          int rr = e >> 4, i = e & 15, gg = blockIdx.x * WG_ROWS + rr;
-          if (gg < p.n_groups) {
-            float v = fin[rr][i][m];
-            int idx = 16 * gg + i;
-            if (v > best || (v == best && idx < bidx)) { best = v; bidx = idx; }
-          }
-        }
-        warp_argmax(best, bidx);
-        float se = 0.f;
-        for (int e = lane; e < 16 * WG_ROWS; e += 64) {
-          int rr = e >> 4, i = e & 15, gg = blockIdx.x * WG_ROWS + rr;
-          if (gg < p.n_groups) se += expf(fin[rr][i][m] - best);
-        }
-        se = warp_sum(se);
-        if (lane == 0) {
-          float* pp = p.lm_part + ((size_t)m * gridDim.x + blockIdx.x) * 3;
-          pp[0] = best;
-          pp[1] = __int_as_float(bidx);
-          pp[2] = se;
-        }
-      }
-    }
-    return;
-  }
-
-  if (ks != 0 || g >= p.n_groups) return;
-  // one wave per row group runs the epilogue
-  float (*f)[NC + 1] = fin[rg];
-  if constexpr (E == Epi::QKV) {
-    const int pos0 = *p.d_len;
-    const int qg = p.nq * p.hd / 16, kg = p.nkv * p.hd / 16;
-    const int per_head = p.hd / 16, half = p.hd / 2;
-    if (g < qg + kg) {
-      const bool is_k = g >= qg;
-      const int gg = is_k ? g - qg : g;
-      const int head = gg / per_head, sub = gg % per_head;
-      for (int idx = lane; idx < 8 * M; idx += 64) {
-        int i = idx & 7, m = idx >> 3;
-        int pos = pos0 + m;
-        if (pos >= p.max_len) continue;
-        float r = rsc[m];
-        float y1 = f[i][m] * r, y2 = f[i + 8][m] * r;
-        int d1 = 8 * sub + i;
-        float2 cs = p.rope[(size_t)pos * half + d1];
-        float o1 = y1 * cs.x - y2 * cs.y;
-        float o2 = y2 * cs.x + y1 * cs.y;
-        if (!is_k) {
-          const int G = p.nq / p.nkv;
-          const float qs = 1.0f / sqrtf((float)p.hd);
-          bf16_bits* qh = p.qb + qtile_head(head / G, p.hd);
-          const int rq = m * G + head % G;
-          qtile_put(qh, p.hd >> 5, rq, d1, o1 * qs);
-          qtile_put(qh, p.hd >> 5, rq, d1 + half, o2 * qs);
-        } else {
-          bf16_bits* kc = p.k_cache + ((size_t)head * p.kv_stride + pos) * p.hd;
-          kc[d1] = f2bf(o1);
-          kc[d1 + half] = f2bf(o2);
-        }
-      }
-    } else {
-      const int r0 = 16 * (g - qg - kg);
-      const int head = r0 / p.hd, d0 = r0 % p.hd;
-      for (int idx = lane; idx < 16 * M; idx += 64) {
-        int i = idx & 15, m = idx >> 4;
-        int pos = pos0 + m;
-        if (pos >= p.max_len) continue;
-        p.v_cache[((size_t)head * p.hd + d0 + i) * p.kv_stride + pos] = f2bf(f[i][m] * rsc[m]);
-      }
-    }
-  } else if constexpr (E == Epi::SWIGLU) {
-    const int KBo = p.F >> 5;
-    for (int idx = lane; idx < 8 * M; idx += 64) {
-      int i = idx & 7, m = idx >> 3;
-      float r = rsc[m];
-      float gt = f[i][m] * r, up = f[i + 8][m] * r;
-      float h = gt / (1.0f + __expf(-gt)) * up;
-      btile_put(p.hb_out, KBo, m, 8 * g + i, h);
-    }
-  } else if constexpr (E == Epi::PARTIAL) {
-    // this split's 16 outputs x M rows, reduced in split order by resid_reduce_kernel
-    float* dst = p.part + (size_t)sidx * kMaxRows * p.H;
-    for (int idx = lane; idx < 16 * M; idx += 64) {
-      const int i = idx & 15, m = idx >> 4;
-      dst[(size_t)m * p.H + 16 * g + i] = f[i][m];
-    }
-  } else {  // RESID
-    const int KBo = p.H >> 5, NP = p.H >> 4;
-    for (int idx = lane; idx < 16 * M; idx += 64) {
-      int i = idx & 15, m = idx >> 4;
-      int n = 16 * g + i;
-      float xn = p.x[(size_t)m * p.H + n] + f[i][m];
-      p.x[(size_t)m * p.H + n] = xn;
-      f[i][m] = xn;
-      btile_put(p.xb_out, KBo, m, n, xn * p.gain_next[n]);
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    for (int m = lane; m < M; m += 64) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s = fmaf(f[i][m], f[i][m], s);
-      p.ss_out[(size_t)m * NP + g] = s;
-    }
-  }
+  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, w, lane, rg, ks, g, sidx, M);
 }
 
 // ---------------------------------------------------------------------------
@@ -771,12 +563,14 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   float* att_o = reinterpret_cast<float*>(ws + pl.att_o);
   float* att_ml = reinterpret_cast<float*>(ws + pl.att_ml);
   hipStream_t s = a.stream;
+  const bool q4 = d.wfmt == SPECDEC_W_Q4G64;
 
   // fused RMSNorm -> QKV -> RoPE -> K/V append (query rows into operand tiles)
   GemvParams p = base;
   p.A = L.wqkv; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.qkv_rows() / 16;
   p.ss_in = ss; p.qb = qb; p.k_cache = a.c->k_layer(l); p.v_cache = a.c->v_layer(l);
-  gemv_kernel<NT, 1, 16, 4, Epi::QKV><<<p.n_groups, 1024, 0, s>>>(p);
+  if (q4) launch_q4_linear(Q4Linear::QKV, p, L.q_wqkv, L.s_wqkv, d.H, s);
+  else gemv_kernel<NT, 1, 16, 4, Epi::QKV><<<p.n_groups, 1024, 0, s>>>(p);
 
   // attention: chunk partials, then the merge into the O-projection operand tiles
   dim3 ag(pl.max_chunks, d.nkv);
@@ -796,13 +590,15 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p = base;
   p.A = L.wo; p.B = reinterpret_cast<const bf16x8_t*>(ob); p.KB = d.qdim() / 32; p.n_groups = d.H / 16;
   p.x = x; p.gain_next = L.mlp_norm; p.xb_out = xb; p.ss_out = ss;
-  gemv_kernel<NT, 1, 16, 4, Epi::RESID><<<p.n_groups, 1024, 0, s>>>(p);
+  if (q4) launch_q4_linear(Q4Linear::O, p, L.q_wo, L.s_wo, d.qdim(), s);
+  else gemv_kernel<NT, 1, 16, 4, Epi::RESID><<<p.n_groups, 1024, 0, s>>>(p);
 
   // RMSNorm -> gate/up -> SwiGLU
   p = base;
   p.A = L.wgu; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.F / 8;
   p.ss_in = ss; p.hb_out = hb;
-  gemv_kernel<NT, 1, 4, 12, Epi::SWIGLU><<<p.n_groups, 256, 0, s>>>(p);
+  if (q4) launch_q4_linear(Q4Linear::GATE_UP, p, L.q_wgu, L.s_wgu, d.H, s);
+  else gemv_kernel<NT, 1, 4, 12, Epi::SWIGLU><<<p.n_groups, 256, 0, s>>>(p);
 
   // down projection + residual; next input is the next layer's (or final) norm
   p = base;
@@ -810,7 +606,8 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.x = x; p.gain_next = (l + 1 < d.L) ? a.m->layers[l + 1].attn_norm : a.m->final_norm; p.xb_out = xb; p.ss_out = ss;
   p.part = reinterpret_cast<float*>(ws + pl.part);
   p.nsplit = kDownSplit;
-  gemv_kernel<NT, 1, 8, 8, Epi::PARTIAL><<<p.n_groups * kDownSplit, 512, 0, s>>>(p);
+  if (q4) launch_q4_linear(Q4Linear::DOWN, p, L.q_wdown, L.s_wdown, d.F, s);
+  else gemv_kernel<NT, 1, 8, 8, Epi::PARTIAL><<<p.n_groups * kDownSplit, 512, 0, s>>>(p);
   resid_reduce_kernel<<<dim3((d.H + 255) / 256, a.rows), 256, 0, s>>>(p.part, kDownSplit, d.H, a.rows, x, p.gain_next, xb,
                                                                      ss, a.gate);
 }
@@ -848,6 +645,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
 }
 
 hipError_t launch_forward(const FwdArgs& a) {
+  if (a.m->d.wfmt == SPECDEC_W_Q4G64 && a.rows > kQ4MaxRows) return hipErrorInvalidValue;
   int nt = (a.rows + 7) / 8;
   switch (nt) {
     case 1: return launch_forward_nt<1>(a);

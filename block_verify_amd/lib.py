@@ -146,23 +146,42 @@ def _dev_bytes(n: int, device) -> torch.Tensor:
 
 
 class Model:
-    """Packed bf16 decoder weights on the device + the library's model handle."""
+    """Packed decoder weights on the device + the library's model handle.
 
-    def __init__(self, shape: ModelShape, tensors, device="cuda", stream=None):
+    tensors: the canonical list (ModelShape.tensor_specs order) of bf16 bit
+    arrays.  For weight_format=W_Q4G64 the linear entries other than lm_head
+    are (codes uint8 [N][K/2], scale fp16 [N][K/64], zero fp16 [N][K/64])
+    tuples; with `share` (a Model) the embedding, final norm and LM head come
+    from that model and their entries may be None.
+    """
+
+    def __init__(self, shape: ModelShape, tensors, device="cuda", stream=None, weight_format: int = W_BF16,
+                 share: "Model | None" = None):
         self.shape = shape
-        self.desc = desc_of(shape)
+        self.desc = desc_of(shape, weight_format)
+        self.share = share
         L = lib()
         nbytes = C.c_size_t()
         check(L.specdec_weights_bytes(C.byref(self.desc), C.byref(nbytes)), "weights_bytes")
         self.blob = _dev_bytes(nbytes.value, device)
         s = _stream(stream)
         for i, t in enumerate(tensors):
-            src = torch.from_numpy(np.ascontiguousarray(t).view(np.int16)).to(device)
+            if t is None:
+                continue
+            if isinstance(t, tuple):
+                codes, sc, zc = t
+                raw = np.concatenate([np.ascontiguousarray(codes, np.uint8).ravel(),
+                                      np.ascontiguousarray(sc, np.float16).view(np.uint8).ravel(),
+                                      np.ascontiguousarray(zc, np.float16).view(np.uint8).ravel()])
+                src = torch.from_numpy(raw).to(device)
+            else:
+                src = torch.from_numpy(np.ascontiguousarray(t).view(np.int16)).to(device)
             check(L.specdec_weights_pack(C.byref(self.desc), i, src.data_ptr(), self.blob.data_ptr(), s), f"pack {i}")
             torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
             del src
         h = C.c_void_p()
-        check(L.specdec_model_create(C.byref(self.desc), self.blob.data_ptr(), None, C.byref(h)), "model_create")
+        check(L.specdec_model_create(C.byref(self.desc), self.blob.data_ptr(), share.handle if share else None,
+                                     C.byref(h)), "model_create")
         self.handle = h
 
     def __del__(self):

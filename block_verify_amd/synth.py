@@ -133,3 +133,19 @@ def quantize_q4g64(w_bf16: np.ndarray):
     q = np.where(flat[..., None], 0, q).astype(np.uint8).reshape(N, K)
     packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
     return packed, s_h, z_h
+
+
+def make_q4_draft(shape, tensors):
+    """Substitute-draft tensors: every linear except the LM head quantised to
+    4-bit group 64 (codes, scale, zero); norms kept; embedding, final norm
+    and LM head None (shared with the target)."""
+    out = []
+    specs = shape.tensor_specs()
+    for i, (name, _, kind) in enumerate(specs):
+        if name in ("embed", "lm_head", "final_norm"):
+            out.append(None)
+        elif kind == "linear":
+            out.append(quantize_q4g64(tensors[i]))
+        else:
+            out.append(tensors[i])
+    return out

@@ -124,3 +124,15 @@ def check_stochastic_round(saved, rows, qz, drafts, m_gpu, com_gpu, seed, rnd):
         near_sample = False
     assert near_accept or near_sample, f"round {rnd}: gpu m={m_gpu} {list(com_gpu)} oracle m={m} {com}"
     return exempt + 1
+
+
+def q4_oracle_weights(shape, target_tensors, q4_tensors):
+    """Oracle view of the substitute draft: the target's tensors with every
+    4-bit linear replaced by its float64 dequantisation."""
+    from oracle import q4
+    from oracle.model import OracleWeights
+    out = list(target_tensors)
+    for i, t in enumerate(q4_tensors):
+        if isinstance(t, tuple):
+            out[i] = q4.dequantize(*t)
+    return OracleWeights(shape, out)

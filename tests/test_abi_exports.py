@@ -58,3 +58,30 @@ def test_host_validation_without_gpu():
     assert L.specdec_round_create(None, None) == b.EINVAL
     assert L.specdec_status_str(b.EDEVICE) == b"device error flag set"
     assert L.specdec_round_state_bytes(64, ctypes.byref(n)) == 0 and n.value == 64 + 64 * 4
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_q4_blob_size_and_shape_checks():
+    """4-bit models: blob = 0.5 byte codes + 8 bytes of (scale, zero) per 128 inputs per row,
+    plus the bf16 embedding / LM head and fp32 gains; unsupported shapes are refused."""
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import QWEN_7B, TINY
+    L = b.lib()
+    n = ctypes.c_size_t()
+    d = b.desc_of(QWEN_7B, b.W_Q4G64)
+    assert L.specdec_weights_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    S = QWEN_7B
+    lin = 0
+    for rows, k in [((S.n_q_heads + 2 * S.n_kv_heads) * S.head_dim, S.hidden), (S.hidden, S.n_q_heads * S.head_dim),
+                    (2 * S.ffn, S.hidden), (S.hidden, S.ffn)]:
+        nb = -(-k // 128)
+        lin += rows * nb * 64 + rows * nb * 8
+    bf16 = 2 * S.vocab * S.hidden * 2
+    assert n.value >= S.n_layers * lin + bf16
+    assert n.value < S.n_layers * lin + bf16 + 4 * 1024 * 1024   # alignment and gains only
+    bad = b.desc_of(TINY, b.W_Q4G64)
+    bad.ffn = 1056   # a multiple of 32, not of 64
+    assert L.specdec_weights_bytes(ctypes.byref(bad), ctypes.byref(n)) == b.ESHAPE
+    big = b.desc_of(TINY, b.W_Q4G64)
+    big.hidden = 8192   # four staged rows of 8192 inputs exceed the 4-bit kernel's LDS budget
+    assert L.specdec_weights_bytes(ctypes.byref(big), ctypes.byref(n)) == b.ESHAPE

@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (assert_logits_close, bf16_bits_to_f64, check_stochastic_round, say, to_np,
-                         tokens_match_teacher_forced)
+from gpu_helpers import (MARGIN, assert_logits_close, bf16_bits_to_f64, check_stochastic_round, oracle_margin,
+                         q4_oracle_weights, say, to_np, tokens_match_teacher_forced)
 
 pytestmark = pytest.mark.gpu
 
@@ -352,3 +352,91 @@ def test_stochastic_job_is_deterministic_eager_and_graph(env):
     _, other = r2.run(N_NEW)
     assert list(other[:N_NEW]) != list(ref[:N_NEW])
     assert r.ws.error_bits() == 0
+
+
+@pytest.fixture(scope="module")
+def q4env(env):
+    from block_verify_amd.synth import make_q4_draft
+    b, S = env["b"], env["shape"]
+    qt = make_q4_draft(S, env["w"])
+    qm = b.Model(S, qt, weight_format=b.W_Q4G64, share=env["model"])
+    return dict(model=qm, ow=q4_oracle_weights(S, env["w"], qt))
+
+
+@pytest.mark.parametrize("rows", [1, 3, 4])
+def test_q4_forward_matches_oracle(env, q4env, rows):
+    """The 4-bit substitute model (shared bf16 embedding / LM head) against the oracle
+    forward with the dequantised weights: prefill (4-row chunks) and a block of rows."""
+    from oracle.model import OracleCache, forward, prefill
+    b, S = env["b"], env["shape"]
+    cache, ws = _fresh(env)
+    t = torch.from_numpy(np.asarray(env["prompt"], np.int32)).cuda()
+    saved = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(q4env["model"], cache, t, ws, chunk=4, logits=saved)
+    oc = OracleCache(S, 512)
+    o_saved = prefill(q4env["ow"], oc, env["prompt"])
+    assert_logits_close(to_np(saved), o_saved, "q4 prefill saved_next")
+    toks = np.random.default_rng(7 + rows).integers(0, S.vocab, rows)
+    logits = torch.empty((rows, S.vocab), dtype=torch.float32, device="cuda")
+    b.decode_step(q4env["model"], cache, torch.from_numpy(toks.astype(np.int32)).cuda(), ws, logits=logits)
+    assert_logits_close(to_np(logits), forward(q4env["ow"], oc, toks), f"q4 block rows={rows}")
+    assert cache.length() == P + rows
+    kk, vv = cache.kv()
+    n = P + rows
+    for l in range(S.n_layers):
+        g = bf16_bits_to_f64(np.stack([to_np(kk[l][:, :n]), to_np(vv[l][:, :n])]))
+        o = np.stack([oc.k[l][:, :n], oc.v[l][:, :n]])
+        assert np.abs(g - o).max() <= 1e-2 * np.abs(o).max()
+    assert ws.error_bits() == 0
+
+
+def test_q4_batch_invariance_and_row_limit(env, q4env):
+    b, S = env["b"], env["shape"]
+    cache, ws = _fresh(env)
+    t = torch.from_numpy(np.asarray(env["prompt"], np.int32)).cuda()
+    b.prefill(q4env["model"], cache, t, ws, chunk=4)
+    toks = torch.from_numpy(np.array([5, 77, 1024, 4095], np.int32)).cuda()
+    lb = torch.empty((4, S.vocab), dtype=torch.float32, device="cuda")
+    b.decode_step(q4env["model"], cache, toks, ws, logits=lb)
+    cache.trim(P, ws)
+    ls = torch.empty((4, S.vocab), dtype=torch.float32, device="cuda")
+    for i in range(4):
+        b.decode_step(q4env["model"], cache, toks[i:i + 1], ws, logits=ls[i])
+    assert torch.equal(lb.view(torch.int32), ls.view(torch.int32))
+    with pytest.raises(b.SpecdecError):
+        b.decode_step(q4env["model"], cache, torch.zeros(5, dtype=torch.int32, device="cuda"), ws)
+
+
+def test_q4_substitute_draft_rounds(env, q4env, gpu_ar):
+    """Substitute-draft rounds on the shared cache (depth 8, schedule A): committed tokens equal
+    greedy AR, d_1 = argmax(saved_next) is always accepted, and every 4-bit draft token is the
+    oracle's argmax on the same prefix (teacher-forced) unless its top-2 margin is < 0.1."""
+    from oracle.model import OracleCache, forward, prefill
+    b, S = env["b"], env["shape"]
+    D = 8
+    r = b.Round(env["model"], D, draft_source=b.DRAFT_Q4_SELF, draft=q4env["model"], max_len=512)
+    r.prefill(env["prompt"])
+    st, toks = r.run(N_NEW)
+    assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+    assert r.tcache.length() == P + st.n_committed
+    assert r.ws.error_bits() == 0
+    # per round, against the oracle on the shared (target-written) cache
+    r.reset(N_NEW)
+    oc = OracleCache(S, 512)
+    prefill(env["ow"], oc, env["prompt"])
+    n0, exempt, ms = 0, 0, []
+    while n0 < N_NEW:
+        r.step()
+        st, toks = r.read_state()
+        drafts = [int(x) for x in to_np(r.debug_view(3, torch.int32))[:D]]
+        assert drafts[0] == gpu_ar[n0]
+        assert st.m_last >= 1
+        rows = forward(q4env["ow"], oc.clone(), drafts[:-1])
+        for j in range(1, D):
+            if int(np.argmax(rows[j - 1])) != drafts[j]:
+                assert oracle_margin(rows[j - 1]) < MARGIN, f"round at {n0}: draft {j}"
+                exempt += 1
+        forward(env["ow"], oc, [int(x) for x in toks[n0:st.n_committed]])
+        ms.append(st.m_last)
+        n0 = st.n_committed
+    say(f"q4 substitute draft: accepted per round {ms}, {exempt} draft tokens exempt by the margin rule")
