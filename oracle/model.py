@@ -12,6 +12,12 @@ Definitions followed:
 * Causal attention (explainer on wmrh.cn, section 3.2): position i sees only
   positions <= i, so one block forward yields every row of a block.
 
+* Same page, section 2.1 (the frozen configuration table): computation in
+  BF16 and the target's KV cache executed in BF16.  The cache therefore
+  stores every K and V entry rounded to bf16 (round to nearest even) when it
+  is appended; everything else here stays float64.  ``kv_bf16=False`` keeps
+  full-precision entries (the plain decoder, for cross-checks).
+
 Decoder details the pages do not give (the plainest Qwen2-style reading):
 pre-norm RMSNorm with eps 1e-6, rotate-half RoPE, grouped-query attention
 (query head h reads kv head h // group), no biases, SwiGLU MLP, untied LM
@@ -32,10 +38,11 @@ class OracleWeights:
     """float64 view of one decoder's weights.
 
     ``tensors`` is the canonical list of bf16 bit arrays (see
-    ``ModelShape.tensor_specs``); entries may also be float arrays already
-    (the q4 path passes dequantised float64 matrices).  With ``cache`` False
-    each matrix is upcast on use and dropped, which keeps 7B-sized models
-    inside host memory.
+    ``ModelShape.tensor_specs``); entries may also be float arrays already,
+    or 4-bit group-64 (codes, scale, zero) tuples of the substitute draft,
+    dequantised on use as in ``oracle.q4``.  With ``cache`` False each matrix
+    is upcast on use and dropped, which keeps 7B-sized models inside host
+    memory.
     """
 
     def __init__(self, shape, tensors, cache: bool = True):
@@ -50,7 +57,10 @@ class OracleWeights:
         if i in self._f64:
             return self._f64[i]
         t = self.tensors[i]
-        if t.dtype == np.uint16:
+        if isinstance(t, tuple):
+            from oracle.q4 import dequantize
+            a = dequantize(*t)
+        elif t.dtype == np.uint16:
             a = bf16_to_f64(t)
         else:
             a = np.asarray(t, dtype=np.float64)
@@ -64,12 +74,20 @@ class OracleWeights:
         return bf16_to_f64(rows) if rows.dtype == np.uint16 else np.asarray(rows, np.float64)
 
 
-class OracleCache:
-    """Contiguous float64 K/V per layer: [n_kv_heads, max_len, head_dim]."""
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits, ties to even), as float64."""
+    m, e = np.frexp(np.asarray(a, dtype=np.float64))   # a = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
-    def __init__(self, shape, max_len: int):
+
+class OracleCache:
+    """Contiguous K/V per layer: [n_kv_heads, max_len, head_dim], entries bf16-valued
+    (float64 arrays) unless kv_bf16 is False."""
+
+    def __init__(self, shape, max_len: int, kv_bf16: bool = True):
         self.shape = shape
         self.max_len = max_len
+        self.kv_bf16 = kv_bf16
         self.k = [np.zeros((shape.n_kv_heads, max_len, shape.head_dim)) for _ in range(shape.n_layers)]
         self.v = [np.zeros((shape.n_kv_heads, max_len, shape.head_dim)) for _ in range(shape.n_layers)]
         self.length = 0
@@ -82,7 +100,7 @@ class OracleCache:
 
     def clone(self) -> "OracleCache":
         c = OracleCache.__new__(OracleCache)
-        c.shape, c.max_len, c.length = self.shape, self.max_len, self.length
+        c.shape, c.max_len, c.length, c.kv_bf16 = self.shape, self.max_len, self.length, self.kv_bf16
         c.k = [a.copy() for a in self.k]
         c.v = [a.copy() for a in self.v]
         return c
@@ -157,8 +175,9 @@ def forward(w: OracleWeights, cache: OracleCache, tokens, last_only: bool = Fals
         v = (h @ w[f"l{l}.wv"].T).reshape(M, sh.n_kv_heads, sh.head_dim)
         q = rope_rotate_half(q, pos, sh.rope_theta)
         k = rope_rotate_half(k, pos, sh.rope_theta)
-        cache.k[l][:, t:t + M, :] = k.transpose(1, 0, 2)
-        cache.v[l][:, t:t + M, :] = v.transpose(1, 0, 2)
+        store = round_bf16 if cache.kv_bf16 else np.asarray
+        cache.k[l][:, t:t + M, :] = store(k.transpose(1, 0, 2))
+        cache.v[l][:, t:t + M, :] = store(v.transpose(1, 0, 2))
         o = causal_attention(q, cache.k[l][:, :t + M], cache.v[l][:, :t + M], pos, sh.group)
         x = x + o @ w[f"l{l}.wo"].T
         h2 = rms_norm(x, w[f"l{l}.mlp_norm"], sh.rms_eps)
@@ -178,8 +197,8 @@ def prefill(w: OracleWeights, cache: OracleCache, tokens, chunk: int = 2048) -> 
     return last
 
 
-def full_recompute_logits(w: OracleWeights, tokens) -> np.ndarray:
+def full_recompute_logits(w: OracleWeights, tokens, kv_bf16: bool = True) -> np.ndarray:
     """Logits of every position of ``tokens`` from a fresh cache (no reuse)."""
     tokens = np.asarray(tokens)
-    c = OracleCache(w.shape, tokens.shape[0])
+    c = OracleCache(w.shape, tokens.shape[0], kv_bf16)
     return forward(w, c, tokens)

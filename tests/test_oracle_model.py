@@ -10,7 +10,7 @@ import torch
 
 from block_verify_amd.shapes import TINY, ModelShape
 from block_verify_amd.synth import make_prompt, make_weights
-from oracle.model import (OracleCache, OracleWeights, causal_attention, forward, full_recompute_logits,
+from oracle.model import (OracleCache, OracleWeights, causal_attention, forward, full_recompute_logits, round_bf16,
                           prefill, rms_norm, rope_rotate_half)
 
 MICRO = ModelShape("micro", 2, 64, 4, 2, 16, 96, 128)
@@ -122,7 +122,7 @@ def _hf_qwen2_logits(shape, tensors, tokens):
 
 def test_forward_matches_transformers_qwen2_tiny(tiny_weights):
     tokens = make_prompt(TINY.vocab, 40, seed=99)
-    ours = full_recompute_logits(OracleWeights(TINY, tiny_weights), tokens)
+    ours = full_recompute_logits(OracleWeights(TINY, tiny_weights), tokens, kv_bf16=False)
     ref = _hf_qwen2_logits(TINY, tiny_weights, tokens)
     # the library evaluates RoPE angles in float32; everything else is float64
     np.testing.assert_allclose(ours, ref, rtol=0, atol=2e-5)
@@ -137,7 +137,7 @@ def test_forward_matches_transformers_nonunit_norm_gains():
             g = (1.0 + 0.5 * rng.standard_normal(shp)).astype(np.float32)
             w[i] = (g.view(np.uint32) >> 16).astype(np.uint16)
     tokens = make_prompt(MICRO.vocab, 23, seed=4)
-    ours = full_recompute_logits(OracleWeights(MICRO, w), tokens)
+    ours = full_recompute_logits(OracleWeights(MICRO, w), tokens, kv_bf16=False)
     ref = _hf_qwen2_logits(MICRO, w, tokens)
     np.testing.assert_allclose(ours, ref, rtol=0, atol=2e-5)
 
@@ -194,3 +194,29 @@ def test_trim_bounds_and_overwrite(tiny_weights):
     c2 = OracleCache(TINY, 16)
     ref = forward(w, c2, [1, 2, 9])
     np.testing.assert_allclose(l_after[0], ref[2], atol=1e-10)
+
+
+def test_round_bf16_matches_torch_conversion():
+    import torch
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.01171875, -3.0e-5, 65504.0]]).astype(np.float32)
+    # halfway cases: bf16 neighbours 1 and 1+2^-7, midpoint 1+2^-8 ties to even (1.0)
+    x = np.concatenate([x, np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_bf16(x.astype(np.float64)), ref)
+    assert round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_cache_stores_bf16_rounded_kv(tiny_weights):
+    """Layer 0's K/V do not depend on earlier rounding: the bf16 cache holds exactly the
+    rounded entries of the full-precision cache; later layers differ only slightly."""
+    w = OracleWeights(TINY, tiny_weights)
+    tokens = make_prompt(TINY.vocab, 20, seed=15)
+    a, b = OracleCache(TINY, 32), OracleCache(TINY, 32, kv_bf16=False)
+    la, lb = forward(w, a, tokens), forward(w, b, tokens)
+    np.testing.assert_array_equal(a.k[0][:, :20], round_bf16(b.k[0][:, :20]))
+    np.testing.assert_array_equal(a.v[0][:, :20], round_bf16(b.v[0][:, :20]))
+    assert not np.array_equal(a.k[0][:, :20], b.k[0][:, :20])
+    assert np.abs(la - lb).max() < 1e-2
