@@ -91,13 +91,14 @@ def gpu_ar(b, model, shape, prompt_t, n, max_len, torch):
     return [int(x) for x in toks[:n].cpu().numpy()], dt
 
 
-def run_spec(b, model, shape, prompt, table, k, schedule, steps, warmup, n_new, max_len, torch):
+def run_spec(b, model, shape, prompt, table, k, schedule, steps, warmup, n_new, max_len, torch, **round_kw):
     """Timed jobs replay the round's four captured HIP graphs; the library records
     the per-term events (draft, verify, accept, repair) between them into a ring
     large enough that every timed round keeps its own timestamps."""
     nvar = (n_new + 1) * max(steps, 1)
     ev = HipEvents(5 * nvar)
-    r = b.Round(model, k, schedule=schedule, table=table, max_len=max_len, events=ev.arr, n_events=5 * nvar)
+    r = b.Round(model, k, schedule=schedule, table=table, max_len=max_len, events=ev.arr, n_events=5 * nvar,
+                **round_kw)
     r.prefill(prompt)
     r.capture()
     for _ in range(warmup):
@@ -236,6 +237,53 @@ def cpu_baseline(shape, weights, k, tau, budget_s=15.0, context=2048):
                        f"{per_round:.3f} s/round; tok/s = {tau:.3f} tokens/round (GPU job) / s per round")}
 
 
+def run_substitute(args, torch):
+    """Substitute-draft job at the 7B shape: depth-8 4-bit self-draft on the shared
+    cache, 2048-token context, greedy, 64 tokens (schedule A).  Prints one JSON
+    line of its own (a measurement of the 4-bit draft step, not the headline)."""
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import QWEN_7B as S, SEED_TARGET
+    from block_verify_amd.synth import make_prompt, make_q4_draft, make_weights
+    D, P = 8, 2048
+    max_len = P + args.n_new + 4 * (D + 2) + 64
+    t0 = time.perf_counter()
+    w = make_weights(S, SEED_TARGET)
+    qt = make_q4_draft(S, w)
+    model = b.Model(S, w)
+    qmodel = b.Model(S, qt, weight_format=b.W_Q4G64, share=model)
+    torch.cuda.synchronize()
+    log(f"7B target + 4-bit draft ready in {time.perf_counter() - t0:.1f} s")
+    prompt = make_prompt(S.vocab, P)
+    ar_toks, ar_s = gpu_ar(b, model, S, torch.from_numpy(prompt).cuda(), args.n_new + D + 2, max_len, torch)
+    ar_tok_s = (args.n_new + D + 1) / ar_s
+    res = run_spec(b, model, S, prompt, None, D, 0, args.steps, args.warmup, args.n_new, max_len, torch,
+                   draft_source=b.DRAFT_Q4_SELF, draft=qmodel)
+    for toks in res["tokens"]:
+        if toks != ar_toks[:args.n_new]:
+            raise RuntimeError("substitute draft: committed tokens differ from the GPU AR decode")
+    t = {k2: float(np.mean(v)) for k2, v in res["terms"].items()}
+    kv_tok = S.kv_bytes_per_token()
+    q4_lin = 0
+    for rows, kk in [((S.n_q_heads + 2 * S.n_kv_heads) * S.head_dim, S.hidden), (S.hidden, S.n_q_heads * S.head_dim),
+                     (2 * S.ffn, S.hidden), (S.hidden, S.ffn)]:
+        nb = -(-kk // 128)
+        q4_lin += S.n_layers * (rows * nb * 64 + rows * nb * 8)
+    ctx = P + args.n_new // 2
+    step_bytes = q4_lin + S.vocab * S.hidden * 2 + kv_tok * ctx + 4 * S.vocab
+    step_ms = t["draft"] / (D - 1)
+    out = {"mode": "substitute-7b", "workload": f"7B-shape target, 4-bit group-64 substitute draft (shared cache, "
+                                                f"shared bf16 embedding / LM head), depth {D}, {P}-token context, "
+                                                f"{args.n_new} tokens, greedy, schedule A",
+           "tok_s": round(args.n_new * args.steps / res["seconds"], 2), "ar_tok_s": round(ar_tok_s, 2),
+           "rounds_per_job": res["rounds"] / args.steps,
+           "accepted_per_round": round(res["accepted"] / max(res["rounds"], 1), 3),
+           "terms_ms": t, "q4_draft_step_ms": round(step_ms, 4),
+           "q4_draft_step_bytes": int(step_bytes),
+           "q4_draft_step_gbs": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+           "q4_linear_bytes": int(q4_lin)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +298,8 @@ def main():
                     help="profiling mode: after the prefill run this many verify forwards of k+1 rows "
                          "(no jobs), then one 256 MiB device copy of known size for counter calibration")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--substitute-7b", action="store_true",
+                    help="measure the 7B substitute-draft job (4-bit draft steps) instead of the headline job")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -257,6 +307,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.substitute_7b:
+        run_substitute(args, torch)
+        return
     from block_verify_amd import lib as b
     from block_verify_amd.shapes import QWEN_1_5B as S, SEED_TARGET
     from block_verify_amd.synth import make_draft_table, make_prompt, make_weights

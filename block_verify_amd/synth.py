@@ -139,13 +139,17 @@ def make_q4_draft(shape, tensors):
     """Substitute-draft tensors: every linear except the LM head quantised to
     4-bit group 64 (codes, scale, zero); norms kept; embedding, final norm
     and LM head None (shared with the target)."""
-    out = []
     specs = shape.tensor_specs()
+    out = [None] * len(specs)
+    lin = []
     for i, (name, _, kind) in enumerate(specs):
         if name in ("embed", "lm_head", "final_norm"):
-            out.append(None)
-        elif kind == "linear":
-            out.append(quantize_q4g64(tensors[i]))
+            continue
+        if kind == "linear":
+            lin.append(i)
         else:
-            out.append(tensors[i])
+            out[i] = tensors[i]
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        for i, q in zip(lin, ex.map(lambda j: quantize_q4g64(tensors[j]), lin)):
+            out[i] = q
     return out

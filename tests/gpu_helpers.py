@@ -126,13 +126,12 @@ def check_stochastic_round(saved, rows, qz, drafts, m_gpu, com_gpu, seed, rnd):
     return exempt + 1
 
 
-def q4_oracle_weights(shape, target_tensors, q4_tensors):
+def q4_oracle_weights(shape, target_tensors, q4_tensors, cache=True):
     """Oracle view of the substitute draft: the target's tensors with every
-    4-bit linear replaced by its float64 dequantisation."""
-    from oracle import q4
+    4-bit linear replaced by its (codes, scale, zero), dequantised on use."""
     from oracle.model import OracleWeights
     out = list(target_tensors)
     for i, t in enumerate(q4_tensors):
         if isinstance(t, tuple):
-            out[i] = q4.dequantize(*t)
-    return OracleWeights(shape, out)
+            out[i] = t
+    return OracleWeights(shape, out, cache=cache)
