@@ -59,10 +59,59 @@ struct GemvParams {
   float* logits;
   int V;
   float* lm_part;        // [rows][gridDim.x][3]
-  // PARTIAL (split-K): [nsplit][kMaxRows][H] partial outputs
+  // PARTIAL (split-K): [nsplit][kMaxRows][H] partial outputs and one
+  // arrival counter per row group (zero between launches); the last split
+  // to arrive sums the partials and runs the RESID epilogue
   float* part;
   int nsplit;
+  int32_t* cnt;
 };
+
+// Stores and loads that bypass the non-coherent per-XCD caches (agent
+// scope), for values one workgroup hands to another inside one launch.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Reads of such values: buffer loads with the sc1 cache policy (the same
+// coherence as agent-scope atomic loads, but ordinary loads the compiler
+// may issue back to back).  The descriptor covers 2 GiB from `base`.
+typedef __amdgpu_buffer_rsrc_t agent_rsrc_t;
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ agent_rsrc_t agent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ float load_agent(agent_rsrc_t r, size_t index) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(index * 4), 0, kCpolSc1));
+}
+// Wait until this wave's outstanding vector memory operations completed.
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+}
+
+// Residual epilogue of 16 outputs (one row group g) x M rows: x += y,
+// the next norm's operand tiles of x * gain and the group's sum of squares.
+// f[i][m] holds y on entry and the new x on exit.
+template <int NC>
+__device__ __forceinline__ void resid_epilogue(const GemvParams& p, float (*f)[NC + 1], int lane, int g, int M) {
+  const int KBo = p.H >> 5, NP = p.H >> 4;
+  for (int idx = lane; idx < 16 * M; idx += 64) {
+    int i = idx & 15, m = idx >> 4;
+    int n = 16 * g + i;
+    float xn = p.x[(size_t)m * p.H + n] + f[i][m];
+    p.x[(size_t)m * p.H + n] = xn;
+    f[i][m] = xn;
+    btile_put(p.xb_out, KBo, m, n, xn * p.gain_next[n]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  for (int m = lane; m < M; m += 64) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = fmaf(f[i][m], f[i][m], s);
+    p.ss_out[(size_t)m * NP + g] = s;
+  }
+}
 
 // Query operand tiles: per kv head, query rows r = m * G + g (g = query head
 // within the group), 16 rows per tile, the bf16 hi and lo parts of q / sqrt(d)
@@ -213,30 +262,38 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
       btile_put(p.hb_out, KBo, m, 8 * g + i, h);
     }
   } else if constexpr (E == Epi::PARTIAL) {
-    // this split's 16 outputs x M rows, reduced in split order by resid_reduce_kernel
+    // this split's 16 outputs x M rows
     float* dst = p.part + (size_t)sidx * kMaxRows * p.H;
     for (int idx = lane; idx < 16 * M; idx += 64) {
       const int i = idx & 15, m = idx >> 4;
-      dst[(size_t)m * p.H + 16 * g + i] = f[i][m];
+      store_agent(dst + (size_t)m * p.H + 16 * g + i, f[i][m]);
     }
-  } else {  // RESID
-    const int KBo = p.H >> 5, NP = p.H >> 4;
+    // the last split of this row group to arrive sums the splits in split
+    // order and finishes the residual; it resets the counter for the next use
+    wait_vmem();
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != p.nsplit - 1) return;
+    const agent_rsrc_t pr = agent_rsrc(p.part);
     for (int idx = lane; idx < 16 * M; idx += 64) {
-      int i = idx & 15, m = idx >> 4;
-      int n = 16 * g + i;
-      float xn = p.x[(size_t)m * p.H + n] + f[i][m];
-      p.x[(size_t)m * p.H + n] = xn;
-      f[i][m] = xn;
-      btile_put(p.xb_out, KBo, m, n, xn * p.gain_next[n]);
+      const int i = idx & 15, m = idx >> 4;
+      float v[kMaxSplit];
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplit; ++s2)
+        if (s2 < p.nsplit && s2 != sidx) v[s2] = load_agent(pr, ((size_t)s2 * kMaxRows + m) * p.H + 16 * g + i);
+      float y = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplit; ++s2)
+        if (s2 < p.nsplit) y += (s2 == sidx) ? f[i][m] : v[s2];
+      f[i][m] = y;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    for (int m = lane; m < M; m += 64) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s = fmaf(f[i][m], f[i][m], s);
-      p.ss_out[(size_t)m * NP + g] = s;
-    }
+    resid_epilogue<NC>(p, f, lane, g, M);
+    if (lane == 0) __hip_atomic_store(p.cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {  // RESID
+    resid_epilogue<NC>(p, f, lane, g, M);
   }
 }
 

@@ -461,38 +461,6 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Split-K finish of the down projection: x += sum of the splits (split
-// order), then the next norm's operand tiles of x * gain and the sums of
-// squares per 16 features.  One workgroup of 256 threads covers 256 features
-// of one row; thread i of a 16-thread group owns feature 16 * group + i.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void resid_reduce_kernel(const float* __restrict__ part, int nsplit, int H, int rows,
-                                                           float* __restrict__ x, const float* __restrict__ gain,
-                                                           bf16_bits* __restrict__ xb, float* __restrict__ ss,
-                                                           const int32_t* gate) {
-  if (gate && *gate == 0) return;
-  __shared__ float sq[256];
-  const int m = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  float xn = 0.f;
-  if (n < H) {
-    float y = 0.f;
-    for (int s2 = 0; s2 < nsplit; ++s2) y += part[((size_t)s2 * kMaxRows + m) * H + n];
-    xn = x[(size_t)m * H + n] + y;
-    x[(size_t)m * H + n] = xn;
-    btile_put(xb, H >> 5, m, n, xn * gain[n]);
-  }
-  sq[threadIdx.x] = xn;
-  __syncthreads();
-  if ((threadIdx.x & 15) == 0 && n < H) {
-    float s2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s2 = fmaf(sq[threadIdx.x + i], sq[threadIdx.x + i], s2);
-    ss[(size_t)m * (H >> 4) + (n >> 4)] = s2;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Final reduction of the LM-head partials: argmax (lowest index on ties) and
 // log-sum-exp per row; then the cache length advances by the row count.
 // ---------------------------------------------------------------------------
@@ -606,10 +574,9 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.x = x; p.gain_next = (l + 1 < d.L) ? a.m->layers[l + 1].attn_norm : a.m->final_norm; p.xb_out = xb; p.ss_out = ss;
   p.part = reinterpret_cast<float*>(ws + pl.part);
   p.nsplit = kDownSplit;
+  p.cnt = reinterpret_cast<int32_t*>(ws + pl.cnt);   // the last split finishes the residual
   if (q4) launch_q4_linear(Q4Linear::DOWN, p, L.q_wdown, L.s_wdown, d.F, s);
   else gemv_kernel<NT, 1, 8, 8, Epi::PARTIAL><<<p.n_groups * kDownSplit, 512, 0, s>>>(p);
-  resid_reduce_kernel<<<dim3((d.H + 255) / 256, a.rows), 256, 0, s>>>(p.part, kDownSplit, d.H, a.rows, x, p.gain_next, xb,
-                                                                     ss, a.gate);
 }
 
 template <int NT>

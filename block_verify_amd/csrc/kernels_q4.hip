@@ -12,8 +12,9 @@
 // and 1024.0 is subtracted), and accumulates code * x pairs with the fp32
 // two-way dot product.  The zero point is applied once per half group:
 //   sum_i (q_i - z) * s * x_i = s * (sum_i q_i * x_i - z * sum_i x_i),
-// with sum_i x_i precomputed per 32 inputs.  The activation rows (at most
-// four) are staged in LDS as fp16.  Reductions run in a fixed order, so a
+// with sum_i x_i taken per 32 inputs from sums of 8 made while the
+// activation rows (at most four) are staged in LDS as fp16; each wave
+// requests its first batch of codes before that staging.  Reductions run in a fixed order, so a
 // row's result does not depend on how many rows share the pass.
 #include "gemv_common.h"
 
@@ -120,13 +121,33 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   const int b0s = (int)(((long)sidx * q.NB) / nsplit), b1s = (int)(((long)(sidx + 1) * q.NB) / nsplit);
   const int KR = (b1s - b0s) * 128;
   _Float16* xs = reinterpret_cast<_Float16*>(q4_lds);                       // [M][KR]
-  float* xh = reinterpret_cast<float*>(q4_lds + (size_t)M * KR * 2);       // [M][KR / 32]
+  float* x8 = reinterpret_cast<float*>(q4_lds + (size_t)M * KR * 2);       // [M][KR / 8] sums of 8
 
   constexpr bool kNorm = (E == Epi::QKV || E == Epi::SWIGLU);
   float ssv[RPW][4];
   if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
 
-  // stage the activation rows of this split as fp16 (x = hi + lo of the tiles)
+  // this wave's first batch of codes is requested before the activations are
+  // staged: the weights do not depend on them
+  const bool active = g < p.n_groups;
+  const int nb = b1s - b0s;
+  const int kb0 = b0s + (int)(((long)ks * nb) / WK), kb1 = b0s + (int)(((long)(ks + 1) * nb) / WK);
+  const u32x4_t* cp = q.codes + (size_t)(active ? g : 0) * q.NB * 64 + lane;
+  const uint32_t* sp = q.scales + (size_t)(active ? g : 0) * q.NB * 32 + (lane >> 5) * 16 + (lane & 15);
+  u32x4_t cv[U];
+  uint32_t sv[U];
+  auto issue = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (b + u < kb1) {
+        cv[u] = __builtin_nontemporal_load(cp + (size_t)(b + u) * 64);
+        sv[u] = __builtin_nontemporal_load(sp + (size_t)(b + u) * 32);
+      }
+  };
+  if (active) issue(kb0);
+
+  // stage the activation rows of this split as fp16 (x = hi + lo of the
+  // tiles) with the float sum of every 8 staged values
   const bf16_bits* bt = reinterpret_cast<const bf16_bits*>(p.B);
   const int k8n = KR >> 3;
   for (int idx = threadIdx.x; idx < M * k8n; idx += blockDim.x) {
@@ -147,37 +168,21 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
       for (int e = 0; e < 8; ++e) o[e] = (_Float16)0.0f;
     }
     *reinterpret_cast<half8_t*>(xs + (size_t)m * KR + (k - b0s * 128)) = o;
-  }
-  __syncthreads();
-  const int c32 = KR >> 5;
-  for (int idx = threadIdx.x; idx < M * c32; idx += blockDim.x) {
-    const _Float16* xp = xs + (size_t)(idx / c32) * KR + (idx % c32) * 32;
-    float s = 0.f;
+    float s8 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) s += (float)xp[e];
-    xh[idx] = s;
+    for (int e = 0; e < 8; ++e) s8 += (float)o[e];
+    x8[idx] = s8;
   }
   __syncthreads();
 
   float y[kQ4MaxRows];
 #pragma unroll
   for (int m = 0; m < kQ4MaxRows; ++m) y[m] = 0.f;
-  if (g < p.n_groups) {
-    const int nb = b1s - b0s;
-    const int kb0 = b0s + (int)(((long)ks * nb) / WK), kb1 = b0s + (int)(((long)(ks + 1) * nb) / WK);
+  if (active) {
     const int qq = lane >> 4;
-    const u32x4_t* cp = q.codes + (size_t)g * q.NB * 64 + lane;
-    const uint32_t* sp = q.scales + (size_t)g * q.NB * 32 + (lane >> 5) * 16 + (lane & 15);
     const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
     for (int b = kb0; b < kb1; b += U) {
-      u32x4_t cv[U];
-      uint32_t sv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (b + u < kb1) {
-          cv[u] = __builtin_nontemporal_load(cp + (size_t)(b + u) * 64);
-          sv[u] = __builtin_nontemporal_load(sp + (size_t)(b + u) * 32);
-        }
+      if (b != kb0) issue(b);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (b + u < kb1) {
@@ -197,6 +202,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
           for (int m = 0; m < kQ4MaxRows; ++m) {
             if (m < M) {
               const half8_t* xp = reinterpret_cast<const half8_t*>(xs + (size_t)m * KR + xoff);
+              const float4 xq = *reinterpret_cast<const float4*>(x8 + (size_t)m * k8n + (xoff >> 3));
               float a0 = 0.f, a1 = 0.f;
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
@@ -206,7 +212,8 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
                 a0 = __builtin_amdgcn_fdot2(qv[4 * v + 2], half2_t{xv[4], xv[5]}, a0, false);
                 a1 = __builtin_amdgcn_fdot2(qv[4 * v + 3], half2_t{xv[6], xv[7]}, a1, false);
               }
-              y[m] = fmaf(s, (a0 + a1) - z * xh[m * c32 + (xoff >> 5)], y[m]);
+              const float xsum = ((xq.x + xq.y) + xq.z) + xq.w;
+              y[m] = fmaf(s, (a0 + a1) - z * xsum, y[m]);
             }
           }
         }
@@ -237,7 +244,7 @@ size_t q4_lds_bytes(int rows, int K, int nsplit) {
   const int NB = (K + 127) / 128;
   const int per = (NB + nsplit - 1) / nsplit + 1;
   const size_t KR = (size_t)per * 128;
-  return (size_t)rows * KR * 2 + (size_t)rows * (KR / 32) * 4;
+  return (size_t)rows * KR * 2 + (size_t)rows * (KR / 8) * 4;
 }
 
 template <int WG_ROWS, int WK, int U, Epi E>
@@ -251,7 +258,7 @@ static hipError_t launch_q4(const GemvParams& p, const Q4Params& q, int grid, hi
     int a = (int)(((long)si * q.NB) / nsplit), b = (int)(((long)(si + 1) * q.NB) / nsplit);
     if (b - a > most) most = b - a;
   }
-  const size_t lds = (size_t)p.rows * most * 128 * 2 + (size_t)p.rows * most * 4 * 4;
+  const size_t lds = (size_t)p.rows * most * 128 * 2 + (size_t)p.rows * most * 16 * 4;
   q4_gemv_kernel<WG_ROWS, WK, U, E><<<grid, 64 * WG_ROWS * WK, lds, s>>>(p, q);
   return hipGetLastError();
 }
@@ -266,8 +273,8 @@ hipError_t launch_q4_linear(Q4Linear which, const GemvParams& p, const uint8_t* 
   switch (which) {
     case Q4Linear::QKV: return launch_q4<1, 8, 4, Epi::QKV>(p, q, p.n_groups, s);
     case Q4Linear::O: return launch_q4<1, 8, 4, Epi::RESID>(p, q, p.n_groups, s);
-    case Q4Linear::GATE_UP: return launch_q4<2, 4, 4, Epi::SWIGLU>(p, q, (p.n_groups + 1) / 2, s);
-    case Q4Linear::DOWN: return launch_q4<1, 8, 4, Epi::PARTIAL>(p, q, p.n_groups * p.nsplit, s);
+    case Q4Linear::GATE_UP: return launch_q4<2, 4, 8, Epi::SWIGLU>(p, q, (p.n_groups + 1) / 2, s);
+    case Q4Linear::DOWN: return launch_q4<1, 8, 8, Epi::PARTIAL>(p, q, p.n_groups * p.nsplit, s);
   }
   return hipErrorInvalidValue;
 }
