@@ -39,7 +39,7 @@ int dims_from_desc(const specdec_model_desc* d, Dims* o) {
     // the 4-bit kernel stages up to kQ4MaxRows activation rows of its input range in LDS
     const size_t lim = 48 * 1024;
     if (q4_lds_bytes(kQ4MaxRows, x.H, 1) > lim || q4_lds_bytes(kQ4MaxRows, x.qdim(), 1) > lim ||
-        q4_lds_bytes(kQ4MaxRows, x.F, kMaxSplit) > lim)
+        q4_lds_bytes(kQ4MaxRows, x.F, kQ4DownSplit) > lim)
       return SPECDEC_ESHAPE;
   }
   *o = x;
@@ -85,7 +85,7 @@ WsPlan ws_plan(const Dims& d, int max_rows, int max_len) {
   p.max_rows = kMaxRows;
   p.nt = kMaxNT;
   p.max_chunks = (max_len + kAttnChunk - 1) / kAttnChunk;
-  p.lm_wgs = (d.V / 16 + 3) / 4;
+  p.lm_wgs = d.V / 16;   // LM-head workgroups for the smallest launch shape (one row group each)
   (void)max_rows;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };

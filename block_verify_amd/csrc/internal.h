@@ -82,7 +82,14 @@ namespace sd {
 
 constexpr int kAttnChunk = 64;
 constexpr int kWsHeader = 65536;   // error word + split-K arrival counters (zeroed once)
-constexpr int kMaxSplit = 4;
+constexpr int kMaxSplit = 8;
+// K splits of the down projection: bf16 (tuned on the verify forward) and
+// 4-bit (bounded by the activations the 4-bit kernel stages in LDS).
+#ifndef SD_DOWN_SPLIT
+#define SD_DOWN_SPLIT 2
+#endif
+constexpr int kDownSplit = SD_DOWN_SPLIT;
+constexpr int kQ4DownSplit = 4;
 
 // Workspace plan for one model.
 struct WsPlan {

@@ -22,9 +22,41 @@
 
 namespace sd {
 
-// K splits of the down projection (fixed per matrix, so a row's summation
-// order never depends on the row count).
-constexpr int kDownSplit = 4;
+// Launch shapes of the skinny products: (row groups per workgroup, k-split
+// waves per row group, weight tiles in flight per wave), and the K splits of
+// the down projection (kDownSplit).  All are fixed per matrix, never by the row count, so
+// a row's summation order does not depend on how many rows share the pass.
+#ifndef SD_CFG_QKV
+#define SD_CFG_QKV 1, 16, 4
+#endif
+#ifndef SD_CFG_O
+#define SD_CFG_O 1, 4, 12
+#endif
+#ifndef SD_CFG_GU
+#define SD_CFG_GU 1, 8, 6
+#endif
+#ifndef SD_CFG_DOWN
+#define SD_CFG_DOWN 1, 16, 9
+#endif
+#ifndef SD_CFG_LM
+#define SD_CFG_LM 4, 1, 12
+#endif
+// U only sets how many tiles a wave keeps in flight (its k-blocks are
+// accumulated in order either way), so it shrinks with the activation tiles
+// per k-block to keep multi-tile passes free of register spills.
+template <int R, int W, int T>
+struct LaunchCfg {
+  static constexpr int WG_ROWS = R, WK = W, THREADS = 64 * R * W;
+  template <int NT>
+  static constexpr int U = NT == 1 ? T : (2 * T / (NT + 1) > 2 ? 2 * T / (NT + 1) : 2);
+};
+using CfgQKV = LaunchCfg<SD_CFG_QKV>;
+using CfgO = LaunchCfg<SD_CFG_O>;
+using CfgGU = LaunchCfg<SD_CFG_GU>;
+using CfgDown = LaunchCfg<SD_CFG_DOWN>;
+using CfgLM = LaunchCfg<SD_CFG_LM>;
+static_assert(CfgDown::WG_ROWS == 1, "the split-K launch maps one row group per workgroup");
+static_assert(kDownSplit <= kMaxSplit, "partial buffer holds kMaxSplit splits");
 
 
 hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStream_t s);
@@ -538,7 +570,9 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.A = L.wqkv; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.qkv_rows() / 16;
   p.ss_in = ss; p.qb = qb; p.k_cache = a.c->k_layer(l); p.v_cache = a.c->v_layer(l);
   if (q4) launch_q4_linear(Q4Linear::QKV, p, L.q_wqkv, L.s_wqkv, d.H, s);
-  else gemv_kernel<NT, 1, 16, 4, Epi::QKV><<<p.n_groups, 1024, 0, s>>>(p);
+  else
+    gemv_kernel<NT, CfgQKV::WG_ROWS, CfgQKV::WK, CfgQKV::template U<NT>, Epi::QKV>
+        <<<(p.n_groups + CfgQKV::WG_ROWS - 1) / CfgQKV::WG_ROWS, CfgQKV::THREADS, 0, s>>>(p);
 
   // attention: chunk partials, then the merge into the O-projection operand tiles
   dim3 ag(pl.max_chunks, d.nkv);
@@ -559,24 +593,29 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.A = L.wo; p.B = reinterpret_cast<const bf16x8_t*>(ob); p.KB = d.qdim() / 32; p.n_groups = d.H / 16;
   p.x = x; p.gain_next = L.mlp_norm; p.xb_out = xb; p.ss_out = ss;
   if (q4) launch_q4_linear(Q4Linear::O, p, L.q_wo, L.s_wo, d.qdim(), s);
-  else gemv_kernel<NT, 1, 16, 4, Epi::RESID><<<p.n_groups, 1024, 0, s>>>(p);
+  else
+    gemv_kernel<NT, CfgO::WG_ROWS, CfgO::WK, CfgO::template U<NT>, Epi::RESID>
+        <<<(p.n_groups + CfgO::WG_ROWS - 1) / CfgO::WG_ROWS, CfgO::THREADS, 0, s>>>(p);
 
   // RMSNorm -> gate/up -> SwiGLU
   p = base;
   p.A = L.wgu; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.F / 8;
   p.ss_in = ss; p.hb_out = hb;
   if (q4) launch_q4_linear(Q4Linear::GATE_UP, p, L.q_wgu, L.s_wgu, d.H, s);
-  else gemv_kernel<NT, 1, 4, 12, Epi::SWIGLU><<<p.n_groups, 256, 0, s>>>(p);
+  else
+    gemv_kernel<NT, CfgGU::WG_ROWS, CfgGU::WK, CfgGU::template U<NT>, Epi::SWIGLU>
+        <<<(p.n_groups + CfgGU::WG_ROWS - 1) / CfgGU::WG_ROWS, CfgGU::THREADS, 0, s>>>(p);
 
   // down projection + residual; next input is the next layer's (or final) norm
   p = base;
   p.A = L.wdown; p.B = reinterpret_cast<const bf16x8_t*>(hb); p.KB = d.F / 32; p.n_groups = d.H / 16;
   p.x = x; p.gain_next = (l + 1 < d.L) ? a.m->layers[l + 1].attn_norm : a.m->final_norm; p.xb_out = xb; p.ss_out = ss;
   p.part = reinterpret_cast<float*>(ws + pl.part);
-  p.nsplit = kDownSplit;
+  p.nsplit = q4 ? kQ4DownSplit : kDownSplit;
   p.cnt = reinterpret_cast<int32_t*>(ws + pl.cnt);   // the last split finishes the residual
   if (q4) launch_q4_linear(Q4Linear::DOWN, p, L.q_wdown, L.s_wdown, d.F, s);
-  else gemv_kernel<NT, 1, 8, 8, Epi::PARTIAL><<<p.n_groups * kDownSplit, 512, 0, s>>>(p);
+  else
+    gemv_kernel<NT, 1, CfgDown::WK, CfgDown::template U<NT>, Epi::PARTIAL><<<p.n_groups * kDownSplit, CfgDown::THREADS, 0, s>>>(p);
 }
 
 template <int NT>
@@ -604,9 +643,8 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
   p.ss_in = ss; p.logits = a.logits;
   float* lm_part = reinterpret_cast<float*>(ws + pl.lm_part);
   p.lm_part = lm_part;
-  constexpr int LMR = 4;
-  int wgs = (p.n_groups + LMR - 1) / LMR;
-  gemv_kernel<NT, LMR, 1, 12, Epi::LMHEAD><<<wgs, 64 * LMR, 0, s>>>(p);
+  int wgs = (p.n_groups + CfgLM::WG_ROWS - 1) / CfgLM::WG_ROWS;
+  gemv_kernel<NT, CfgLM::WG_ROWS, CfgLM::WK, CfgLM::template U<NT>, Epi::LMHEAD><<<wgs, CfgLM::THREADS, 0, s>>>(p);
   lm_reduce_kernel<<<a.rows, 256, 0, s>>>(lm_part, wgs, a.rows, a.argmax, a.lse, a.c->d_len, err, a.gate);
   return hipGetLastError();
 }
