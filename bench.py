@@ -315,6 +315,29 @@ def run_8k(b, model, S, args, torch):
             "verify_gbs": round(gbs, 1), "verify_frac": round(gbs / PEAK_HBM_GBS, 4), "verify_bytes": vb}
 
 
+def run_stochastic_4k(b, model, S, args, torch):
+    """The 4096-token stochastic leg: modified rejection sampling with the noisy
+    self-draft (q = softmax(target logits + N(0,1) noise), Philox seed 3),
+    schedule A, k = 4, 64 tokens per job."""
+    from block_verify_amd.synth import make_noise, make_prompt
+    k, P = 4, 4096
+    max_len = P + args.n_new + 4 * (k + 2) + 64
+    prompt = make_prompt(S.vocab, P)
+    noise = make_noise(args.n_new + 2 * k + 2, S.vocab)
+    r = run_spec(b, model, S, prompt, None, k, 0, args.steps, args.warmup, args.n_new, max_len, torch,
+                 mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=3)
+    if any(t != r["tokens"][0] for t in r["tokens"]):
+        raise RuntimeError("stochastic leg: jobs with the same seeds committed different tokens")
+    t = {k2: float(np.mean(v)) for k2, v in r["terms"].items()}
+    tok_s = args.n_new * args.steps / r["seconds"]
+    log(f"4K stochastic: {tok_s:.1f} tok/s, accept {t['accept'] * 1e3:.1f} us")
+    return {"workload": f"1.5B-shape target, {P}-token context, modified rejection sampling, noisy self-draft "
+                        f"(N(0,1) logit noise, seed 2; Philox seed 3), k={k}, {args.n_new} tokens, schedule A",
+            "tok_s": round(tok_s, 2), "rounds_per_job": r["rounds"] / args.steps,
+            "accepted_per_round": round(r["accepted"] / max(r["rounds"], 1), 3), "terms_ms": t,
+            "accept_us": round(t["accept"] * 1e3, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +353,7 @@ def main():
                          "(no jobs), then one 256 MiB device copy of known size for counter calibration")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-8k", action="store_true", help="skip the 8192-token leg")
+    ap.add_argument("--no-stochastic", action="store_true", help="skip the 4096-token stochastic leg")
     ap.add_argument("--substitute-7b", action="store_true",
                     help="measure the 7B substitute-draft job (4-bit draft steps) instead of the headline job")
     args = ap.parse_args()
@@ -407,6 +431,8 @@ def main():
     }
     if not args.no_8k:
         out["context_8k"] = run_8k(b, model, S, args, torch)
+    if not args.no_stochastic:
+        out["stochastic_4k"] = run_stochastic_4k(b, model, S, args, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(S, weights, k, tau, args.cpu_budget, P)
     print(json.dumps(out), flush=True)

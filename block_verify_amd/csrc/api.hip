@@ -520,7 +520,8 @@ int specdec_round_prefill(specdec_round* r, const int32_t* d_prompt, int32_t n, 
   const specdec_round_desc& q = r->desc;
   const bool B = q.schedule == SPECDEC_SCHEDULE_B;
   const int rows = q.k + (B ? 1 : 0);
-  int need = n + 64 + 2 * rows;
+  // room for the prompt and at least one round (specdec_round_reset checks the whole job)
+  int need = n + 2 * rows + 2;
   if (need > q.target_cache->max_len) return SPECDEC_ECAPACITY;
   if (B && n < 2) return SPECDEC_EINVAL;
   hipStream_t s = (hipStream_t)stream;

@@ -42,13 +42,19 @@ namespace sd {
 #define SD_CFG_LM 4, 1, 12
 #endif
 // U only sets how many tiles a wave keeps in flight (its k-blocks are
-// accumulated in order either way), so it shrinks with the activation tiles
-// per k-block to keep multi-tile passes free of register spills.
+// accumulated in order either way), so multi-tile passes cap it by the
+// registers a wave of this workgroup size may hold: (1 + NT) 4-register
+// tiles per k-block in flight, ~40 registers for the rest.
 template <int R, int W, int T>
 struct LaunchCfg {
   static constexpr int WG_ROWS = R, WK = W, THREADS = 64 * R * W;
+  static constexpr int kVgprs = (512 / (THREADS / 256 > 1 ? THREADS / 256 : 1)) < 256
+                                    ? 512 / (THREADS / 256 > 1 ? THREADS / 256 : 1) : 256;
   template <int NT>
-  static constexpr int U = NT == 1 ? T : (2 * T / (NT + 1) > 2 ? 2 * T / (NT + 1) : 2);
+  static constexpr int U = NT == 1 ? T
+                                   : ((kVgprs - 40) / ((1 + NT) * 4) < T
+                                          ? ((kVgprs - 40) / ((1 + NT) * 4) > 1 ? (kVgprs - 40) / ((1 + NT) * 4) : 1)
+                                          : T);
 };
 using CfgQKV = LaunchCfg<SD_CFG_QKV>;
 using CfgO = LaunchCfg<SD_CFG_O>;

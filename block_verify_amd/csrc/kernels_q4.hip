@@ -240,6 +240,23 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, w, lane, rg, ks, g, sidx, M);
 }
 
+// Launch shapes (row groups per workgroup, k-split waves, code blocks in
+// flight per wave); the down projection takes one row group per workgroup.
+#ifndef SD_Q4_QKV
+#define SD_Q4_QKV 1, 8, 4
+#endif
+#ifndef SD_Q4_O
+#define SD_Q4_O 1, 8, 4
+#endif
+#ifndef SD_Q4_GU
+#define SD_Q4_GU 2, 4, 8
+#endif
+#ifndef SD_Q4_DOWN
+#define SD_Q4_DOWN 4, 12
+#endif
+template <int R, int W, int T>
+constexpr int Q4Rows() { return R; }
+
 size_t q4_lds_bytes(int rows, int K, int nsplit) {
   const int NB = (K + 127) / 128;
   const int per = (NB + nsplit - 1) / nsplit + 1;
@@ -271,10 +288,13 @@ hipError_t launch_q4_linear(Q4Linear which, const GemvParams& p, const uint8_t* 
   q.K = K;
   q.NB = (K + 127) / 128;
   switch (which) {
-    case Q4Linear::QKV: return launch_q4<1, 8, 4, Epi::QKV>(p, q, p.n_groups, s);
-    case Q4Linear::O: return launch_q4<1, 8, 4, Epi::RESID>(p, q, p.n_groups, s);
-    case Q4Linear::GATE_UP: return launch_q4<2, 4, 8, Epi::SWIGLU>(p, q, (p.n_groups + 1) / 2, s);
-    case Q4Linear::DOWN: return launch_q4<1, 8, 8, Epi::PARTIAL>(p, q, p.n_groups * p.nsplit, s);
+    case Q4Linear::QKV:
+      return launch_q4<SD_Q4_QKV, Epi::QKV>(p, q, (p.n_groups + Q4Rows<SD_Q4_QKV>() - 1) / Q4Rows<SD_Q4_QKV>(), s);
+    case Q4Linear::O:
+      return launch_q4<SD_Q4_O, Epi::RESID>(p, q, (p.n_groups + Q4Rows<SD_Q4_O>() - 1) / Q4Rows<SD_Q4_O>(), s);
+    case Q4Linear::GATE_UP:
+      return launch_q4<SD_Q4_GU, Epi::SWIGLU>(p, q, (p.n_groups + Q4Rows<SD_Q4_GU>() - 1) / Q4Rows<SD_Q4_GU>(), s);
+    case Q4Linear::DOWN: return launch_q4<1, SD_Q4_DOWN, Epi::PARTIAL>(p, q, p.n_groups * p.nsplit, s);
   }
   return hipErrorInvalidValue;
 }

@@ -228,7 +228,10 @@ void specdec_round_destroy(specdec_round* r);
  * of `chunk` rows and snapshot the post-prefill state.  The caches are
  * first trimmed to 0.  Schedule A prefills all n tokens into the target and
  * keeps the last row as saved_next; schedule B prefills n-1 tokens and
- * leaves prompt[n-1] pending.  An independent draft model prefills all n. */
+ * leaves prompt[n-1] pending.  An independent draft model prefills all n.
+ * SPECDEC_ECAPACITY unless the target cache holds n + 2 * (verify rows) + 2
+ * positions (the prompt and one round); specdec_round_reset checks the
+ * whole job. */
 int specdec_round_prefill(specdec_round* r, const int32_t* d_prompt, int32_t n, int32_t chunk, void* stream);
 
 /* Return to the post-prefill snapshot: trim every cache back to its

@@ -440,3 +440,17 @@ def test_q4_substitute_draft_rounds(env, q4env, gpu_ar):
         ms.append(st.m_last)
         n0 = st.n_committed
     say(f"q4 substitute draft: accepted per round {ms}, {exempt} draft tokens exempt by the margin rule")
+
+
+def test_round_prefill_fits_a_tight_cache(env, gpu_ar):
+    """A cache sized for the prompt and one job only (no spare margin) runs the job."""
+    from block_verify_amd.synth import make_draft_table
+    b = env["b"]
+    table = make_draft_table(np.array(gpu_ar), env["shape"].vocab, 0.4)
+    tight = P + N_NEW + 2 * (K + 1) + 2
+    r = b.Round(env["model"], K, table=table, max_len=tight)
+    r.prefill(env["prompt"])
+    st, toks = r.run(N_NEW)
+    assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+    with pytest.raises(b.SpecdecError):
+        r.reset(N_NEW + 2 * (K + 1))
