@@ -125,6 +125,10 @@ RoundWsPlan round_ws_plan(int V, int k) {
   p.q_lse = take(K1 * 4);
   p.snap = take(kNumSnap * 4);
   p.dbg = take((2 * kMaxK + 2) * 4);
+  p.smax = take((size_t)n_slices(V) * 4);
+  p.ssum = take((size_t)n_slices(V) * 4);
+  p.sw = take((size_t)n_slices(V) * 8);
+  p.sctl = take(4 * 4);
   p.draft_argmax = take(4);
   p.rows_logits = take(K1 * V * 4);
   p.saved_logits = take((size_t)V * 4);
@@ -478,6 +482,10 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   v.snap_logits = reinterpret_cast<float*>(w + rp.snap_logits);
   v.snap = reinterpret_cast<int32_t*>(w + rp.snap);
   v.dbg = reinterpret_cast<float*>(w + rp.dbg);
+  v.smax = reinterpret_cast<float*>(w + rp.smax);
+  v.ssum = reinterpret_cast<float*>(w + rp.ssum);
+  v.sw = reinterpret_cast<double*>(w + rp.sw);
+  v.sctl = reinterpret_cast<int32_t*>(w + rp.sctl);
   v.t_len = q.target_cache->d_len;
   v.d_len = q.draft_source == SPECDEC_DRAFT_MODEL ? q.draft_cache->d_len : nullptr;
   v.err = static_cast<int32_t*>(q.d_ws);

@@ -183,36 +183,33 @@ __global__ void reset_kernel(RoundDev r, int32_t n_target) {
 }
 
 // ---------------------------------------------------------------------------
-// Inverse-CDF sampling over one vocabulary row with 1024 threads: each
-// thread sums a contiguous segment in float64 (index order), a fixed-order
-// scan of the segment sums locates the segment whose running total first
-// exceeds u * total, and that segment is walked in index order.
-// Weight of entry i is wfun(i) >= 0.
+// Inverse-CDF sampling over a whole row by one workgroup of NT threads (the
+// rare fallback of the residual): each thread sums a contiguous segment in
+// float64 (index order), thread 0 scans the segment sums in order for the
+// segment whose running total first exceeds u * total, and that segment is
+// walked in index order.  Weight of entry i is wfun(i) >= 0.
 // ---------------------------------------------------------------------------
-constexpr int kSampleThreads = 1024;
-
-template <class WF>
+template <int NT, class WF>
 __device__ int block_sample(WF wfun, int V, float u, double* sh, double* total_out) {
   const int tid = threadIdx.x;
-  const int seg = (V + kSampleThreads - 1) / kSampleThreads;
+  const int seg = (V + NT - 1) / NT;
   const int i0 = tid * seg, i1 = min(V, i0 + seg);
   double s = 0.0;
   for (int i = i0; i < i1; ++i) s += (double)wfun(i);
   sh[tid] = s;
   __syncthreads();
-  // inclusive scan of segment sums, thread 0 walks them in order
   __shared__ int pick_seg;
   __shared__ double pick_base;
   __shared__ int picked;
   if (tid == 0) {
     double run = 0.0;
-    for (int t = 0; t < kSampleThreads; ++t) run += sh[t];
+    for (int t = 0; t < NT; ++t) run += sh[t];
     double total = run;
     double target = (double)u * total;
     run = 0.0;
-    int ps = kSampleThreads - 1;
+    int ps = NT - 1;
     double base = 0.0;
-    for (int t = 0; t < kSampleThreads; ++t) {
+    for (int t = 0; t < NT; ++t) {
       if (run + sh[t] > target) { ps = t; base = run; break; }
       run += sh[t];
     }
@@ -241,99 +238,265 @@ __device__ int block_sample(WF wfun, int V, float u, double* sh, double* total_o
   return res;
 }
 
-// Block-wide max and sum-exp (fixed tree) of a row; returns lse.
-__device__ float block_lse(const float* __restrict__ row, const float* __restrict__ add, int V, float* shf) {
-  const int tid = threadIdx.x;
-  float mx = -INFINITY;
-  for (int i = tid; i < V; i += blockDim.x) mx = fmaxf(mx, row[i] + (add ? add[i] : 0.f));
-  shf[tid] = mx;
+// ---------------------------------------------------------------------------
+// Row sampling spread over the chip.  A row of V entries is cut into slices
+// of kSliceElems; one 256-thread workgroup per slice.
+//   stats:   slice max and sum of exp(x - slice max) (noisy draft rows only,
+//            which also writes x = z + noise);
+//   weights: log-sum-exp of the row from the slice stats (every workgroup
+//            combines them in slice order), then the float64 sum of the
+//            slice's sampling weights;
+//   select:  one workgroup scans the slice sums in order for u * total,
+//            then walks the chosen slice with a prefix sum.
+// Orders are fixed by index, so the result does not depend on timing.
+// ---------------------------------------------------------------------------
+constexpr int kSliceThreads = 256;
+constexpr int kPerThread = kSliceElems / kSliceThreads;
+
+template <typename T>
+__device__ __forceinline__ T block_reduce_256(T v, T* sh, bool is_max) {
+  const int t = threadIdx.x;
+  sh[t] = v;
   __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (tid < s) shf[tid] = fmaxf(shf[tid], shf[tid + s]);
+  for (int s2 = kSliceThreads / 2; s2 > 0; s2 >>= 1) {
+    if (t < s2) sh[t] = is_max ? (sh[t] > sh[t + s2] ? sh[t] : sh[t + s2]) : sh[t] + sh[t + s2];
     __syncthreads();
   }
-  mx = shf[0];
+  T r = sh[0];
   __syncthreads();
-  float se = 0.f;
-  for (int i = tid; i < V; i += blockDim.x) se += expf(row[i] + (add ? add[i] : 0.f) - mx);
-  shf[tid] = se;
-  __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (tid < s) shf[tid] += shf[tid + s];
-    __syncthreads();
-  }
-  float lse = mx + logf(shf[0]);
-  __syncthreads();
-  return lse;
+  return r;
 }
 
-// Noisy self-draft, step j: q_j = softmax(z_j + noise[n0 + j]); stores the
-// noisy logits and their lse, draws d_j with the draft stream of Philox and
-// writes it into the verify block.
-__global__ __launch_bounds__(kSampleThreads) void draft_sample_kernel(RoundDev r, const float* __restrict__ z, int j) {
+// Weight modes of the sampler.
+enum { kWDraft = 0, kWResidual = 1, kWTarget = 2 };
+
+// Noisy self-draft, step j: x = z + noise[n0 + j] into q_logits[j]; slice stats.
+__global__ __launch_bounds__(kSliceThreads) void draft_stats_kernel(RoundDev r, const float* __restrict__ z, int j) {
   if (r.flags[kFlagOpen] == 0) return;
-  __shared__ double shd[kSampleThreads];
-  __shared__ float shf[kSampleThreads];
-  __shared__ double total;
-  const int V = r.V;
-  specdec_round_state* st = r.state;
-  const int row = st->n_committed + j;
+  __shared__ float shf[kSliceThreads];
+  const int V = r.V, sl = blockIdx.x;
+  const int row = r.state->n_committed + j;
   const bool ok = row < r.noise_rows;
-  if (!ok && threadIdx.x == 0) raise_error(r.err, kErrTable);
+  if (!ok && sl == 0 && threadIdx.x == 0) raise_error(r.err, kErrTable);
   const float* nz = r.noise + (size_t)(ok ? row : 0) * V;
   float* qz = r.q_logits + (size_t)j * V;
-  for (int i = threadIdx.x; i < V; i += blockDim.x) qz[i] = z[i] + nz[i];
-  __syncthreads();
-  float lse = block_lse(qz, nullptr, V, shf);
-  float u = philox_uniform(r.seed, (uint64_t)st->round, (uint64_t)j, 0);
-  int tok = block_sample([&](int i) { return expf(qz[i] - lse); }, V, u, shd, &total);
-  if (threadIdx.x == 0) {
-    r.q_lse[j] = lse;
-    r.block[j] = tok;
+  float xv[kPerThread];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = sl * kSliceElems + e * kSliceThreads + threadIdx.x;
+    xv[e] = -INFINITY;
+    if (i < V) {
+      xv[e] = z[i] + nz[i];
+      qz[i] = xv[e];
+    }
+    mx = fmaxf(mx, xv[e]);
   }
+  mx = block_reduce_256(mx, shf, true);
+  float se = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) se += (xv[e] == -INFINITY) ? 0.f : expf(xv[e] - mx);
+  se = block_reduce_256(se, shf, false);
+  if (threadIdx.x == 0) { r.smax[sl] = mx; r.ssum[sl] = se; }
+}
+
+// log-sum-exp of a row from its slice stats (slice order; same value in every workgroup).
+__device__ float combine_lse(const RoundDev& r, int S, float* shf) {
+  float mx = -INFINITY;
+  for (int s2 = threadIdx.x; s2 < S; s2 += kSliceThreads) mx = fmaxf(mx, r.smax[s2]);
+  mx = block_reduce_256(mx, shf, true);
+  float l = 0.f;
+  for (int s2 = threadIdx.x; s2 < S; s2 += kSliceThreads) l += r.ssum[s2] * expf(r.smax[s2] - mx);
+  l = block_reduce_256(l, shf, false);
+  return mx + logf(l);
+}
+
+// The sampling weight of entry i for the current mode.
+struct SampleRows {
+  const float* lp; float lp_lse;   // target row (residual / bonus)
+  const float* lq; float lq_lse;   // draft row (draft sample / residual)
+  int mode;
+};
+__device__ __forceinline__ double sample_weight(const SampleRows& w, int i) {
+  if (w.mode == kWDraft) return (double)expf(w.lq[i] - w.lq_lse);
+  if (w.mode == kWTarget) return (double)expf(w.lp[i] - w.lp_lse);
+  return (double)fmaxf(0.f, expf(w.lp[i] - w.lp_lse) - expf(w.lq[i] - w.lq_lse));
+}
+
+__device__ SampleRows accept_rows(const RoundDev& r, int m, int mode) {
+  const specdec_round_state* st = r.state;
+  SampleRows w;
+  w.lp = m == 0 ? r.saved_logits : r.rows_logits + (size_t)(m - 1) * r.V;
+  w.lp_lse = m == 0 ? st->saved_lse : r.rows_lse[m - 1];
+  w.lq = r.q_logits + (size_t)(m < r.k ? m : 0) * r.V;
+  w.lq_lse = r.q_lse[m < r.k ? m : 0];
+  w.mode = mode;
+  return w;
+}
+
+// Slice sums of the sampling weights.  j >= 0: draft step j (log-sum-exp of
+// the noisy row first, stored in q_lse[j]); j < 0: the accept step's row and
+// mode from sctl.
+__global__ __launch_bounds__(kSliceThreads) void slice_weights_kernel(RoundDev r, int j) {
+  if (r.flags[kFlagOpen] == 0) return;
+  __shared__ float shf[kSliceThreads];
+  __shared__ double shd[kSliceThreads];
+  const int V = r.V, sl = blockIdx.x;
+  SampleRows w;
+  if (j >= 0) {
+    const float lse = combine_lse(r, gridDim.x, shf);
+    if (sl == 0 && threadIdx.x == 0) r.q_lse[j] = lse;
+    w.lq = r.q_logits + (size_t)j * V;
+    w.lq_lse = lse;
+    w.lp = nullptr; w.lp_lse = 0.f;
+    w.mode = kWDraft;
+  } else {
+    w = accept_rows(r, r.sctl[0], r.sctl[1]);
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = sl * kSliceElems + e * kSliceThreads + threadIdx.x;
+    if (i < V) acc += sample_weight(w, i);
+  }
+  acc = block_reduce_256(acc, shd, false);
+  if (threadIdx.x == 0) r.sw[sl] = acc;
+}
+
+// Inverse CDF over the slice sums: the smallest index whose running weight
+// exceeds u * total.  Returns -1 when the total is not above `floor`.
+__device__ int select_index(const RoundDev& r, const SampleRows& w, int S, float u, double floor_total,
+                            double* shd, int* shi) {
+  __shared__ int s_pick;
+  __shared__ double s_base, s_target;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    double total = 0.0;
+    for (int s2 = 0; s2 < S; ++s2) total += r.sw[s2];
+    const double target = (double)u * total;
+    double run = 0.0;
+    int ps = -1;
+    if (total > floor_total) {
+      ps = S - 1;
+      for (int s2 = 0; s2 < S; ++s2) {
+        if (run + r.sw[s2] > target) { ps = s2; break; }
+        run += r.sw[s2];
+      }
+    }
+    s_pick = ps;
+    s_base = run;
+    s_target = target;
+  }
+  __syncthreads();
+  const int ps = s_pick;
+  if (ps < 0) return -1;
+  // inclusive prefix sum of the chosen slice, element order
+  double v[kPerThread];
+  double own = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = ps * kSliceElems + t * kPerThread + e;
+    v[e] = i < r.V ? sample_weight(w, i) : 0.0;
+    own += v[e];
+  }
+  shd[t] = own;
+  __syncthreads();
+  for (int off = 1; off < kSliceThreads; off <<= 1) {   // Hillis-Steele scan of thread totals
+    const double add = t >= off ? shd[t - off] : 0.0;
+    __syncthreads();
+    shd[t] += add;
+    __syncthreads();
+  }
+  double run = s_base + (t > 0 ? shd[t - 1] : 0.0);
+  int hit = 0x7fffffff, last = -1;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = ps * kSliceElems + t * kPerThread + e;
+    if (v[e] > 0.0) last = i;
+    run += v[e];
+    if (hit == 0x7fffffff && run > s_target && v[e] > 0.0) hit = i;
+  }
+  shi[t] = hit;
+  __syncthreads();
+  for (int s2 = kSliceThreads / 2; s2 > 0; s2 >>= 1) {
+    if (t < s2) shi[t] = min(shi[t], shi[t + s2]);
+    __syncthreads();
+  }
+  int pick = shi[0];
+  __syncthreads();
+  if (pick == 0x7fffffff) {   // rounding left u * total past the walked slice: its last positive entry
+    shi[t] = last;
+    __syncthreads();
+    for (int s2 = kSliceThreads / 2; s2 > 0; s2 >>= 1) {
+      if (t < s2) shi[t] = max(shi[t], shi[t + s2]);
+      __syncthreads();
+    }
+    pick = shi[0] >= 0 ? shi[0] : ps * kSliceElems;
+    __syncthreads();
+  }
+  return pick;
+}
+
+// Draft step j: the sampled token goes into the verify block.
+__global__ __launch_bounds__(kSliceThreads) void draft_select_kernel(RoundDev r, int j) {
+  if (r.flags[kFlagOpen] == 0) return;
+  __shared__ double shd[kSliceThreads];
+  __shared__ int shi[kSliceThreads];
+  SampleRows w;
+  w.lq = r.q_logits + (size_t)j * r.V;
+  w.lq_lse = r.q_lse[j];
+  w.lp = nullptr; w.lp_lse = 0.f;
+  w.mode = kWDraft;
+  const float u = philox_uniform(r.seed, (uint64_t)r.state->round, (uint64_t)j, 0);
+  const int tok = select_index(r, w, n_slices(r.V), u, -1.0, shd, shi);
+  if (threadIdx.x == 0) r.block[j] = tok;
 }
 
 // Modified rejection sampling over the k drafts of the round (schedule A):
 // p_1 = softmax(saved_next), p_(j+1) = softmax(rows[j]), q_j as drawn.
-__global__ __launch_bounds__(kSampleThreads) void accept_stochastic_kernel(RoundDev r) {
+// Decides m (accept while u_j < min(1, p_j(d_j) / (q_j(d_j) + 1e-10))) and
+// which row the resample uses: the residual of row m, or the bonus row.
+__global__ void accept_decide_kernel(RoundDev r) {
   if (r.flags[kFlagOpen] == 0) return;
-  __shared__ double shd[kSampleThreads];
-  __shared__ double total;
+  if (threadIdx.x != 0) return;
   specdec_round_state* st = r.state;
   const int k = r.k, V = r.V;
-  const int32_t* d = r.block;
-  auto prow = [&](int j) -> const float* { return j == 0 ? r.saved_logits : r.rows_logits + (size_t)(j - 1) * V; };
-  auto plse = [&](int j) -> float { return j == 0 ? st->saved_lse : r.rows_lse[j - 1]; };
-  const float ur = philox_uniform(r.seed, (uint64_t)st->round, 0, 2);
   int m = 0;
-  int c = -1;
   for (; m < k; ++m) {
-    const float* lp = prow(m);
-    const float lp_lse = plse(m);
+    const float* lp = m == 0 ? r.saved_logits : r.rows_logits + (size_t)(m - 1) * V;
+    const float lp_lse = m == 0 ? st->saved_lse : r.rows_lse[m - 1];
     const float* lq = r.q_logits + (size_t)m * V;
-    const float lq_lse = r.q_lse[m];
-    const int x = d[m];
-    float px = expf(lp[x] - lp_lse), qx = expf(lq[x] - lq_lse);
-    float ratio = fminf(1.0f, px / (qx + 1e-10f));
-    float ua = philox_uniform(r.seed, (uint64_t)st->round, (uint64_t)m, 1);
-    if (threadIdx.x == 0 && r.dbg) { r.dbg[2 * m] = ratio; r.dbg[2 * m + 1] = ua; }
-    if (ua < ratio) continue;
-    // first rejection: residual norm(max(0, p - q)), fallback to p
-    auto wres = [&](int i) { return fmaxf(0.f, expf(lp[i] - lp_lse) - expf(lq[i] - lq_lse)); };
-    c = block_sample(wres, V, ur, shd, &total);
-    if (!(total > 1e-10)) c = block_sample([&](int i) { return expf(lp[i] - lp_lse); }, V, ur, shd, &total);
-    break;
+    const int x = r.block[m];
+    const float px = expf(lp[x] - lp_lse), qx = expf(lq[x] - r.q_lse[m]);
+    const float ratio = fminf(1.0f, px / (qx + 1e-10f));
+    const float ua = philox_uniform(r.seed, (uint64_t)st->round, (uint64_t)m, 1);
+    if (r.dbg) { r.dbg[2 * m] = ratio; r.dbg[2 * m + 1] = ua; }
+    if (!(ua < ratio)) break;
   }
-  if (m == k) {
-    const float* lp = prow(k);
-    const float lp_lse = plse(k);
-    c = block_sample([&](int i) { return expf(lp[i] - lp_lse); }, V, ur, shd, &total);
+  r.sctl[0] = m;
+  r.sctl[1] = m < k ? kWResidual : kWTarget;
+}
+
+// The resample (or bonus) and the commit: tokens, lengths, repair token.
+__global__ __launch_bounds__(kSliceThreads) void accept_select_kernel(RoundDev r) {
+  if (r.flags[kFlagOpen] == 0) return;
+  __shared__ double shd[kSliceThreads];
+  __shared__ int shi[kSliceThreads];
+  __shared__ double total;
+  specdec_round_state* st = r.state;
+  const int k = r.k, m = r.sctl[0];
+  const float ur = philox_uniform(r.seed, (uint64_t)st->round, 0, 2);
+  int c = select_index(r, accept_rows(r, m, r.sctl[1]), n_slices(r.V), ur, r.sctl[1] == kWResidual ? 1e-10 : -1.0,
+                       shd, shi);
+  if (c < 0) {   // residual mass <= 1e-10: sample p of that row (one workgroup, rare)
+    const SampleRows wp = accept_rows(r, m, kWTarget);
+    c = block_sample<kSliceThreads>([&](int i) { return sample_weight(wp, i); }, r.V, ur, shd, &total);
   }
   if (threadIdx.x == 0) {
     int n = st->n_committed;
     int32_t* toks = reinterpret_cast<int32_t*>(st + 1);
     for (int j = 0; j < m; ++j) {
-      if (n < st->cap) toks[n] = d[j]; else raise_error(r.err, kErrOutput);
+      if (n < st->cap) toks[n] = r.block[j]; else raise_error(r.err, kErrOutput);
       ++n;
     }
     if (n < st->cap) toks[n] = c; else raise_error(r.err, kErrOutput);
@@ -360,11 +523,16 @@ hipError_t launch_rewind(const RoundDev& r, int32_t* len, int n, hipStream_t s) 
 hipError_t launch_snapshot(const RoundDev& r, const int32_t* last, hipStream_t s) { snapshot_kernel<<<64, 256, 0, s>>>(r, last); return hipGetLastError(); }
 hipError_t launch_reset(const RoundDev& r, int32_t n_target, hipStream_t s) { reset_kernel<<<64, 256, 0, s>>>(r, n_target); return hipGetLastError(); }
 hipError_t launch_draft_sample(const RoundDev& r, const float* z, int j, hipStream_t s) {
-  draft_sample_kernel<<<1, kSampleThreads, 0, s>>>(r, z, j);
+  const int S = n_slices(r.V);
+  draft_stats_kernel<<<S, kSliceThreads, 0, s>>>(r, z, j);
+  slice_weights_kernel<<<S, kSliceThreads, 0, s>>>(r, j);
+  draft_select_kernel<<<1, kSliceThreads, 0, s>>>(r, j);
   return hipGetLastError();
 }
 hipError_t launch_accept_stochastic(const RoundDev& r, hipStream_t s) {
-  accept_stochastic_kernel<<<1, kSampleThreads, 0, s>>>(r);
+  accept_decide_kernel<<<1, 64, 0, s>>>(r);
+  slice_weights_kernel<<<n_slices(r.V), kSliceThreads, 0, s>>>(r, -1);
+  accept_select_kernel<<<1, kSliceThreads, 0, s>>>(r);
   return hipGetLastError();
 }
 

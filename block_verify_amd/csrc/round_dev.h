@@ -7,6 +7,10 @@
 namespace sd {
 
 constexpr int kMaxK = SPECDEC_MAX_K;
+// Rows sampled by inverse CDF are cut into slices of kSliceElems entries,
+// one 256-thread workgroup each.
+constexpr int kSliceElems = 1024;
+inline __host__ __device__ int n_slices(int V) { return (V + kSliceElems - 1) / kSliceElems; }
 
 enum { kFlagOpen = 0, kFlagRepair = 1, kNumFlags = 4 };
 enum { kSnapTLen = 0, kSnapDLen = 1, kSnapArgmax = 2, kSnapLse = 3, kSnapLast = 4, kNumSnap = 8 };
@@ -30,6 +34,10 @@ struct RoundDev {
   float* snap_logits;      // [V]
   int32_t* snap;           // [kNumSnap]
   float* dbg;              // [2 * kMaxK + 2] ratios / uniforms of the last stochastic round
+  float* smax;             // [slices] per-slice max of a sampled row
+  float* ssum;             // [slices] per-slice sum of exp(x - slice max)
+  double* sw;              // [slices] per-slice sum of the sampling weights
+  int32_t* sctl;           // [4] sampler control: accepted count m, weight mode
   int32_t* t_len;
   int32_t* d_len;          // independent draft's cache length, or null
   int32_t* err;
@@ -44,6 +52,7 @@ struct RoundDev {
 // Round scratch layout inside d_round_ws.
 struct RoundWsPlan {
   size_t flags, block, repair_tok, rows_argmax, rows_lse, repair_argmax, repair_lse, q_lse, snap, dbg;
+  size_t smax, ssum, sw, sctl;
   size_t rows_logits, saved_logits, q_logits, z, draft_logits, draft_argmax, snap_logits, total;
 };
 RoundWsPlan round_ws_plan(int V, int k);

@@ -454,3 +454,71 @@ def test_round_prefill_fits_a_tight_cache(env, gpu_ar):
     assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
     with pytest.raises(b.SpecdecError):
         r.reset(N_NEW + 2 * (K + 1))
+
+
+@pytest.mark.parametrize("schedule", [0, 1])
+@pytest.mark.parametrize("k", [1, 16])
+def test_spec_extreme_draft_counts(env, gpu_ar, schedule, k):
+    """k = 1 and the maximum k = 16 (a 17-row verify under schedule B) commit the greedy tokens."""
+    from block_verify_amd.synth import make_draft_table
+    b = env["b"]
+    n = 24
+    ar = _gpu_ar(env, n + k + 2)
+    table = make_draft_table(np.array(ar), env["shape"].vocab, 0.3)
+    r = b.Round(env["model"], k, schedule=schedule, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    st, toks = r.run(n)
+    assert list(toks[:n]) == ar[:n]
+    assert r.tcache.length() == P + st.n_committed - (1 if schedule == 1 else 0)
+    assert r.ws.error_bits() == 0
+
+
+@pytest.mark.parametrize("schedule,plen", [(0, 1), (1, 2)])
+def test_spec_shortest_prompt(env, schedule, plen):
+    """The shortest prompts each schedule takes (1 token for A, 2 for B, whose last one stays pending)."""
+    from block_verify_amd.synth import make_draft_table
+    b, S = env["b"], env["shape"]
+    prompt = env["prompt"][:plen]
+    cache, ws = _fresh(env)
+    n = 12
+    toks = torch.zeros(n + K + 3, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(env["model"], cache, torch.from_numpy(np.asarray(prompt, np.int32)).cuda(), ws, logits=scratch,
+              argmax=toks[0:1])
+    for i in range(n + K + 1):
+        b.decode_step(env["model"], cache, toks[i:i + 1], ws, logits=scratch, argmax=toks[i + 1:i + 2])
+    ar = [int(x) for x in to_np(toks)[:n + K + 2]]
+    table = make_draft_table(np.array(ar), S.vocab, 0.4)
+    r = b.Round(env["model"], K, schedule=schedule, table=table, max_len=128)
+    r.prefill(prompt)
+    st, got = r.run(n)
+    assert list(got[:n]) == ar[:n]
+    assert r.tcache.length() == plen + st.n_committed - (1 if schedule == 1 else 0)
+
+
+def test_host_rejects_empty_and_oversized_inputs(env):
+    b = env["b"]
+    cache, ws = _fresh(env, max_len=64)
+    with pytest.raises(b.SpecdecError):
+        b.decode_step(env["model"], cache, torch.zeros(0, dtype=torch.int32, device="cuda"), ws)
+    with pytest.raises(b.SpecdecError):
+        b.decode_step(env["model"], cache, torch.zeros(33, dtype=torch.int32, device="cuda"), ws)
+    with pytest.raises(b.SpecdecError):
+        b.Round(env["model"], 17, table=np.zeros(64, np.int32), max_len=256)
+    r = b.Round(env["model"], K, schedule=1, table=np.zeros(64, np.int32), max_len=256)
+    with pytest.raises(b.SpecdecError):
+        r.prefill(env["prompt"][:1])   # schedule B needs a pending token besides the prefix
+
+
+def test_stochastic_zero_noise_accepts_every_draft(env):
+    """q = p (no noise): min(1, p/q) = 1 up to rounding, so each round accepts all k drafts
+    and adds a bonus token."""
+    b, S = env["b"], env["shape"]
+    noise = np.zeros((N_NEW + 2 * K + 2, S.vocab), np.float32)
+    r = b.Round(env["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=3,
+                max_len=512)
+    r.prefill(env["prompt"])
+    st, toks = r.run(N_NEW)
+    assert st.accepted_total == K * st.round
+    assert st.n_committed == (K + 1) * st.round
+    assert r.ws.error_bits() == 0
