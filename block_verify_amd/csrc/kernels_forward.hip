@@ -304,6 +304,7 @@ __device__ __forceinline__ f32x4_t mfma_i(const i32x4_t& a, const i32x4_t& b, f3
 }
 
 constexpr int kAttnQPrefetch = 2;   // query tiles (of 16 rows) held in registers
+constexpr int kAttnTileSplit = 4;   // workgroups sharing one chunk's query tiles
 
 template <int HD>
 __global__ __launch_bounds__(64) void attn_chunk_kernel(const bf16_bits* __restrict__ qb, const bf16_bits* __restrict__ Kc,
@@ -325,15 +326,20 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const bf16_bits* __restr
   const int col = lane & 15, grp = lane >> 4;
   const size_t rstride = (size_t)kMaxRows * 8;
 
+  // query tiles t0, t0 + TS, ... of this head (TS = gridDim.z workgroups per chunk)
+  const int t0 = blockIdx.z, TS = gridDim.z;
+  if (t0 >= NTq) return;
   const i32x4_t* qh = reinterpret_cast<const i32x4_t*>(qb + qtile_head(h, HD));
   i32x4_t qv[kAttnQPrefetch][KBH][2];
 #pragma unroll
-  for (int t = 0; t < kAttnQPrefetch; ++t)
+  for (int pt = 0; pt < kAttnQPrefetch; ++pt) {
+    const int t = t0 + pt * TS;
     if (t < NTq)
 #pragma unroll
       for (int kb = 0; kb < KBH; ++kb)
 #pragma unroll
-        for (int hl = 0; hl < 2; ++hl) qv[t][kb][hl] = qh[(((size_t)t * KBH + kb) * 2 + hl) * 64 + lane];
+        for (int hl = 0; hl < 2; ++hl) qv[pt][kb][hl] = qh[(((size_t)t * KBH + kb) * 2 + hl) * 64 + lane];
+  }
 
   const bf16_bits* kbase = Kc + (size_t)h * lp * HD;
   i32x4_t ka[4][KBH];
@@ -367,11 +373,11 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const bf16_bits* __restr
 
   float* ob = o_part + ((size_t)h * max_chunks + c) * rstride * HD;
   float* mb = ml_part + ((size_t)h * max_chunks + c) * rstride * 2;
-  for (int t = 0; t < NTq; ++t) {
+  for (int t = t0, pt = 0; t < NTq; t += TS, ++pt) {
     i32x4_t qt[KBH][2];
-    if (t < kAttnQPrefetch) {
+    if (pt < kAttnQPrefetch) {
 #pragma unroll
-      for (int kb = 0; kb < KBH; ++kb) { qt[kb][0] = qv[t & 1][kb][0]; qt[kb][1] = qv[t & 1][kb][1]; }
+      for (int kb = 0; kb < KBH; ++kb) { qt[kb][0] = qv[pt & 1][kb][0]; qt[kb][1] = qv[pt & 1][kb][1]; }
     } else {
 #pragma unroll
       for (int kb = 0; kb < KBH; ++kb)
@@ -581,7 +587,10 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
         <<<(p.n_groups + CfgQKV::WG_ROWS - 1) / CfgQKV::WG_ROWS, CfgQKV::THREADS, 0, s>>>(p);
 
   // attention: chunk partials, then the merge into the O-projection operand tiles
-  dim3 ag(pl.max_chunks, d.nkv);
+  // query tiles of 16 rows per kv head, spread over up to kAttnTileSplit
+  // workgroups per chunk (each tile's arithmetic is the same either way)
+  const int ntq = (a.rows * d.group() + 15) / 16;
+  dim3 ag(pl.max_chunks, d.nkv, ntq < kAttnTileSplit ? ntq : kAttnTileSplit);
   if (d.hd == 128) {
     attn_chunk_kernel<128><<<ag, 64, 0, s>>>(qb, a.c->k_layer(l), a.c->v_layer(l), a.c->d_len, a.rows, a.c->max_len,
                                               a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, a.gate);
