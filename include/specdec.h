@@ -149,7 +149,10 @@ int specdec_kv_trim(specdec_cache* c, int32_t new_len, int32_t* d_err, void* str
  * sticky device error word at offset 0 (int32). */
 int specdec_workspace_bytes(const specdec_model_desc* desc, int32_t max_rows, int32_t max_len, size_t* bytes);
 
-/* Zero the workspace header (error word) on `stream`. */
+/* Zero the workspace header on `stream`: the error word and the arrival
+ * counters the split-K down projection uses (each forward leaves them at
+ * zero again).  Required once before the first forward.  Forwards that share
+ * one workspace must not overlap (enqueue them on one stream). */
 int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------- forwards */
@@ -159,13 +162,15 @@ int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream);
  * d_tokens int32 [rows] (device).  Outputs (any may be NULL): d_logits fp32
  * [rows][vocab], d_argmax int32 [rows] (lowest index on ties), d_lse fp32
  * [rows] (log-sum-exp of the row).  This is the decode step (rows = 1) and
- * the block verify (rows = k or k+1). */
+ * the block verify (rows = k or k+1).  4-bit models take rows <= 4
+ * (SPECDEC_ECAPACITY beyond). */
 int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t rows,
                         float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
                         void* stream);
 
 /* Prefill `n` tokens in passes of `chunk` rows (chunk clipped to
- * SPECDEC_MAX_ROWS), starting at the current length.  Writes the last row's
+ * SPECDEC_MAX_ROWS, or to 4 for a 4-bit model), starting at the current
+ * length.  Writes the last row's
  * logits / argmax / lse (any may be NULL). */
 int specdec_prefill(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t n, int32_t chunk,
                     float* d_last_logits, int32_t* d_last_argmax, float* d_last_lse, void* d_ws,

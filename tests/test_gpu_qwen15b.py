@@ -131,22 +131,34 @@ def test_gpu_ar_against_oracle_teacher_forced(big, ar_tokens):
     say(f"1.5B AR vs oracle: {N_NEW} tokens, {exempt} differ where the oracle top-2 margin < {MARGIN}")
 
 
+@pytest.mark.parametrize("graph", [False, True])
 @pytest.mark.parametrize("schedule", [0, 1])
-def test_spec_job_equals_gpu_ar(big, ar_tokens, schedule):
+def test_spec_job_equals_gpu_ar(big, ar_tokens, schedule, graph):
+    """The benchmark's job (eager rounds, and the captured round replayed as HIP graphs as
+    the benchmark times it) commits the GPU's greedy tokens."""
     from block_verify_amd.synth import make_draft_table
     b, S = big["b"], big["S"]
     table = make_draft_table(np.array(ar_tokens), S.vocab, C)
     r = b.Round(big["model"], K, schedule=schedule, table=table, max_len=big["max_len"])
     r.prefill(big["prompt"])
-    st, toks = r.run(N_NEW)
+    if graph:
+        r.capture()
+    st, toks = r.run(N_NEW, graph=graph)
     assert list(toks[:N_NEW]) == ar_tokens[:N_NEW]
     assert r.tcache.length() == P + st.n_committed - (1 if schedule == 1 else 0)
     assert r.ws.error_bits() == 0
-    examined = 0
-    n0 = 0
-    # accepted drafts per round follow the table's corruption pattern exactly
-    say(f"schedule {'AB'[schedule]}: {st.round} rounds, {st.accepted_total} drafts accepted")
-    assert st.round >= N_NEW // (K + 1)
+    # accepted drafts per round follow the table's corruption pattern exactly:
+    # a round at n0 accepts the leading drafts that equal the greedy tokens
+    n0, rounds, accepted = 0, 0, 0
+    while n0 < N_NEW:
+        m = 0
+        while m < K and table[n0 + m] == ar_tokens[n0 + m]:
+            m += 1
+        n0 += m + 1
+        rounds += 1
+        accepted += m
+    say(f"schedule {'AB'[schedule]}{' graph' if graph else ''}: {st.round} rounds, {st.accepted_total} drafts accepted")
+    assert (st.round, st.accepted_total) == (rounds, accepted)
 
 
 P4 = 4096
