@@ -20,6 +20,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 arithmetic stays off on the device
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading kernel arguments arrive preloaded in scalar registers
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 

@@ -266,7 +266,7 @@ int specdec_cache_bytes(const specdec_model_desc* desc, int32_t max_len, size_t*
   if (rc) return rc;
   if (!bytes || max_len <= 0) return SPECDEC_EINVAL;
   if (max_len > 65536) return SPECDEC_ECAPACITY;
-  const size_t lp = ((size_t)max_len + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
+  const size_t lp = ((size_t)max_len + kKvPad - 1) / kKvPad * kKvPad;
   size_t kv = align256((size_t)d.L * 2 * d.nkv * lp * d.hd * 2);
   size_t rope = align256((size_t)max_len * (d.hd / 2) * 8);
   *bytes = kv + rope;
@@ -287,12 +287,12 @@ int specdec_cache_create(const specdec_model_desc* desc, void* d_mem, size_t byt
   if (!c) return SPECDEC_EINVAL;
   c->d = d;
   c->kv = static_cast<bf16_bits*>(d_mem);
-  const size_t lpad = ((size_t)max_len + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
+  const size_t lpad = ((size_t)max_len + kKvPad - 1) / kKvPad * kKvPad;
   size_t kv = align256((size_t)d.L * 2 * d.nkv * lpad * d.hd * 2);
   c->rope = reinterpret_cast<float2*>(static_cast<char*>(d_mem) + kv);
   c->d_len = d_len;
   c->max_len = max_len;
-  c->lp = (max_len + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
+  c->lp = (max_len + kKvPad - 1) / kKvPad * kKvPad;
   // RoPE table in double precision on the host: angle = pos * theta^(-2i/d)
   const int half = d.hd / 2;
   std::vector<float2> tab((size_t)max_len * half);

@@ -89,19 +89,71 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 }
 
+// Epilogue operands that do not depend on the product: the residual rows
+// and next-norm gains (RESID, PARTIAL) and the RoPE rotations and cache
+// position of the query/key groups (QKV).  The epilogue wave requests them
+// while its weight tiles are in flight, so the epilogue waits on no load of
+// its own.  Lane l holds entry idx = l + 64 j of the epilogue's loops.
+constexpr int kPreX = 16 * kMaxRows / 64;   // residual values per lane
+constexpr int kPreR = 8 * kMaxRows / 64;    // RoPE pairs per lane
+struct EpiPre {
+  float xv[kPreX];
+  float gain;
+  float2 cs[kPreR];
+  int pos0;
+};
+
+// RESID / PARTIAL: x[m][16 g + i] for idx = 16 m + i, and gain_next[16 g + i]
+// (i = lane % 16 for every j).  Row group g owns these x entries for the
+// whole launch, so reading them before the product is safe.
+template <Epi E>
+__device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, int g, int M, EpiPre& pre) {
+  if constexpr (E == Epi::RESID || E == Epi::PARTIAL) {
+    if (g < p.n_groups) {
+      pre.gain = p.gain_next[16 * g + (lane & 15)];
+#pragma unroll
+      for (int j = 0; j < kPreX; ++j) {
+        const int idx = lane + 64 * j;
+        if (idx < 16 * M) pre.xv[j] = p.x[(size_t)(idx >> 4) * p.H + 16 * g + (idx & 15)];
+      }
+    }
+  }
+}
+
+// QKV: the rotation pairs of this query/key group at positions pos0 + m
+// (idx = 8 m + i, i = lane % 8); pos0 is the cache length read at launch.
+template <Epi E>
+__device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane, int g, int M, EpiPre& pre) {
+  if constexpr (E == Epi::QKV) {
+    const int qg = p.nq * p.hd / 16, kg = p.nkv * p.hd / 16;
+    if (g < qg + kg) {
+      const int sub = (g >= qg ? g - qg : g) % (p.hd / 16), half = p.hd / 2;
+#pragma unroll
+      for (int j = 0; j < kPreR; ++j) {
+        const int idx = lane + 64 * j, m = idx >> 3, pos = pre.pos0 + m;
+        if (m < M && pos < p.max_len) pre.cs[j] = p.rope[(size_t)pos * half + 8 * sub + (idx & 7)];
+      }
+    }
+  }
+}
+
 // Residual epilogue of 16 outputs (one row group g) x M rows: x += y,
 // the next norm's operand tiles of x * gain and the group's sum of squares.
-// f[i][m] holds y on entry and the new x on exit.
+// f[i][m] holds y on entry and the new x on exit; pre holds x and the gains.
 template <int NC>
-__device__ __forceinline__ void resid_epilogue(const GemvParams& p, float (*f)[NC + 1], int lane, int g, int M) {
+__device__ __forceinline__ void resid_epilogue(const GemvParams& p, float (*f)[NC + 1], const EpiPre& pre, int lane,
+                                               int g, int M) {
   const int KBo = p.H >> 5, NP = p.H >> 4;
-  for (int idx = lane; idx < 16 * M; idx += 64) {
-    int i = idx & 15, m = idx >> 4;
-    int n = 16 * g + i;
-    float xn = p.x[(size_t)m * p.H + n] + f[i][m];
-    p.x[(size_t)m * p.H + n] = xn;
-    f[i][m] = xn;
-    btile_put(p.xb_out, KBo, m, n, xn * p.gain_next[n]);
+#pragma unroll
+  for (int j = 0; j < kPreX; ++j) {
+    const int idx = lane + 64 * j;
+    if (idx < 16 * M) {
+      const int i = idx & 15, m = idx >> 4, n = 16 * g + i;
+      const float xn = pre.xv[j] + f[i][m];
+      p.x[(size_t)m * p.H + n] = xn;
+      f[i][m] = xn;
+      btile_put(p.xb_out, KBo, m, n, xn * pre.gain);
+    }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -164,8 +216,9 @@ __device__ __forceinline__ void norm_finish(const GemvParams& p, int w, int lane
 // m; rsc[m] the RMSNorm scale of row m (norm epilogues).  LMHEAD runs on the
 // whole workgroup; the others on wave (rg, ks == 0) of each row group.
 template <int WG_ROWS, int NC, Epi E>
-__device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[16][NC + 1], const float* rsc, int w,
-                                              int lane, int rg, int ks, int g, int sidx, int M) {
+__device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[16][NC + 1], const float* rsc,
+                                              const EpiPre& pre, int w, int lane, int rg, int ks, int g, int sidx,
+                                              int M) {
   (void)w;
   if constexpr (E == Epi::LMHEAD) {
     // logits and this workgroup's (max, argmax, sum exp) per row
@@ -212,23 +265,26 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
   // one wave per row group runs the epilogue
   float (*f)[NC + 1] = fin[rg];
   if constexpr (E == Epi::QKV) {
-    const int pos0 = *p.d_len;
+    const int pos0 = pre.pos0;
     const int qg = p.nq * p.hd / 16, kg = p.nkv * p.hd / 16;
     const int per_head = p.hd / 16, half = p.hd / 2;
     if (g < qg + kg) {
       const bool is_k = g >= qg;
       const int gg = is_k ? g - qg : g;
       const int head = gg / per_head, sub = gg % per_head;
-      for (int idx = lane; idx < 8 * M; idx += 64) {
-        int i = idx & 7, m = idx >> 3;
-        int pos = pos0 + m;
-        if (pos >= p.max_len) continue;
+#pragma unroll
+      for (int j = 0; j < kPreR; ++j) {
+        const int idx = lane + 64 * j, i = idx & 7, m = idx >> 3;
+        const int pos = pos0 + m;
+        if (m >= M || pos >= p.max_len) continue;
         float r = rsc[m];
         float y1 = f[i][m] * r, y2 = f[i + 8][m] * r;
         int d1 = 8 * sub + i;
-        float2 cs = p.rope[(size_t)pos * half + d1];
-        float o1 = y1 * cs.x - y2 * cs.y;
-        float o2 = y2 * cs.x + y1 * cs.y;
+        const float2 cs = pre.cs[j];
+        // explicit fused forms: the rounding must not depend on how the
+        // compiler contracts this loop in each launch shape
+        const float o1 = fmaf(y1, cs.x, -(y2 * cs.y));
+        const float o2 = fmaf(y2, cs.x, y1 * cs.y);
         if (!is_k) {
           const int G = p.nq / p.nkv;
           const float qs = 1.0f / sqrtf((float)p.hd);
@@ -290,10 +346,10 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    resid_epilogue<NC>(p, f, lane, g, M);
+    resid_epilogue<NC>(p, f, pre, lane, g, M);
     if (lane == 0) __hip_atomic_store(p.cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {  // RESID
-    resid_epilogue<NC>(p, f, lane, g, M);
+    resid_epilogue<NC>(p, f, pre, lane, g, M);
   }
 }
 

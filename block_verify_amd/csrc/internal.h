@@ -66,7 +66,7 @@ struct specdec_model {
 
 // K is [nkv][lp][hd] per layer; V is kept transposed, [nkv][hd][lp], so the
 // attention's P*V operand reads 8 consecutive keys of one head dim as 16
-// contiguous bytes.  lp = max_len rounded up to the 64-key attention chunk.
+// contiguous bytes.  lp = max_len rounded up to kKvPad positions.
 struct specdec_cache {
   sd::Dims d;
   bf16_bits* kv;      // [L][K|V][...]
@@ -80,7 +80,12 @@ struct specdec_cache {
 
 namespace sd {
 
-constexpr int kAttnChunk = 64;
+#ifndef SD_ATTN_CHUNK
+#define SD_ATTN_CHUNK 64
+#endif
+constexpr int kAttnChunk = SD_ATTN_CHUNK;   // keys per attention chunk (64 or 128)
+constexpr int kKvPad = 128;                 // cache positions are padded to a multiple of this
+static_assert(kKvPad % kAttnChunk == 0, "chunks tile the padded cache");
 constexpr int kWsHeader = 65536;   // error word + split-K arrival counters (zeroed once)
 constexpr int kMaxSplit = 8;
 // K splits of the down projection: bf16 (tuned on the verify forward) and

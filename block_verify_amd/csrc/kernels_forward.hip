@@ -63,6 +63,11 @@ using CfgDown = LaunchCfg<SD_CFG_DOWN>;
 using CfgLM = LaunchCfg<SD_CFG_LM>;
 static_assert(CfgDown::WG_ROWS == 1, "the split-K launch maps one row group per workgroup");
 static_assert(kDownSplit <= kMaxSplit, "partial buffer holds kMaxSplit splits");
+#ifndef SD_O_SPLIT
+#define SD_O_SPLIT 1
+#endif
+constexpr int kOSplit = SD_O_SPLIT;   // K splits of the O projection (1: one workgroup per row group)
+static_assert(kOSplit <= kMaxSplit && (kOSplit == 1 || CfgO::WG_ROWS == 1), "O split-K shape");
 
 
 hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStream_t s);
@@ -183,26 +188,40 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 // Streams the weight tiles of one row group over k-blocks [kb0, kb1) through
 // MFMA.  Tiles travel as 32-bit integer vectors (bit-cast to bf16 only at the
 // MFMA) so the guarded unroll never needs 16-bit lane merges; kb0/kb1 are
-// wave-uniform, so the guards are scalar branches.
-template <int NT, int U>
+// wave-uniform, so the guards are scalar branches.  `issued` runs once, right
+// after the first batch of loads has been requested (also when the wave has
+// no k-blocks).
+template <int NT, int U, typename Issued>
 __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, const bf16x8_t* __restrict__ B, int KB,
-                                            int kb0, int kb1, int lane, f32x4_t (&acc)[NT]) {
+                                            int kb0, int kb1, int lane, f32x4_t (&acc)[NT], Issued&& issued) {
   const i32x4_t* a = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
   const i32x4_t* b = reinterpret_cast<const i32x4_t*>(B) + (size_t)kb0 * 64 + lane;
   const size_t tstride = (size_t)KB * 64;
   const int n = kb1 - kb0;
-  // up to U weight tiles in flight per wave; the activation tiles are L2-resident
-  for (int i = 0; i < n; i += U) {
-    i32x4_t av[U];
-    i32x4_t bv[U][NT];
+  if (n <= 0) {
+    issued();
+    return;
+  }
+  // up to U weight tiles in flight per wave; the activation tiles are
+  // L2-resident.  The loads of a batch are unconditional (slots past the
+  // wave's last k-block re-read it, and their products are skipped): guarded
+  // loads into register arrays make the compiler wait on each one.
+  i32x4_t av[U];
+  i32x4_t bv[U][NT];
+  auto load = [&](int i) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i + u < n) av[u] = __builtin_nontemporal_load(a + (size_t)(i + u) * 64);
+    for (int u = 0; u < U; ++u) {
+      const int kb = i + u < n ? i + u : n - 1;
+      av[u] = __builtin_nontemporal_load(a + (size_t)kb * 64);
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i + u < n)
+    for (int u = 0; u < U; ++u) {
+      const int kb = i + u < n ? i + u : n - 1;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bv[u][t] = b[t * tstride + (size_t)(i + u) * 64];
+      for (int t = 0; t < NT; ++t) bv[u][t] = b[t * tstride + (size_t)kb * 64];
+    }
+  };
+  auto multiply = [&](int i) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (i + u < n)
@@ -210,12 +229,36 @@ __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, cons
         for (int t = 0; t < NT; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
                                                           __builtin_bit_cast(bf16x8_t, bv[u][t]), acc[t], 0, 0, 0);
+  };
+  // the first batch is peeled so `issued` has one place in the schedule; the
+  // scheduling barrier keeps the weight requests ahead of whatever `issued`
+  // requests (the compiler would otherwise hoist those small loads, and the
+  // waits they carry, above the weight stream)
+  load(0);
+  __builtin_amdgcn_sched_barrier(0);
+  issued();
+  __builtin_amdgcn_sched_barrier(0);
+  multiply(0);
+  for (int i = U; i < n; i += U) {
+    load(i);
+    multiply(i);
   }
 }
 
+// The fields the weight stream needs come first as plain arguments, which
+// the launch preloads into scalar registers; the rest of GemvParams is read
+// from the argument block where it is used.
 template <int NT, int WG_ROWS, int WK, int U, Epi E>
-__global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
-  if (p.gate && *p.gate == 0) return;
+__global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* gate, const int32_t* d_len,
+                                                                 const bf16x8_t* __restrict__ A,
+                                                                 const bf16x8_t* __restrict__ B, int KB, int n_groups,
+                                                                 int rows, int nsplit_arg, GemvParams p) {
+  EpiPre pre;
+  // the gate word (the length stands in for a null gate) and the cache
+  // position are requested together, before any branch
+  const int gv = *(gate ? gate : d_len);
+  if constexpr (E == Epi::QKV) pre.pos0 = *d_len;
+  if (gate && gv == 0) return;
   constexpr int NW = WG_ROWS * WK;
   constexpr int NC = NT * 8;        // activation rows covered
   constexpr int RPW = (kMaxRows + NW - 1) / NW;
@@ -228,23 +271,38 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
   // scalar branches instead of EXEC-masked regions around MFMA operands
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = w / WK, ks = w % WK;
-  const int nsplit = (E == Epi::PARTIAL) ? p.nsplit : 1;
+  const int nsplit = (E == Epi::PARTIAL) ? nsplit_arg : 1;
   const int sidx = (E == Epi::PARTIAL) ? (int)(blockIdx.x % nsplit) : 0;
   const int g = (E == Epi::PARTIAL) ? (int)(blockIdx.x / nsplit) : (int)(blockIdx.x * WG_ROWS + rg);
-  const int M = p.rows;
+  const int M = rows;
 
-  // sums of squares of the normalised input, issued before the weight stream
+  // Right after the first weight requests (which need only the preloaded
+  // arguments): the sums of squares of the normalised input, the epilogue
+  // wave's residual operands and RoPE rotations.  They are used only after
+  // the product, so their latency hides under the weight stream.
   constexpr bool kNorm = (E == Epi::QKV || E == Epi::SWIGLU || E == Epi::LMHEAD);
   float ssv[RPW][4];
-  if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
+  auto prefetch = [&] {
+    if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
+    if (ks == 0) {
+      epi_prefetch_x<E>(p, lane, g, M, pre);
+      epi_prefetch_rope<E>(p, lane, g, M, pre);
+    }
+  };
 
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (g < p.n_groups) {
-    const int s0 = (int)(((long)sidx * p.KB) / nsplit), s1 = (int)(((long)(sidx + 1) * p.KB) / nsplit);
-    const int kb0 = s0 + (int)(((long)ks * (s1 - s0)) / WK), kb1 = s0 + (int)(((long)(ks + 1) * (s1 - s0)) / WK);
-    mfma_stream<NT, U>(p.A + (size_t)g * p.KB * 64, p.B, p.KB, kb0, kb1, lane, acc);
+  if (g < n_groups) {
+    // 32-bit unsigned arithmetic: every term is small (split index < 8,
+    // k-blocks < 2^16), and a 64-bit division costs hundreds of instructions
+    const unsigned uk = (unsigned)KB, un = (unsigned)nsplit;
+    const int s0 = (int)((unsigned)sidx * uk / un), s1 = (int)((unsigned)(sidx + 1) * uk / un);
+    const unsigned span = (unsigned)(s1 - s0);
+    const int kb0 = s0 + (int)((unsigned)ks * span / WK), kb1 = s0 + (int)((unsigned)(ks + 1) * span / WK);
+    mfma_stream<NT, U>(A + (size_t)g * KB * 64, B, KB, kb0, kb1, lane, acc, prefetch);
+  } else {
+    prefetch();
   }
   if constexpr (kNorm) norm_finish<RPW, NW>(p, w, lane, M, ssv, rsc);
   // hi + lo (columns c and c+8) in registers, then the waves' partials in LDS
@@ -266,7 +324,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
   }
   __syncthreads();
 
-  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, w, lane, rg, ks, g, sidx, M);
+  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, pre, w, lane, rg, ks, g, sidx, M);
 }
 
 // ---------------------------------------------------------------------------
@@ -274,15 +332,20 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(GemvParams p) {
 // boundaries are fixed by absolute key index, then a fixed-order merge of the
 // chunk partials per output.
 //
-// Chunk partial: one wave per (kv head, chunk).  All operand tiles are loaded
-// up front: K rows (operand A of S^T = K Q^T; 8 consecutive head dims per
-// lane), V^T rows (operand A of O^T = V^T P^T; the cache keeps V transposed so
-// 8 consecutive keys of one head dim are 16 contiguous bytes) and the query
-// tiles.  The bf16 hi/lo split of q and of P runs along the MFMA k dimension
-// (two MFMAs into one accumulator), so no cross-lane combine is needed.  Per
-// 16-row query tile: scores, causal mask, row max / sum of exp over the chunk,
-// P^T through a small LDS tile, O^T on MFMA.  Keys past the current length
-// are masked in the scores and zeroed in V^T.
+// Chunk partial: one workgroup per (kv head, chunk, query-tile slice) with
+// one wave per 16 keys.  Wave w loads the K rows of keys 16w..16w+15
+// (operand A of S^T = K Q^T; 8 consecutive head dims per lane) and the V^T
+// rows of its share of the head dims (operand A of O^T = V^T P^T over all
+// keys of the chunk; the cache
+// keeps V transposed so 8 consecutive keys of one head dim are 16 contiguous
+// bytes), so each wave keeps a small, fixed set of loads in flight.  Per
+// 16-row query tile: each wave's 16 x 16 score tile goes to LDS with the
+// causal mask applied; every wave then reads the chunk's scores of its lanes' query
+// rows, forms the row max and sum of exp over the chunk in one fixed order
+// (so all waves hold identical values) and P^T for its own output dims.  The
+// bf16 hi/lo split of q and of P runs along the MFMA k dimension (two MFMAs
+// into one accumulator).  Keys past the current length are masked in the
+// scores and zeroed in V^T.
 // ---------------------------------------------------------------------------
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
@@ -303,63 +366,84 @@ __device__ __forceinline__ f32x4_t mfma_i(const i32x4_t& a, const i32x4_t& b, f3
                                                  0, 0);
 }
 
-constexpr int kAttnQPrefetch = 2;   // query tiles (of 16 rows) held in registers
-constexpr int kAttnTileSplit = 4;   // workgroups sharing one chunk's query tiles
+constexpr int kAttnWaves = kAttnChunk / 16;   // waves per chunk workgroup: 16 keys each
+#ifndef SD_ATTN_TILE_SPLIT
+#define SD_ATTN_TILE_SPLIT 4
+#endif
+constexpr int kAttnTileSplit = SD_ATTN_TILE_SPLIT;   // workgroups sharing one chunk's query tiles
+constexpr int kAttnMaxWgTiles = (kQTiles + kAttnTileSplit - 1) / kAttnTileSplit;   // query tiles per workgroup
 
 template <int HD>
-__global__ __launch_bounds__(64) void attn_chunk_kernel(const bf16_bits* __restrict__ qb, const bf16_bits* __restrict__ Kc,
-                                                        const bf16_bits* __restrict__ Vt, const int32_t* __restrict__ d_len,
-                                                        int rows, int max_len, int lp, int G, float* __restrict__ o_part,
-                                                        float* __restrict__ ml_part, int max_chunks, const int32_t* gate) {
-  if (gate && *gate == 0) return;
-  constexpr int C = kAttnChunk;   // 64 keys
-  constexpr int KBH = HD / 32;    // k-blocks over the head dimension
-  constexpr int DT = HD / 16;     // 16-dim output tiles
-  __shared__ __attribute__((aligned(16))) float Pl[16][C + 4];
-  const int c = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
+    const int32_t* gate, const int32_t* __restrict__ d_len, const bf16_bits* __restrict__ qb,
+    const bf16_bits* __restrict__ Kc, const bf16_bits* __restrict__ Vt, int rows, int max_len, int lp, int G,
+    float* __restrict__ o_part, float* __restrict__ ml_part, int max_chunks) {
+  // the gate word (the length stands in for a null gate) and the length are
+  // requested together, before any branch
+  const int gv = *(gate ? gate : d_len);
   const int len = *d_len;
+  constexpr int C = kAttnChunk;                 // keys per chunk
+  constexpr int NW = kAttnWaves;
+  constexpr int KBH = HD / 32;                  // k-blocks over the head dimension
+  constexpr int DT = HD / 16;                   // 16-dim output tiles
+  constexpr int DTW = (DT + NW - 1) / NW;       // output tiles per wave
+  constexpr int KB2 = C / 32;                   // 32-key blocks of P^T
+  __shared__ __attribute__((aligned(16))) float Pl[16][C + 4];
+  __shared__ i32x4_t qs[kAttnMaxWgTiles][KBH * 2][64];
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int T = len + rows;
   if (T > max_len) T = max_len;
   const int key0 = c * C;
-  if (key0 >= T) return;
+  // one branch on both words, so neither load waits for the other
+  if (((gate != nullptr) & (gv == 0)) | (key0 >= T)) return;
   const int R = rows * G, NTq = (R + 15) / 16;
   const int col = lane & 15, grp = lane >> 4;
   const size_t rstride = (size_t)kMaxRows * 8;
 
-  // query tiles t0, t0 + TS, ... of this head (TS = gridDim.z workgroups per chunk)
+  // query tiles t0, t0 + TS, ... of this head (TS = gridDim.z workgroups per
+  // chunk), staged once per workgroup in LDS: each wave loads a share
   const int t0 = blockIdx.z, TS = gridDim.z;
   if (t0 >= NTq) return;
+  const int ntw = (NTq - t0 + TS - 1) / TS;   // tiles of this workgroup (<= kAttnMaxWgTiles)
   const i32x4_t* qh = reinterpret_cast<const i32x4_t*>(qb + qtile_head(h, HD));
-  i32x4_t qv[kAttnQPrefetch][KBH][2];
+  // this wave's share of the query tile parts, requested before the K/V rows
+  // and written to LDS once every load of the wave is in flight
+  // (unconditional loads, parts past the workgroup's tiles re-read part 0:
+  // guarded loads into a register array would each be waited on)
+  constexpr int QPW = (kAttnMaxWgTiles * KBH * 2 + NW - 1) / NW;
+  i32x4_t qreg[QPW];
 #pragma unroll
-  for (int pt = 0; pt < kAttnQPrefetch; ++pt) {
-    const int t = t0 + pt * TS;
-    if (t < NTq)
-#pragma unroll
-      for (int kb = 0; kb < KBH; ++kb)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) qv[pt][kb][hl] = qh[(((size_t)t * KBH + kb) * 2 + hl) * 64 + lane];
+  for (int j = 0; j < QPW; ++j) {
+    int idx = w + NW * j;
+    if (idx >= ntw * KBH * 2) idx = 0;
+    const int pt = idx / (KBH * 2), part = idx % (KBH * 2);
+    qreg[j] = qh[((size_t)(t0 + pt * TS) * KBH * 2 + part) * 64 + lane];
   }
 
+  // this wave's 16 key rows
   const bf16_bits* kbase = Kc + (size_t)h * lp * HD;
-  i32x4_t ka[4][KBH];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    int krow = key0 + 16 * kt + col;
+  i32x4_t ka[KBH];
+  {
+    int krow = key0 + 16 * w + col;
     if (krow > T - 1) krow = T - 1;
 #pragma unroll
     for (int kb = 0; kb < KBH; ++kb)
-      ka[kt][kb] = *reinterpret_cast<const i32x4_t*>(kbase + (size_t)krow * HD + kb * 32 + 8 * grp);
+      ka[kb] = *reinterpret_cast<const i32x4_t*>(kbase + (size_t)krow * HD + kb * 32 + 8 * grp);
   }
+  // this wave's V^T rows (head dims 16 * (DTW * w + j) + col), all keys of the chunk
   const bf16_bits* vbase = Vt + (size_t)h * HD * lp;
-  i32x4_t va[DT][2];
+  i32x4_t va[DTW][KB2];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int j = 0; j < DTW; ++j)
+    if (DTW * w + j < DT)
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-      va[dt][kb2] = *reinterpret_cast<const i32x4_t*>(vbase + (size_t)(16 * dt + col) * lp + key0 + 32 * kb2 + 8 * grp);
+      for (int kb2 = 0; kb2 < KB2; ++kb2)
+        va[j][kb2] = *reinterpret_cast<const i32x4_t*>(vbase + (size_t)(16 * (DTW * w + j) + col) * lp + key0 +
+                                                        32 * kb2 + 8 * grp);
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
+  for (int kb2 = 0; kb2 < KB2; ++kb2) {
     const int nvalid = T - (key0 + 32 * kb2 + 8 * grp);
     if (nvalid < 8) {
       i32x4_t mask;
@@ -367,141 +451,185 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const bf16_bits* __restr
       for (int j = 0; j < 4; ++j)
         mask[j] = (2 * j < nvalid ? 0x0000FFFF : 0) | (2 * j + 1 < nvalid ? (int32_t)0xFFFF0000u : 0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) va[dt][kb2] &= mask;
+      for (int j = 0; j < DTW; ++j) va[j][kb2] &= mask;
     }
   }
 
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    const int idx = w + NW * j;
+    if (idx < ntw * KBH * 2) qs[idx / (KBH * 2)][idx % (KBH * 2)][lane] = qreg[j];
+  }
   float* ob = o_part + ((size_t)h * max_chunks + c) * rstride * HD;
   float* mb = ml_part + ((size_t)h * max_chunks + c) * rstride * 2;
+  // the staged query tiles are complete
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   for (int t = t0, pt = 0; t < NTq; t += TS, ++pt) {
     i32x4_t qt[KBH][2];
-    if (pt < kAttnQPrefetch) {
 #pragma unroll
-      for (int kb = 0; kb < KBH; ++kb) { qt[kb][0] = qv[pt & 1][kb][0]; qt[kb][1] = qv[pt & 1][kb][1]; }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KBH; ++kb)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) qt[kb][hl] = qh[(((size_t)t * KBH + kb) * 2 + hl) * 64 + lane];
+    for (int kb = 0; kb < KBH; ++kb) {
+      qt[kb][0] = qs[pt][2 * kb][lane];
+      qt[kb][1] = qs[pt][2 * kb + 1][lane];
     }
-    // S^T tile per 16 keys: lane (col = query row, grp) holds keys 4 * grp + r
     const int row = 16 * t + col;
     const int m = row / G;
     const bool rvalid = row < R;
-    float sv[4][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    // S^T tile of this wave's keys: lane (col = query row, grp) holds keys 16 w + 4 grp + r
+    {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KBH; ++kb) {
-        acc = mfma_i(ka[kt][kb], qt[kb][0], acc);
-        acc = mfma_i(ka[kt][kb], qt[kb][1], acc);
+        acc = mfma_i(ka[kb], qt[kb][0], acc);
+        acc = mfma_i(ka[kb], qt[kb][1], acc);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kidx = key0 + 16 * kt + 4 * grp + r;
+        const int kidx = key0 + 16 * w + 4 * grp + r;
         const bool ok = rvalid && kidx < T && kidx <= len + m;
-        sv[kt][r] = ok ? acc[r] : -INFINITY;
-        mx = fmaxf(mx, sv[kt][r]);
+        Pl[col][16 * w + 4 * grp + r] = ok ? acc[r] : -INFINITY;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // the row's C scores: lane (col, grp) holds keys 32 kb2 + 8 grp + e
+    float sv[KB2][8];
+#pragma unroll
+    for (int kb2 = 0; kb2 < KB2; ++kb2) {
+      const float4* src = reinterpret_cast<const float4*>(&Pl[col][32 * kb2 + 8 * grp]);
+      const float4 p0 = src[0], p1 = src[1];
+      sv[kb2][0] = p0.x; sv[kb2][1] = p0.y; sv[kb2][2] = p0.z; sv[kb2][3] = p0.w;
+      sv[kb2][4] = p1.x; sv[kb2][5] = p1.y; sv[kb2][6] = p1.z; sv[kb2][7] = p1.w;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < KB2; ++kb2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[kb2][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     float sum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kb2 = 0; kb2 < KB2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = (mx == -INFINITY) ? 0.f : __expf(sv[kt][r] - mx);
-        sv[kt][r] = pv;
+      for (int e = 0; e < 8; ++e) {
+        const float pv = (mx == -INFINITY) ? 0.f : __expf(sv[kb2][e] - mx);
+        sv[kb2][e] = pv;
         sum += pv;
       }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Pl[col][16 * kt + 4 * grp + r] = sv[kt][r];
-    if (grp == 0 && rvalid) { mb[row * 2] = mx; mb[row * 2 + 1] = sum; }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (w == 0 && grp == 0 && rvalid) { mb[row * 2] = mx; mb[row * 2 + 1] = sum; }
     // operand B: P^T (keys x query rows), hi and lo parts along k
-    i32x4_t pb[2][2];
+    i32x4_t pb[KB2][2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const float4* src = reinterpret_cast<const float4*>(&Pl[col][32 * kb2 + 8 * grp]);
-      const float4 p0 = src[0], p1 = src[1];
-      const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      pack_hilo8(pv8, pb[kb2][0], pb[kb2][1]);
-    }
+    for (int kb2 = 0; kb2 < KB2; ++kb2) pack_hilo8(sv[kb2], pb[kb2][0], pb[kb2][1]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int j = 0; j < DTW; ++j) {
+      if (DTW * w + j >= DT) break;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        acc = mfma_i(va[dt][kb2], pb[kb2][0], acc);
-        acc = mfma_i(va[dt][kb2], pb[kb2][1], acc);
+      for (int kb2 = 0; kb2 < KB2; ++kb2) {
+        acc = mfma_i(va[j][kb2], pb[kb2][0], acc);
+        acc = mfma_i(va[j][kb2], pb[kb2][1], acc);
       }
-      // lane (col = query row, grp) holds O[row][16 dt + 4 grp + r]
+      // lane (col = query row, grp) holds O[row][16 (DTW w + j) + 4 grp + r]
       if (rvalid)
-        *reinterpret_cast<float4*>(ob + (size_t)row * HD + 16 * dt + 4 * grp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(ob + (size_t)row * HD + 16 * (DTW * w + j) + 4 * grp) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
+    // the next tile rewrites the score tile
     __builtin_amdgcn_s_barrier();
   }
 }
 
-// Merge: one workgroup per (row, query head), thread d owns head dim d.  The
-// partial loads of a batch of chunks are issued first; the chunk statistics
-// go to LDS and every thread forms the same weights and normaliser in chunk
-// order; the sum over chunks runs in chunk order.
+// Merge: one workgroup of four waves per (row, query head, 64 head dims);
+// lane l owns head dim 64 * blockIdx.y + l and wave w the chunks c = w, w + 4,
+// ...  The partial loads of the first batch of chunks and the first
+// statistics are issued before the cache length arrives (entries past the
+// row's chunk count are read but never used).  The chunk statistics go to
+// LDS and every thread forms the same weights in chunk order; each wave sums
+// its chunks in increasing order, then the four wave sums are added in wave
+// order and divided by the normaliser (summed in chunk order).  Every order
+// depends only on the row's own position.
 constexpr int kMaxMergeChunks = 1024;
+constexpr int kMergeWaves = 4;
 
 template <int HD>
-__global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part,
-                                                       const int32_t* __restrict__ d_len, int rows, int max_len, int nq,
-                                                       int nkv, int max_chunks, bf16_bits* __restrict__ ob,
-                                                       const int32_t* gate) {
-  if (gate && *gate == 0) return;
+__global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
+    const int32_t* gate, const int32_t* __restrict__ d_len, const float* __restrict__ o_part,
+    const float* __restrict__ ml_part, int rows, int max_len, int nq, int nkv, int max_chunks,
+    bf16_bits* __restrict__ ob) {
   __shared__ float sm[kMaxMergeChunks], sw[kMaxMergeChunks], sl[kMaxMergeChunks];
+  __shared__ float wsum[kMergeWaves][64];
+  const int gv = *(gate ? gate : d_len);   // requested with the length, before any branch
+  const int len = *d_len;
   const int m = blockIdx.x / nq, hq = blockIdx.x % nq;
   const int G = nq / nkv, h = hq / G, r = m * G + hq % G;
-  int pos = *d_len + m;
-  if (pos >= max_len) pos = max_len - 1;
-  const int nch = pos / kAttnChunk + 1;
   const size_t rstride = (size_t)kMaxRows * 8;
   const float* ml = ml_part + ((size_t)h * max_chunks * rstride + r) * 2;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int d = 64 * blockIdx.y + lane;
   const float* op = o_part + ((size_t)h * max_chunks * rstride + r) * HD + d;
   const size_t cst = rstride * HD;
-  constexpr int BATCH = 48;
+  constexpr int BATCH = 36;   // chunks per wave per pass
+  constexpr int NT = 64 * kMergeWaves;
   float ov[BATCH];
 #pragma unroll
-  for (int u = 0; u < BATCH; ++u) ov[u] = (u < nch) ? op[(size_t)u * cst] : 0.f;
-  for (int c = d; c < nch; c += HD) {
+  for (int u = 0; u < BATCH; ++u) {
+    const int c = w + kMergeWaves * u;
+    ov[u] = (c < max_chunks) ? op[(size_t)c * cst] : 0.f;
+  }
+  float m0 = 0.f, l0 = 0.f;
+  if ((int)threadIdx.x < max_chunks) {
+    m0 = ml[(size_t)threadIdx.x * rstride * 2];
+    l0 = ml[(size_t)threadIdx.x * rstride * 2 + 1];
+  }
+  if (gate && gv == 0) return;
+  int pos = len + m;
+  if (pos >= max_len) pos = max_len - 1;
+  const int nch = pos / kAttnChunk + 1;
+  if ((int)threadIdx.x < nch) { sm[threadIdx.x] = m0; sl[threadIdx.x] = l0; }
+  for (int c = threadIdx.x + NT; c < nch; c += NT) {
     sm[c] = ml[(size_t)c * rstride * 2];
     sl[c] = ml[(size_t)c * rstride * 2 + 1];
   }
   __syncthreads();
   float mx = -INFINITY;
   for (int c = 0; c < nch; ++c) mx = fmaxf(mx, sm[c]);
-  for (int c = d; c < nch; c += HD) sw[c] = (sm[c] == -INFINITY) ? 0.f : __expf(sm[c] - mx);
+  for (int c = threadIdx.x; c < nch; c += NT) sw[c] = (sm[c] == -INFINITY) ? 0.f : __expf(sm[c] - mx);
   __syncthreads();
-  float L = 0.f;
-  for (int c = 0; c < nch; ++c) L = fmaf(sw[c], sl[c], L);
   float acc = 0.f;
 #pragma unroll
-  for (int u = 0; u < BATCH; ++u)
-    if (u < nch) acc = fmaf(sw[u], ov[u], acc);
-  for (int c0 = BATCH; c0 < nch; c0 += BATCH) {
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) ov[u] = (c0 + u < nch) ? op[(size_t)(c0 + u) * cst] : 0.f;
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-      if (c0 + u < nch) acc = fmaf(sw[c0 + u], ov[u], acc);
+  for (int u = 0; u < BATCH; ++u) {
+    const int c = w + kMergeWaves * u;
+    if (c < nch) acc = fmaf(sw[c], ov[u], acc);
   }
-  btile_put(ob, (nq * HD) >> 5, m, hq * HD + d, acc / L);
+  for (int c0 = kMergeWaves * BATCH; c0 < nch; c0 += kMergeWaves * BATCH) {
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = c0 + w + kMergeWaves * u;
+      ov[u] = (c < nch) ? op[(size_t)c * cst] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = c0 + w + kMergeWaves * u;
+      if (c < nch) acc = fmaf(sw[c], ov[u], acc);
+    }
+  }
+  wsum[w][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    float L = 0.f;
+    for (int c = 0; c < nch; ++c) L = fmaf(sw[c], sl[c], L);
+    float o = 0.f;
+#pragma unroll
+    for (int v = 0; v < kMergeWaves; ++v) o += wsum[v][lane];
+    btile_put(ob, (nq * HD) >> 5, m, hq * HD + d, o / L);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -560,6 +688,12 @@ __global__ __launch_bounds__(256) void lm_reduce_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 // Host launcher of one forward pass.
 // ---------------------------------------------------------------------------
+template <int NT, int WG_ROWS, int WK, int U, Epi E>
+static void launch_gemv(int wgs, hipStream_t s, const GemvParams& p) {
+  gemv_kernel<NT, WG_ROWS, WK, U, E><<<wgs, 64 * WG_ROWS * WK, 0, s>>>(p.gate, p.d_len, p.A, p.B, p.KB, p.n_groups,
+                                                                      p.rows, p.nsplit, p);
+}
+
 template <int NT>
 static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   const Dims& d = a.m->d;
@@ -583,8 +717,8 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.ss_in = ss; p.qb = qb; p.k_cache = a.c->k_layer(l); p.v_cache = a.c->v_layer(l);
   if (q4) launch_q4_linear(Q4Linear::QKV, p, L.q_wqkv, L.s_wqkv, d.H, s);
   else
-    gemv_kernel<NT, CfgQKV::WG_ROWS, CfgQKV::WK, CfgQKV::template U<NT>, Epi::QKV>
-        <<<(p.n_groups + CfgQKV::WG_ROWS - 1) / CfgQKV::WG_ROWS, CfgQKV::THREADS, 0, s>>>(p);
+    launch_gemv<NT, CfgQKV::WG_ROWS, CfgQKV::WK, CfgQKV::template U<NT>, Epi::QKV>(
+        (p.n_groups + CfgQKV::WG_ROWS - 1) / CfgQKV::WG_ROWS, s, p);
 
   // attention: chunk partials, then the merge into the O-projection operand tiles
   // query tiles of 16 rows per kv head, spread over up to kAttnTileSplit
@@ -592,15 +726,17 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   const int ntq = (a.rows * d.group() + 15) / 16;
   dim3 ag(pl.max_chunks, d.nkv, ntq < kAttnTileSplit ? ntq : kAttnTileSplit);
   if (d.hd == 128) {
-    attn_chunk_kernel<128><<<ag, 64, 0, s>>>(qb, a.c->k_layer(l), a.c->v_layer(l), a.c->d_len, a.rows, a.c->max_len,
-                                              a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, a.gate);
-    attn_merge_kernel<128><<<a.rows * d.nq, 128, 0, s>>>(att_o, att_ml, a.c->d_len, a.rows, a.c->max_len, d.nq, d.nkv,
-                                                         pl.max_chunks, ob, a.gate);
+    attn_chunk_kernel<128><<<ag, 64 * kAttnWaves, 0, s>>>(a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l),
+                                                           a.rows, a.c->max_len, a.c->lp, d.group(), att_o, att_ml,
+                                                           pl.max_chunks);
+    attn_merge_kernel<128><<<dim3(a.rows * d.nq, 2), 64 * kMergeWaves, 0, s>>>(
+        a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
   } else {
-    attn_chunk_kernel<64><<<ag, 64, 0, s>>>(qb, a.c->k_layer(l), a.c->v_layer(l), a.c->d_len, a.rows, a.c->max_len,
-                                             a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, a.gate);
-    attn_merge_kernel<64><<<a.rows * d.nq, 64, 0, s>>>(att_o, att_ml, a.c->d_len, a.rows, a.c->max_len, d.nq, d.nkv,
-                                                       pl.max_chunks, ob, a.gate);
+    attn_chunk_kernel<64><<<ag, 64 * kAttnWaves, 0, s>>>(a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l),
+                                                          a.rows, a.c->max_len, a.c->lp, d.group(), att_o, att_ml,
+                                                          pl.max_chunks);
+    attn_merge_kernel<64><<<dim3(a.rows * d.nq, 1), 64 * kMergeWaves, 0, s>>>(
+        a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
   }
 
   // O projection + residual; next input is the MLP norm
@@ -608,9 +744,14 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.A = L.wo; p.B = reinterpret_cast<const bf16x8_t*>(ob); p.KB = d.qdim() / 32; p.n_groups = d.H / 16;
   p.x = x; p.gain_next = L.mlp_norm; p.xb_out = xb; p.ss_out = ss;
   if (q4) launch_q4_linear(Q4Linear::O, p, L.q_wo, L.s_wo, d.qdim(), s);
-  else
-    gemv_kernel<NT, CfgO::WG_ROWS, CfgO::WK, CfgO::template U<NT>, Epi::RESID>
-        <<<(p.n_groups + CfgO::WG_ROWS - 1) / CfgO::WG_ROWS, CfgO::THREADS, 0, s>>>(p);
+  else if (kOSplit > 1) {
+    p.part = reinterpret_cast<float*>(ws + pl.part);
+    p.nsplit = kOSplit;
+    p.cnt = reinterpret_cast<int32_t*>(ws + pl.cnt);
+    launch_gemv<NT, 1, CfgO::WK, CfgO::template U<NT>, Epi::PARTIAL>(p.n_groups * kOSplit, s, p);
+  } else
+    launch_gemv<NT, CfgO::WG_ROWS, CfgO::WK, CfgO::template U<NT>, Epi::RESID>(
+        (p.n_groups + CfgO::WG_ROWS - 1) / CfgO::WG_ROWS, s, p);
 
   // RMSNorm -> gate/up -> SwiGLU
   p = base;
@@ -618,8 +759,8 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.ss_in = ss; p.hb_out = hb;
   if (q4) launch_q4_linear(Q4Linear::GATE_UP, p, L.q_wgu, L.s_wgu, d.H, s);
   else
-    gemv_kernel<NT, CfgGU::WG_ROWS, CfgGU::WK, CfgGU::template U<NT>, Epi::SWIGLU>
-        <<<(p.n_groups + CfgGU::WG_ROWS - 1) / CfgGU::WG_ROWS, CfgGU::THREADS, 0, s>>>(p);
+    launch_gemv<NT, CfgGU::WG_ROWS, CfgGU::WK, CfgGU::template U<NT>, Epi::SWIGLU>(
+        (p.n_groups + CfgGU::WG_ROWS - 1) / CfgGU::WG_ROWS, s, p);
 
   // down projection + residual; next input is the next layer's (or final) norm
   p = base;
@@ -630,7 +771,7 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.cnt = reinterpret_cast<int32_t*>(ws + pl.cnt);   // the last split finishes the residual
   if (q4) launch_q4_linear(Q4Linear::DOWN, p, L.q_wdown, L.s_wdown, d.F, s);
   else
-    gemv_kernel<NT, 1, CfgDown::WK, CfgDown::template U<NT>, Epi::PARTIAL><<<p.n_groups * kDownSplit, CfgDown::THREADS, 0, s>>>(p);
+    launch_gemv<NT, 1, CfgDown::WK, CfgDown::template U<NT>, Epi::PARTIAL>(p.n_groups * kDownSplit, s, p);
 }
 
 template <int NT>
@@ -659,7 +800,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
   float* lm_part = reinterpret_cast<float*>(ws + pl.lm_part);
   p.lm_part = lm_part;
   int wgs = (p.n_groups + CfgLM::WG_ROWS - 1) / CfgLM::WG_ROWS;
-  gemv_kernel<NT, CfgLM::WG_ROWS, CfgLM::WK, CfgLM::template U<NT>, Epi::LMHEAD><<<wgs, CfgLM::THREADS, 0, s>>>(p);
+  launch_gemv<NT, CfgLM::WG_ROWS, CfgLM::WK, CfgLM::template U<NT>, Epi::LMHEAD>(wgs, s, p);
   lm_reduce_kernel<<<a.rows, 256, 0, s>>>(lm_part, wgs, a.rows, a.argmax, a.lse, a.c->d_len, err, a.gate);
   return hipGetLastError();
 }

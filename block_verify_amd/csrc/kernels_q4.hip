@@ -102,6 +102,9 @@ struct Q4Params {
 
 template <int WG_ROWS, int WK, int U, Epi E>
 __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p, Q4Params q) {
+  EpiPre pre;
+  // the cache position is requested together with the gate
+  if constexpr (E == Epi::QKV) pre.pos0 = *p.d_len;
   if (p.gate && *p.gate == 0) return;
   constexpr int NW = WG_ROWS * WK;
   constexpr int NC = 8;
@@ -118,7 +121,9 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   const int sidx = (E == Epi::PARTIAL) ? (int)(blockIdx.x % nsplit) : 0;
   const int g = (E == Epi::PARTIAL) ? (int)(blockIdx.x / nsplit) : (int)(blockIdx.x * WG_ROWS + rg);
   const int M = p.rows;
-  const int b0s = (int)(((long)sidx * q.NB) / nsplit), b1s = (int)(((long)(sidx + 1) * q.NB) / nsplit);
+  // 32-bit unsigned arithmetic (small terms; a 64-bit division is long)
+  const int b0s = (int)((unsigned)sidx * (unsigned)q.NB / (unsigned)nsplit);
+  const int b1s = (int)((unsigned)(sidx + 1) * (unsigned)q.NB / (unsigned)nsplit);
   const int KR = (b1s - b0s) * 128;
   _Float16* xs = reinterpret_cast<_Float16*>(q4_lds);                       // [M][KR]
   float* x8 = reinterpret_cast<float*>(q4_lds + (size_t)M * KR * 2);       // [M][KR / 8] sums of 8
@@ -126,12 +131,14 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   constexpr bool kNorm = (E == Epi::QKV || E == Epi::SWIGLU);
   float ssv[RPW][4];
   if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
+  // the epilogue wave's residual operands, likewise
+  if (ks == 0) epi_prefetch_x<E>(p, lane, g, M, pre);
 
   // this wave's first batch of codes is requested before the activations are
   // staged: the weights do not depend on them
   const bool active = g < p.n_groups;
   const int nb = b1s - b0s;
-  const int kb0 = b0s + (int)(((long)ks * nb) / WK), kb1 = b0s + (int)(((long)(ks + 1) * nb) / WK);
+  const int kb0 = b0s + (int)((unsigned)ks * (unsigned)nb / WK), kb1 = b0s + (int)((unsigned)(ks + 1) * (unsigned)nb / WK);
   const u32x4_t* cp = q.codes + (size_t)(active ? g : 0) * q.NB * 64 + lane;
   const uint32_t* sp = q.scales + (size_t)(active ? g : 0) * q.NB * 32 + (lane >> 5) * 16 + (lane & 15);
   u32x4_t cv[U];
@@ -145,6 +152,8 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
       }
   };
   if (active) issue(kb0);
+  // the RoPE rotations need the cache position, so they follow the code requests
+  if (ks == 0) epi_prefetch_rope<E>(p, lane, g, M, pre);
 
   // stage the activation rows of this split as fp16 (x = hi + lo of the
   // tiles) with the float sum of every 8 staged values
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
     fin[rr][i][m] = v;
   }
   __syncthreads();
-  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, w, lane, rg, ks, g, sidx, M);
+  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, pre, w, lane, rg, ks, g, sidx, M);
 }
 
 // Launch shapes (row groups per workgroup, k-split waves, code blocks in

@@ -217,7 +217,7 @@ class Cache:
         here is transposed back (a strided view, no copy).
         """
         sh = self.shape
-        lp = (self.max_len + 63) // 64 * 64
+        lp = (self.max_len + 127) // 128 * 128
         per = sh.n_kv_heads * lp * sh.head_dim
         raw = self.mem[: 2 * sh.n_layers * 2 * per].view(torch.int16).view(sh.n_layers, 2, per)
         k = raw[:, 0].view(sh.n_layers, sh.n_kv_heads, lp, sh.head_dim)[:, :, : self.max_len]

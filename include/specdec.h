@@ -124,7 +124,7 @@ void specdec_model_destroy(specdec_model* m);
 /* ------------------------------------------------------------------ cache */
 
 /* Bytes of a KV cache of `max_len` positions (at most 65536).  With
- * lp = max_len rounded up to 64, each layer holds bf16 K as
+ * lp = max_len rounded up to 128, each layer holds bf16 K as
  * [kv head][lp][head_dim] followed by bf16 V transposed as
  * [kv head][head_dim][lp]; then the fp32 RoPE table [max_len][head_dim/2]
  * of (cos, sin). */
