@@ -101,7 +101,7 @@ WsPlan ws_plan(const Dims& d, int max_rows, int max_len) {
   p.hb = take((size_t)kMaxNT * d.F * 32);
   p.att_o = take((size_t)d.nkv * p.max_chunks * (R * 8) * d.hd * 4);
   p.att_ml = take((size_t)d.nkv * p.max_chunks * (R * 8) * 2 * 4);
-  p.part = take((size_t)kMaxSplit * kMaxRows * d.H * 4);
+  p.part = take((size_t)kMaxSplit * kMaxRows * d.H * 8);   // (value, tag) pairs
   p.lm_part = take(R * p.lm_wgs * 3 * 4);
   p.toks = take(R * 4 * 2);
   p.logits = take(R * (size_t)d.V * 4);
@@ -333,7 +333,9 @@ int specdec_workspace_bytes(const specdec_model_desc* desc, int32_t max_rows, in
 
 int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream) {
   if (!d_ws || ws_bytes < (size_t)kWsHeader) return SPECDEC_EINVAL;
-  return hip_status(hipMemsetAsync(d_ws, 0, kWsHeader, (hipStream_t)stream));
+  // all of it: the error word, the split-K sequence numbers and the tags of
+  // the split-K partials start at zero (a tag is never zero after a launch)
+  return hip_status(hipMemsetAsync(d_ws, 0, ws_bytes, (hipStream_t)stream));
 }
 
 static int check_fwd(const specdec_model* m, const specdec_cache* c, int32_t rows, size_t ws_bytes, WsPlan* plan) {

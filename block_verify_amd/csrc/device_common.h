@@ -127,6 +127,7 @@ enum : int32_t {
   kErrNonFinite = 4,    // non-finite logits
   kErrTable = 8,        // draft table / noise read past its end
   kErrOutput = 16,      // committed-token buffer full
+  kErrSync = 32,        // a split-K hand-off waited past its bound
 };
 
 __device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {

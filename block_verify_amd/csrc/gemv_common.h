@@ -59,9 +59,9 @@ struct GemvParams {
   float* logits;
   int V;
   float* lm_part;        // [rows][gridDim.x][3]
-  // PARTIAL (split-K): [nsplit][kMaxRows][H] partial outputs and one
-  // arrival counter per row group (zero between launches); the last split
-  // to arrive sums the partials and runs the RESID epilogue
+  // PARTIAL (split-K): [nsplit][kMaxRows][H] (value, tag) pairs of the
+  // splits' partial outputs and one launch sequence number per row group;
+  // the last split sums the others' values and runs the RESID epilogue
   float* part;
   int nsplit;
   int32_t* cnt;
@@ -83,6 +83,18 @@ __device__ __forceinline__ agent_rsrc_t agent_rsrc(const void* base) {
 __device__ __forceinline__ float load_agent(agent_rsrc_t r, size_t index) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(index * 4), 0, kCpolSc1));
 }
+// 64-bit (value, tag) words: one store and one load each, so a reader sees
+// both halves of one write (naturally aligned 8-byte accesses).
+__device__ __forceinline__ void store_agent_pair(float* p, float v, uint32_t tag) {
+  const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t load_agent_pair(agent_rsrc_t r, size_t index) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (uint32_t)(index * 8), 0, kCpolSc1);
+}
+constexpr int kHandoffSpins = 1 << 18;   // bound of a finisher's wait for one value
+
 // Wait until this wave's outstanding vector memory operations completed.
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -101,6 +113,7 @@ struct EpiPre {
   float gain;
   float2 cs[kPreR];
   int pos0;
+  uint32_t seq;   // PARTIAL: the row group's launch sequence number before this launch
 };
 
 // RESID / PARTIAL: x[m][16 g + i] for idx = 16 m + i, and gain_next[16 g + i]
@@ -108,6 +121,9 @@ struct EpiPre {
 // whole launch, so reading them before the product is safe.
 template <Epi E>
 __device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, int g, int M, EpiPre& pre) {
+  if constexpr (E == Epi::PARTIAL) {
+    if (g < p.n_groups) pre.seq = (uint32_t)p.cnt[g];
+  }
   if constexpr (E == Epi::RESID || E == Epi::PARTIAL) {
     if (g < p.n_groups) {
       pre.gain = p.gain_next[16 * g + (lane & 15)];
@@ -318,36 +334,58 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
       btile_put(p.hb_out, KBo, m, 8 * g + i, h);
     }
   } else if constexpr (E == Epi::PARTIAL) {
-    // this split's 16 outputs x M rows
-    float* dst = p.part + (size_t)sidx * kMaxRows * p.H;
-    for (int idx = lane; idx < 16 * M; idx += 64) {
-      const int i = idx & 15, m = idx >> 4;
-      store_agent(dst + (size_t)m * p.H + 16 * g + i, f[i][m]);
+    // Split-K hand-off.  Splits 0 .. nsplit-2 store their 16 outputs x M rows
+    // as (value, tag) pairs and are done; split nsplit-1 finishes the row
+    // group.  The tag is the row group's launch sequence number (seq + 1,
+    // seq read from the workspace at launch), so the finisher's loads are
+    // their own readiness test: it takes a value once its tag matches (a
+    // bounded wait; the producers of a row group come first in launch order
+    // and wait on nothing).  The splits are summed in split order and the
+    // finisher stores the new sequence number for the next launch.
+    const uint32_t tag = pre.seq + 1u;
+    const int last = p.nsplit - 1;
+    if (sidx != last) {
+      float* dst = p.part + (size_t)sidx * kMaxRows * p.H * 2;
+      for (int idx = lane; idx < 16 * M; idx += 64) {
+        const int i = idx & 15, m = idx >> 4;
+        store_agent_pair(dst + ((size_t)m * p.H + 16 * g + i) * 2, f[i][m], tag);
+      }
+      return;
     }
-    // the last split of this row group to arrive sums the splits in split
-    // order and finishes the residual; it resets the counter for the next use
-    wait_vmem();
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != p.nsplit - 1) return;
     const agent_rsrc_t pr = agent_rsrc(p.part);
-    for (int idx = lane; idx < 16 * M; idx += 64) {
-      const int i = idx & 15, m = idx >> 4;
-      float v[kMaxSplit];
-#pragma unroll
-      for (int s2 = 0; s2 < kMaxSplit; ++s2)
-        if (s2 < p.nsplit && s2 != sidx) v[s2] = load_agent(pr, ((size_t)s2 * kMaxRows + m) * p.H + 16 * g + i);
-      float y = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < kMaxSplit; ++s2)
-        if (s2 < p.nsplit) y += (s2 == sidx) ? f[i][m] : v[s2];
-      f[i][m] = y;
+    bool late = false;
+    // a value once its tag matches (reloading while it does not)
+    auto take = [&](u32x2_t w, size_t at) -> float {
+      for (int spin = 0; w.y != tag; ++spin) {
+        if (spin == kHandoffSpins) { late = true; break; }
+        __builtin_amdgcn_s_sleep(1);
+        w = load_agent_pair(pr, at);
+      }
+      return __uint_as_float(w.x);
+    };
+    // two lane-strided entries at a time (all of them when M <= 8), each
+    // split's pair of loads in flight together
+    for (int idxa = lane; idxa < 16 * M; idxa += 128) {
+      const int idxb = idxa + 64;
+      const bool vb = idxb < 16 * M;
+      const int ib = vb ? idxb : idxa;
+      float ya = 0.f, yb = 0.f;
+      for (int s2 = 0; s2 < last; ++s2) {
+        const size_t base = (size_t)s2 * kMaxRows * p.H + 16 * g;
+        const size_t ata = base + (size_t)(idxa >> 4) * p.H + (idxa & 15);
+        const size_t atb = base + (size_t)(ib >> 4) * p.H + (ib & 15);
+        const u32x2_t wa = load_agent_pair(pr, ata), wb = load_agent_pair(pr, atb);
+        ya += take(wa, ata);
+        yb += take(wb, atb);
+      }
+      f[idxa & 15][idxa >> 4] = ya + f[idxa & 15][idxa >> 4];
+      if (vb) f[idxb & 15][idxb >> 4] = yb + f[idxb & 15][idxb >> 4];
     }
+    if (late) raise_error(p.err, kErrSync);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     resid_epilogue<NC>(p, f, pre, lane, g, M);
-    if (lane == 0) __hip_atomic_store(p.cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) p.cnt[g] = (int32_t)tag;
   } else {  // RESID
     resid_epilogue<NC>(p, f, pre, lane, g, M);
   }

@@ -86,7 +86,7 @@ namespace sd {
 constexpr int kAttnChunk = SD_ATTN_CHUNK;   // keys per attention chunk (64 or 128)
 constexpr int kKvPad = 128;                 // cache positions are padded to a multiple of this
 static_assert(kKvPad % kAttnChunk == 0, "chunks tile the padded cache");
-constexpr int kWsHeader = 65536;   // error word + split-K arrival counters (zeroed once)
+constexpr int kWsHeader = 65536;   // error word + split-K launch sequence numbers
 constexpr int kMaxSplit = 8;
 // K splits of the down projection: bf16 (tuned on the verify forward) and
 // 4-bit (bounded by the activations the 4-bit kernel stages in LDS).

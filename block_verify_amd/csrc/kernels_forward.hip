@@ -245,6 +245,69 @@ __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, cons
   }
 }
 
+// The same stream for a workgroup of R row groups that share the k-split:
+// the R waves on one k-range load the batch's activation tiles once between
+// them (wave rg takes tiles rg, rg + R, ...) and exchange them through LDS,
+// so each wave requests U / R activation tiles per batch instead of U.  The
+// products and their order are those of mfma_stream.  Every wave of the
+// workgroup runs the same number of batches (nmax is the longest k-range),
+// also when its row group is past the matrix (active == false: it still
+// loads its share of the activation tiles).
+template <int NT, int U, int R, typename Issued>
+__device__ __forceinline__ void mfma_stream_shared(const bf16x8_t* __restrict__ A, bool active,
+                                                   const bf16x8_t* __restrict__ B, int KB, int kb0, int kb1, int nmax,
+                                                   int rg, int lane, f32x4_t (&acc)[NT], i32x4_t (*bsh)[NT][64],
+                                                   Issued&& issued) {
+  static_assert(U % R == 0, "each wave loads an equal share of a batch");
+  constexpr int US = U / R;
+  const i32x4_t* a = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
+  const i32x4_t* b = reinterpret_cast<const i32x4_t*>(B) + (size_t)kb0 * 64 + lane;
+  const size_t tstride = (size_t)KB * 64;
+  const int n = kb1 - kb0;   // equal for the R waves of this k-range
+  for (int i = 0; i < nmax; i += U) {
+    if (i > 0) __syncthreads();   // the previous batch's tiles have been read
+    // this wave's share of the activation tiles first, then its weight tiles
+    i32x4_t bs[US][NT];
+    if (n > 0)
+#pragma unroll
+      for (int j = 0; j < US; ++j) {
+        const int u = rg + R * j, kb = i + u < n ? i + u : n - 1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bs[j][t] = b[t * tstride + (size_t)kb * 64];
+      }
+    i32x4_t av[U];
+    if (active && n > 0)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kb = i + u < n ? i + u : n - 1;
+        av[u] = __builtin_nontemporal_load(a + (size_t)kb * 64);
+      }
+    if (i == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      issued();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (n > 0)
+#pragma unroll
+      for (int j = 0; j < US; ++j)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bsh[rg + R * j][t][lane] = bs[j][t];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (active)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i + u < n)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
+                                                            __builtin_bit_cast(bf16x8_t, bsh[u][t][lane]), acc[t], 0,
+                                                            0, 0);
+  }
+  if (nmax <= 0) issued();
+}
+
 // The fields the weight stream needs come first as plain arguments, which
 // the launch preloads into scalar registers; the rest of GemvParams is read
 // from the argument block where it is used.
@@ -262,6 +325,10 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   constexpr int NW = WG_ROWS * WK;
   constexpr int NC = NT * 8;        // activation rows covered
   constexpr int RPW = (kMaxRows + NW - 1) / NW;
+  // row groups of a workgroup share their activation tiles through LDS when
+  // the batch fits (the arithmetic is the same either way)
+  constexpr bool kShareB = WG_ROWS > 1 && U % WG_ROWS == 0 && WK * U * NT * 1024 <= 48 * 1024;
+  __shared__ i32x4_t bsh[kShareB ? WK : 1][kShareB ? U : 1][NT][64];
   __shared__ float red[NW][16][NC + 1];
   __shared__ float fin[WG_ROWS][16][NC + 1];
   __shared__ float rsc[kMaxRows];
@@ -293,13 +360,18 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (g < n_groups) {
-    // 32-bit unsigned arithmetic: every term is small (split index < 8,
-    // k-blocks < 2^16), and a 64-bit division costs hundreds of instructions
-    const unsigned uk = (unsigned)KB, un = (unsigned)nsplit;
-    const int s0 = (int)((unsigned)sidx * uk / un), s1 = (int)((unsigned)(sidx + 1) * uk / un);
-    const unsigned span = (unsigned)(s1 - s0);
-    const int kb0 = s0 + (int)((unsigned)ks * span / WK), kb1 = s0 + (int)((unsigned)(ks + 1) * span / WK);
+  // 32-bit unsigned arithmetic: every term is small (split index < 8,
+  // k-blocks < 2^16), and a 64-bit division costs hundreds of instructions
+  const unsigned uk = (unsigned)KB, un = (unsigned)nsplit;
+  const int s0 = (int)((unsigned)sidx * uk / un), s1 = (int)((unsigned)(sidx + 1) * uk / un);
+  const unsigned span = (unsigned)(s1 - s0);
+  const int kb0 = s0 + (int)((unsigned)ks * span / WK), kb1 = s0 + (int)((unsigned)(ks + 1) * span / WK);
+  if constexpr (kShareB) {
+    const int nmax = (int)((span + WK - 1) / WK);
+    const int gg = g < n_groups ? g : 0;
+    mfma_stream_shared<NT, U, WG_ROWS>(A + (size_t)gg * KB * 64, g < n_groups, B, KB, kb0, kb1, nmax, rg, lane, acc,
+                                       bsh[ks], prefetch);
+  } else if (g < n_groups) {
     mfma_stream<NT, U>(A + (size_t)g * KB * 64, B, KB, kb0, kb1, lane, acc, prefetch);
   } else {
     prefetch();

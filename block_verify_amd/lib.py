@@ -18,7 +18,7 @@ from .shapes import ModelShape
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecdec.so")
 
 OK, EINVAL, ECAPACITY, ESHAPE, EHIP, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-DERR_CAPACITY, DERR_TRIM, DERR_NONFINITE, DERR_TABLE, DERR_OUTPUT = 1, 2, 4, 8, 16
+DERR_CAPACITY, DERR_TRIM, DERR_NONFINITE, DERR_TABLE, DERR_OUTPUT, DERR_SYNC = 1, 2, 4, 8, 16, 32
 W_BF16, W_Q4G64 = 0, 1
 GREEDY, STOCHASTIC = 0, 1
 SCHEDULE_A, SCHEDULE_B = 0, 1

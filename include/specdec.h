@@ -62,7 +62,8 @@ enum {
   SPECDEC_DERR_TRIM = 2,       /* trim above the current length (length unchanged) */
   SPECDEC_DERR_NONFINITE = 4,  /* non-finite logits */
   SPECDEC_DERR_TABLE = 8,      /* draft table or noise read past its end */
-  SPECDEC_DERR_OUTPUT = 16     /* committed-token buffer full (tokens dropped) */
+  SPECDEC_DERR_OUTPUT = 16,    /* committed-token buffer full (tokens dropped) */
+  SPECDEC_DERR_SYNC = 32       /* a split-K hand-off inside a forward waited past its bound */
 };
 
 enum { SPECDEC_W_BF16 = 0, SPECDEC_W_Q4G64 = 1 };
@@ -149,10 +150,11 @@ int specdec_kv_trim(specdec_cache* c, int32_t new_len, int32_t* d_err, void* str
  * sticky device error word at offset 0 (int32). */
 int specdec_workspace_bytes(const specdec_model_desc* desc, int32_t max_rows, int32_t max_len, size_t* bytes);
 
-/* Zero the workspace header on `stream`: the error word and the arrival
- * counters the split-K down projection uses (each forward leaves them at
- * zero again).  Required once before the first forward.  Forwards that share
- * one workspace must not overlap (enqueue them on one stream). */
+/* Zero the whole workspace (ws_bytes) on `stream`: the error word, the
+ * launch sequence numbers of the split-K row groups and the tags of the
+ * split-K partials.  Required once before the first forward; later forwards
+ * keep these consistent themselves.  Forwards that share one workspace must
+ * not overlap (enqueue them on one stream). */
 int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------- forwards */
