@@ -246,8 +246,9 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
       if (gg < p.n_groups) p.logits[(size_t)m * p.V + 16 * gg + i] = v;
     }
     __syncthreads();
-    if (w == 0) {
-      for (int m = 0; m < M; ++m) {
+    {
+      // rows spread over the waves; each row's order is fixed by its lanes
+      for (int m = w; m < M; m += (int)(blockDim.x >> 6)) {
         // lane owns entries lane and lane + 64 of the workgroup's 16 * WG_ROWS
         float best = -INFINITY;
         int bidx = 0x7fffffff;

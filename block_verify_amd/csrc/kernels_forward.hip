@@ -706,53 +706,70 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
 
 // ---------------------------------------------------------------------------
 // Final reduction of the LM-head partials: argmax (lowest index on ties) and
-// log-sum-exp per row; then the cache length advances by the row count.
+// log-sum-exp per row; then the cache length advances by the row count.  One
+// 1024-thread workgroup per row: thread t takes partials t + 1024 j (all of
+// them requested before any is used), then a wave reduction and the waves in
+// order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void lm_reduce_kernel(const float* __restrict__ part, int n_wg, int rows,
-                                                        int32_t* __restrict__ argmax_out, float* __restrict__ lse_out,
-                                                        int32_t* __restrict__ d_len, int32_t* err, const int32_t* gate) {
+constexpr int kLmrThreads = 1024, kLmrWaves = kLmrThreads / 64, kLmrPer = 4;
+
+__global__ __launch_bounds__(kLmrThreads) void lm_reduce_kernel(const float* __restrict__ part, int n_wg, int rows,
+                                                                int32_t* __restrict__ argmax_out,
+                                                                float* __restrict__ lse_out,
+                                                                int32_t* __restrict__ d_len, int32_t* err,
+                                                                const int32_t* gate) {
   if (gate && *gate == 0) return;
   const int m = blockIdx.x;
   const float* pp = part + (size_t)m * n_wg * 3;
-  __shared__ float sb[256];
-  __shared__ int si[256];
-  __shared__ float ss[256];
-  float best = -INFINITY;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ float sb[kLmrWaves], ss[kLmrWaves];
+  __shared__ int si[kLmrWaves];
+  float best = -INFINITY, se = 0.f;
   int bidx = 0x7fffffff;
   bool bad = false;
-  for (int i = threadIdx.x; i < n_wg; i += 256) {
-    float v = pp[i * 3];
-    int ix = __float_as_int(pp[i * 3 + 1]);
-    if (!(fabsf(v) <= 3.0e38f)) bad = true;
-    if (v > best || (v == best && ix < bidx)) { best = v; bidx = ix; }
-  }
-  sb[threadIdx.x] = best;
-  si[threadIdx.x] = bidx;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      float ob = sb[threadIdx.x + s];
-      int oi = si[threadIdx.x + s];
-      if (ob > sb[threadIdx.x] || (ob == sb[threadIdx.x] && oi < si[threadIdx.x])) {
-        sb[threadIdx.x] = ob;
-        si[threadIdx.x] = oi;
-      }
+  float mv[kLmrPer], sv[kLmrPer];
+  int iv[kLmrPer];
+  // pass 1: this thread's partials (a batch of kLmrPer at a time)
+  for (int i0 = 0; i0 < n_wg; i0 += kLmrThreads * kLmrPer) {
+#pragma unroll
+    for (int j = 0; j < kLmrPer; ++j) {
+      int i = i0 + (int)threadIdx.x + kLmrThreads * j;
+      const bool ok = i < n_wg;
+      if (!ok) i = 0;   // a valid slot, not used
+      mv[j] = pp[i * 3];
+      iv[j] = __float_as_int(pp[i * 3 + 1]);
+      sv[j] = pp[i * 3 + 2];
+      if (!ok) { mv[j] = -INFINITY; iv[j] = 0x7fffffff; sv[j] = 0.f; }
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLmrPer; ++j) {
+      if (i0 + (int)threadIdx.x + kLmrThreads * j < n_wg && !(fabsf(mv[j]) <= 3.0e38f)) bad = true;
+      if (mv[j] > best || (mv[j] == best && iv[j] < bidx)) { best = mv[j]; bidx = iv[j]; }
+    }
   }
-  const float gmax = sb[0];
-  float se = 0.f;
-  for (int i = threadIdx.x; i < n_wg; i += 256) se += pp[i * 3 + 2] * expf(pp[i * 3] - gmax);
-  ss[threadIdx.x] = se;
+  warp_argmax(best, bidx);
+  if (lane == 0) { sb[w] = best; si[w] = bidx; }
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) ss[threadIdx.x] += ss[threadIdx.x + s];
-    __syncthreads();
+  float gmax = sb[0];
+  int gidx = si[0];
+  for (int v = 1; v < kLmrWaves; ++v)
+    if (sb[v] > gmax || (sb[v] == gmax && si[v] < gidx)) { gmax = sb[v]; gidx = si[v]; }
+  // pass 2: sum of exp relative to the row max (in registers when n_wg fits one batch)
+  if (n_wg <= kLmrThreads * kLmrPer) {
+#pragma unroll
+    for (int j = 0; j < kLmrPer; ++j) se += sv[j] * expf(mv[j] - gmax);
+  } else {
+    for (int i = threadIdx.x; i < n_wg; i += kLmrThreads) se += pp[i * 3 + 2] * expf(pp[i * 3] - gmax);
   }
+  se = warp_sum(se);
+  if (lane == 0) ss[w] = se;
+  __syncthreads();
   if (bad) raise_error(err, kErrNonFinite);
   if (threadIdx.x == 0) {
-    if (argmax_out) argmax_out[m] = si[0];
-    if (lse_out) lse_out[m] = gmax + logf(ss[0]);
+    float tot = 0.f;
+    for (int v = 0; v < kLmrWaves; ++v) tot += ss[v];
+    if (argmax_out) argmax_out[m] = gidx;
+    if (lse_out) lse_out[m] = gmax + logf(tot);
     if (m == 0) *d_len += rows;
   }
 }
@@ -873,7 +890,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
   p.lm_part = lm_part;
   int wgs = (p.n_groups + CfgLM::WG_ROWS - 1) / CfgLM::WG_ROWS;
   launch_gemv<NT, CfgLM::WG_ROWS, CfgLM::WK, CfgLM::template U<NT>, Epi::LMHEAD>(wgs, s, p);
-  lm_reduce_kernel<<<a.rows, 256, 0, s>>>(lm_part, wgs, a.rows, a.argmax, a.lse, a.c->d_len, err, a.gate);
+  lm_reduce_kernel<<<a.rows, kLmrThreads, 0, s>>>(lm_part, wgs, a.rows, a.argmax, a.lse, a.c->d_len, err, a.gate);
   return hipGetLastError();
 }
 
