@@ -106,12 +106,15 @@ __device__ __forceinline__ void wait_vmem() {
 // position of the query/key groups (QKV).  The epilogue wave requests them
 // while its weight tiles are in flight, so the epilogue waits on no load of
 // its own.  Lane l holds entry idx = l + 64 j of the epilogue's loops.
-constexpr int kPreX = 16 * kMaxRows / 64;   // residual values per lane
-constexpr int kPreR = 8 * kMaxRows / 64;    // RoPE pairs per lane
+// Sized for the NC activation rows a launch shape covers (NC = 8 per
+// operand tile), so a one-tile pass holds a few registers only.
+template <int NC>
 struct EpiPre {
-  float xv[kPreX];
+  static constexpr int kX = (16 * NC + 63) / 64;   // residual values per lane
+  static constexpr int kR = (8 * NC + 63) / 64;    // RoPE pairs per lane
+  float xv[kX];
   float gain;
-  float2 cs[kPreR];
+  float2 cs[kR];
   int pos0;
   uint32_t seq;   // PARTIAL: the row group's launch sequence number before this launch
 };
@@ -119,8 +122,8 @@ struct EpiPre {
 // RESID / PARTIAL: x[m][16 g + i] for idx = 16 m + i, and gain_next[16 g + i]
 // (i = lane % 16 for every j).  Row group g owns these x entries for the
 // whole launch, so reading them before the product is safe.
-template <Epi E>
-__device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, int g, int M, EpiPre& pre) {
+template <Epi E, int NC>
+__device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, int g, int M, EpiPre<NC>& pre) {
   if constexpr (E == Epi::PARTIAL) {
     if (g < p.n_groups) pre.seq = (uint32_t)p.cnt[g];
   }
@@ -128,7 +131,7 @@ __device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, in
     if (g < p.n_groups) {
       pre.gain = p.gain_next[16 * g + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < kPreX; ++j) {
+      for (int j = 0; j < EpiPre<NC>::kX; ++j) {
         const int idx = lane + 64 * j;
         if (idx < 16 * M) pre.xv[j] = p.x[(size_t)(idx >> 4) * p.H + 16 * g + (idx & 15)];
       }
@@ -138,14 +141,14 @@ __device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, in
 
 // QKV: the rotation pairs of this query/key group at positions pos0 + m
 // (idx = 8 m + i, i = lane % 8); pos0 is the cache length read at launch.
-template <Epi E>
-__device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane, int g, int M, EpiPre& pre) {
+template <Epi E, int NC>
+__device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane, int g, int M, EpiPre<NC>& pre) {
   if constexpr (E == Epi::QKV) {
     const int qg = p.nq * p.hd / 16, kg = p.nkv * p.hd / 16;
     if (g < qg + kg) {
       const int sub = (g >= qg ? g - qg : g) % (p.hd / 16), half = p.hd / 2;
 #pragma unroll
-      for (int j = 0; j < kPreR; ++j) {
+      for (int j = 0; j < EpiPre<NC>::kR; ++j) {
         const int idx = lane + 64 * j, m = idx >> 3, pos = pre.pos0 + m;
         if (m < M && pos < p.max_len) pre.cs[j] = p.rope[(size_t)pos * half + 8 * sub + (idx & 7)];
       }
@@ -157,11 +160,11 @@ __device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane,
 // the next norm's operand tiles of x * gain and the group's sum of squares.
 // f[i][m] holds y on entry and the new x on exit; pre holds x and the gains.
 template <int NC>
-__device__ __forceinline__ void resid_epilogue(const GemvParams& p, float (*f)[NC + 1], const EpiPre& pre, int lane,
+__device__ __forceinline__ void resid_epilogue(const GemvParams& p, float (*f)[NC + 1], const EpiPre<NC>& pre, int lane,
                                                int g, int M) {
   const int KBo = p.H >> 5, NP = p.H >> 4;
 #pragma unroll
-  for (int j = 0; j < kPreX; ++j) {
+  for (int j = 0; j < EpiPre<NC>::kX; ++j) {
     const int idx = lane + 64 * j;
     if (idx < 16 * M) {
       const int i = idx & 15, m = idx >> 4, n = 16 * g + i;
@@ -233,7 +236,7 @@ __device__ __forceinline__ void norm_finish(const GemvParams& p, int w, int lane
 // whole workgroup; the others on wave (rg, ks == 0) of each row group.
 template <int WG_ROWS, int NC, Epi E>
 __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[16][NC + 1], const float* rsc,
-                                              const EpiPre& pre, int w, int lane, int rg, int ks, int g, int sidx,
+                                              const EpiPre<NC>& pre, int w, int lane, int rg, int ks, int g, int sidx,
                                               int M) {
   (void)w;
   if constexpr (E == Epi::LMHEAD) {
@@ -290,7 +293,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
       const int gg = is_k ? g - qg : g;
       const int head = gg / per_head, sub = gg % per_head;
 #pragma unroll
-      for (int j = 0; j < kPreR; ++j) {
+      for (int j = 0; j < EpiPre<NC>::kR; ++j) {
         const int idx = lane + 64 * j, i = idx & 7, m = idx >> 3;
         const int pos = pos0 + m;
         if (m >= M || pos >= p.max_len) continue;

@@ -185,12 +185,52 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
+// One batch of exactly R tiles: straight-line loads (a guarded load into a
+// register array makes the compiler wait on it), then `issued` once when it
+// is the wave's first batch, then the products in k order.
+template <int NT, int R, typename Issued>
+__device__ __forceinline__ void mfma_batch(const i32x4_t* a, const i32x4_t* b, size_t tstride, int i,
+                                           f32x4_t (&acc)[NT], bool first, Issued& issued) {
+  i32x4_t av[R];
+  i32x4_t bv[R][NT];
+#pragma unroll
+  for (int u = 0; u < R; ++u) av[u] = __builtin_nontemporal_load(a + (size_t)(i + u) * 64);
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bv[u][t] = b[t * tstride + (size_t)(i + u) * 64];
+  if (first) {
+    // the scheduling barriers keep the weight requests ahead of whatever
+    // `issued` requests (the compiler would otherwise hoist those small
+    // loads, and the waits they carry, above the weight stream)
+    __builtin_amdgcn_sched_barrier(0);
+    issued();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
+                                                      __builtin_bit_cast(bf16x8_t, bv[u][t]), acc[t], 0, 0, 0);
+}
+
+// The last r < U tiles of a wave's range, as a batch of exactly r.
+template <int NT, int U, typename Issued>
+__device__ __forceinline__ void mfma_tail(const i32x4_t* a, const i32x4_t* b, size_t tstride, int i, int r,
+                                          f32x4_t (&acc)[NT], bool first, Issued& issued) {
+  if constexpr (U > 1) {
+    if (r == U - 1) mfma_batch<NT, (U > 1 ? U - 1 : 1)>(a, b, tstride, i, acc, first, issued);
+    else mfma_tail<NT, (U > 1 ? U - 1 : 1)>(a, b, tstride, i, r, acc, first, issued);
+  }
+}
+
 // Streams the weight tiles of one row group over k-blocks [kb0, kb1) through
-// MFMA.  Tiles travel as 32-bit integer vectors (bit-cast to bf16 only at the
-// MFMA) so the guarded unroll never needs 16-bit lane merges; kb0/kb1 are
-// wave-uniform, so the guards are scalar branches.  `issued` runs once, right
-// after the first batch of loads has been requested (also when the wave has
-// no k-blocks).
+// MFMA, up to U tiles in flight per wave (the activation tiles are
+// L2-resident).  Tiles travel as 32-bit integer vectors (bit-cast to bf16
+// only at the MFMA).  kb0/kb1 are wave-uniform, so every branch here is a
+// scalar one.  `issued` runs once, right after the first batch of loads has
+// been requested (also when the wave has no k-blocks).
 template <int NT, int U, typename Issued>
 __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, const bf16x8_t* __restrict__ B, int KB,
                                             int kb0, int kb1, int lane, f32x4_t (&acc)[NT], Issued&& issued) {
@@ -202,47 +242,9 @@ __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, cons
     issued();
     return;
   }
-  // up to U weight tiles in flight per wave; the activation tiles are
-  // L2-resident.  The loads of a batch are unconditional (slots past the
-  // wave's last k-block re-read it, and their products are skipped): guarded
-  // loads into register arrays make the compiler wait on each one.
-  i32x4_t av[U];
-  i32x4_t bv[U][NT];
-  auto load = [&](int i) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = i + u < n ? i + u : n - 1;
-      av[u] = __builtin_nontemporal_load(a + (size_t)kb * 64);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = i + u < n ? i + u : n - 1;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) bv[u][t] = b[t * tstride + (size_t)kb * 64];
-    }
-  };
-  auto multiply = [&](int i) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i + u < n)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
-                                                          __builtin_bit_cast(bf16x8_t, bv[u][t]), acc[t], 0, 0, 0);
-  };
-  // the first batch is peeled so `issued` has one place in the schedule; the
-  // scheduling barrier keeps the weight requests ahead of whatever `issued`
-  // requests (the compiler would otherwise hoist those small loads, and the
-  // waits they carry, above the weight stream)
-  load(0);
-  __builtin_amdgcn_sched_barrier(0);
-  issued();
-  __builtin_amdgcn_sched_barrier(0);
-  multiply(0);
-  for (int i = U; i < n; i += U) {
-    load(i);
-    multiply(i);
-  }
+  int i = 0;
+  for (; i + U <= n; i += U) mfma_batch<NT, U>(a, b, tstride, i, acc, i == 0, issued);
+  if (i < n) mfma_tail<NT, U>(a, b, tstride, i, n - i, acc, i == 0, issued);
 }
 
 // The same stream for a workgroup of R row groups that share the k-split:
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
                                                                  const bf16x8_t* __restrict__ A,
                                                                  const bf16x8_t* __restrict__ B, int KB, int n_groups,
                                                                  int rows, int nsplit_arg, GemvParams p) {
-  EpiPre pre;
+  EpiPre<NT * 8> pre;
   // the gate word (the length stands in for a null gate) and the cache
   // position are requested together, before any branch
   const int gv = *(gate ? gate : d_len);
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   if (gate && gv == 0) return;
   constexpr int NW = WG_ROWS * WK;
   constexpr int NC = NT * 8;        // activation rows covered
-  constexpr int RPW = (kMaxRows + NW - 1) / NW;
+  constexpr int RPW = (NC + NW - 1) / NW;   // norm rows per wave (NC covers every row)
   // row groups of a workgroup share their activation tiles through LDS when
   // the batch fits (the arithmetic is the same either way)
   constexpr bool kShareB = WG_ROWS > 1 && U % WG_ROWS == 0 && WK * U * NT * 1024 <= 48 * 1024;
@@ -352,8 +354,8 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   auto prefetch = [&] {
     if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
     if (ks == 0) {
-      epi_prefetch_x<E>(p, lane, g, M, pre);
-      epi_prefetch_rope<E>(p, lane, g, M, pre);
+      epi_prefetch_x<E, NC>(p, lane, g, M, pre);
+      epi_prefetch_rope<E, NC>(p, lane, g, M, pre);
     }
   };
 

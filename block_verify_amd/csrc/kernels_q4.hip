@@ -102,7 +102,7 @@ struct Q4Params {
 
 template <int WG_ROWS, int WK, int U, Epi E>
 __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p, Q4Params q) {
-  EpiPre pre;
+  EpiPre<8> pre;
   // the cache position is requested together with the gate
   if constexpr (E == Epi::QKV) pre.pos0 = *p.d_len;
   if (p.gate && *p.gate == 0) return;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   float ssv[RPW][4];
   if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
   // the epilogue wave's residual operands, likewise
-  if (ks == 0) epi_prefetch_x<E>(p, lane, g, M, pre);
+  if (ks == 0) epi_prefetch_x<E, NC>(p, lane, g, M, pre);
 
   // this wave's first batch of codes is requested before the activations are
   // staged: the weights do not depend on them
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   };
   if (active) issue(kb0);
   // the RoPE rotations need the cache position, so they follow the code requests
-  if (ks == 0) epi_prefetch_rope<E>(p, lane, g, M, pre);
+  if (ks == 0) epi_prefetch_rope<E, NC>(p, lane, g, M, pre);
 
   // stage the activation rows of this split as fp16 (x = hi + lo of the
   // tiles) with the float sum of every 8 staged values

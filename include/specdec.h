@@ -80,8 +80,8 @@ enum { SPECDEC_DRAFT_TABLE = 0, SPECDEC_DRAFT_MODEL = 1, SPECDEC_DRAFT_NOISY_SEL
 /* Decoder dimensions.  Pre-norm RMSNorm decoder with rotate-half RoPE,
  * grouped-query attention (query head h reads kv head h / (n_q/n_kv)),
  * SwiGLU MLP, untied LM head, no biases.  Supported: hidden, q_dim and ffn
- * multiples of 32 (64 for q4), head_dim 64 or 128, n_q a multiple of n_kv,
- * n_q / n_kv <= 8, vocab a multiple of 16. */
+ * multiples of 32 (64 for q4), hidden <= 4096, head_dim 64 or 128, n_q a
+ * multiple of n_kv, n_q / n_kv <= 8, vocab a multiple of 16 and <= 2^24. */
 typedef struct {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   float rope_theta, rms_eps;

@@ -53,6 +53,9 @@ def test_host_validation_without_gpu():
     bad = b.desc_of(TINY)
     bad.n_q_heads = 3
     assert L.specdec_weights_bytes(ctypes.byref(bad), ctypes.byref(n)) == b.ESHAPE
+    bad = b.desc_of(TINY)
+    bad.hidden = 4096 + 32   # the norm scale reads at most 256 partials of 16 features
+    assert L.specdec_weights_bytes(ctypes.byref(bad), ctypes.byref(n)) == b.ESHAPE
     assert L.specdec_cache_bytes(ctypes.byref(b.desc_of(TINY)), 0, ctypes.byref(n)) == b.EINVAL
     assert L.specdec_decode_step(None, None, None, 1, None, None, None, None, 0, None) == b.EINVAL
     assert L.specdec_round_create(None, None) == b.EINVAL
@@ -83,5 +86,5 @@ def test_q4_blob_size_and_shape_checks():
     bad.ffn = 1056   # a multiple of 32, not of 64
     assert L.specdec_weights_bytes(ctypes.byref(bad), ctypes.byref(n)) == b.ESHAPE
     big = b.desc_of(TINY, b.W_Q4G64)
-    big.hidden = 8192   # four staged rows of 8192 inputs exceed the 4-bit kernel's LDS budget
+    big.hidden = 8192   # past the hidden limit (and the 4-bit kernel's LDS budget)
     assert L.specdec_weights_bytes(ctypes.byref(big), ctypes.byref(n)) == b.ESHAPE
