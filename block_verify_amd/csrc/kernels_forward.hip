@@ -27,7 +27,7 @@ namespace sd {
 // the down projection (kDownSplit).  All are fixed per matrix, never by the row count, so
 // a row's summation order does not depend on how many rows share the pass.
 #ifndef SD_CFG_QKV
-#define SD_CFG_QKV 1, 16, 4
+#define SD_CFG_QKV 1, 8, 6
 #endif
 #ifndef SD_CFG_O
 #define SD_CFG_O 1, 4, 12
@@ -36,10 +36,10 @@ namespace sd {
 #define SD_CFG_GU 1, 8, 6
 #endif
 #ifndef SD_CFG_DOWN
-#define SD_CFG_DOWN 1, 16, 9
+#define SD_CFG_DOWN 1, 8, 18
 #endif
 #ifndef SD_CFG_LM
-#define SD_CFG_LM 4, 1, 12
+#define SD_CFG_LM 2, 2, 12
 #endif
 // U only sets how many tiles a wave keeps in flight (its k-blocks are
 // accumulated in order either way), so multi-tile passes cap it by the
