@@ -103,12 +103,15 @@ struct Q4Params {
 template <int WG_ROWS, int WK, int U, Epi E>
 __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p, Q4Params q) {
   EpiPre<8> pre;
-  // the cache position is requested together with the gate
+  // the gate word (the length stands in for a null gate) and the cache
+  // position are requested together, before any branch
+  const int gv = *(p.gate ? p.gate : p.d_len);
   if constexpr (E == Epi::QKV) pre.pos0 = *p.d_len;
-  if (p.gate && *p.gate == 0) return;
+  if (p.gate && gv == 0) return;
   constexpr int NW = WG_ROWS * WK;
   constexpr int NC = 8;
   constexpr int RPW = (kQ4MaxRows + NW - 1) / NW;
+  constexpr int NT = 64 * NW;
   extern __shared__ __align__(16) unsigned char q4_lds[];
   __shared__ float red[NW][16][NC + 1];
   __shared__ float fin[WG_ROWS][16][NC + 1];
@@ -128,105 +131,144 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   _Float16* xs = reinterpret_cast<_Float16*>(q4_lds);                       // [M][KR]
   float* x8 = reinterpret_cast<float*>(q4_lds + (size_t)M * KR * 2);       // [M][KR / 8] sums of 8
 
+  // The activation rows of this split are staged in LDS as fp16 (x = hi + lo
+  // of the tiles) with the float sum of every 8 staged values.  Their loads
+  // (L2-resident) go out first, SP per thread, then the wave's first batch of
+  // codes (HBM): loads complete in issue order, so writing the activations to
+  // LDS then waits for them only.  The loads are unconditional (an index past
+  // the rows re-reads entry 0): guarded loads into registers are each waited on.
+  const bf16_bits* bt = reinterpret_cast<const bf16_bits*>(p.B);
+  const int k8n = KR >> 3, nstage = M * k8n;
+  // staging pairs in flight per thread: enough for one activation row of
+  // the 7B-shape splits in one pass (the down projection's split is longest)
+  constexpr int SP = (E == Epi::PARTIAL) ? 3 : 1;
+  uint4 hv[SP], lv[SP];
+  auto stage_load = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < SP; ++j) {
+      int idx = base + (int)threadIdx.x + NT * j;
+      if (idx >= nstage) idx = 0;
+      const int m = idx / k8n;
+      int k = b0s * 128 + (idx % k8n) * 8;
+      if (k >= q.K) k = 0;   // the block past K reads a valid tile and stores zeros
+      const size_t bi = btile_index(p.KB, m, k);
+      hv[j] = *reinterpret_cast<const uint4*>(bt + bi);
+      lv[j] = *reinterpret_cast<const uint4*>(bt + bi + 64);
+    }
+  };
+  auto stage_store = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < SP; ++j) {
+      const int idx = base + (int)threadIdx.x + NT * j;
+      if (idx < nstage) {
+        const int m = idx / k8n, k = b0s * 128 + (idx % k8n) * 8;
+        half8_t o;
+        if (k < q.K) {
+          const uint32_t hw[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w}, lw[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[2 * e] = (_Float16)(__uint_as_float(hw[e] << 16) + __uint_as_float(lw[e] << 16));
+            o[2 * e + 1] = (_Float16)(__uint_as_float(hw[e] & 0xFFFF0000u) + __uint_as_float(lw[e] & 0xFFFF0000u));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (_Float16)0.0f;
+        }
+        *reinterpret_cast<half8_t*>(xs + (size_t)m * KR + (k - b0s * 128)) = o;
+        float s8 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s8 += (float)o[e];
+        x8[idx] = s8;
+      }
+    }
+  };
+
   constexpr bool kNorm = (E == Epi::QKV || E == Epi::SWIGLU);
   float ssv[RPW][4];
-  if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
-  // the epilogue wave's residual operands, likewise
-  if (ks == 0) epi_prefetch_x<E, NC>(p, lane, g, M, pre);
-
-  // this wave's first batch of codes is requested before the activations are
-  // staged: the weights do not depend on them
   const bool active = g < p.n_groups;
   const int nb = b1s - b0s;
   const int kb0 = b0s + (int)((unsigned)ks * (unsigned)nb / WK), kb1 = b0s + (int)((unsigned)(ks + 1) * (unsigned)nb / WK);
+  const int n = active ? kb1 - kb0 : 0;
   const u32x4_t* cp = q.codes + (size_t)(active ? g : 0) * q.NB * 64 + lane;
   const uint32_t* sp = q.scales + (size_t)(active ? g : 0) * q.NB * 32 + (lane >> 5) * 16 + (lane & 15);
-  u32x4_t cv[U];
-  uint32_t sv[U];
-  auto issue = [&](int b) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (b + u < kb1) {
-        cv[u] = __builtin_nontemporal_load(cp + (size_t)(b + u) * 64);
-        sv[u] = __builtin_nontemporal_load(sp + (size_t)(b + u) * 32);
-      }
-  };
-  if (active) issue(kb0);
-  // the RoPE rotations need the cache position, so they follow the code requests
-  if (ks == 0) epi_prefetch_rope<E, NC>(p, lane, g, M, pre);
 
-  // stage the activation rows of this split as fp16 (x = hi + lo of the
-  // tiles) with the float sum of every 8 staged values
-  const bf16_bits* bt = reinterpret_cast<const bf16_bits*>(p.B);
-  const int k8n = KR >> 3;
-  for (int idx = threadIdx.x; idx < M * k8n; idx += blockDim.x) {
-    const int m = idx / k8n, k = b0s * 128 + (idx % k8n) * 8;
-    half8_t o;
-    if (k < q.K) {
-      const size_t bi = btile_index(p.KB, m, k);
-      const uint4 hv = *reinterpret_cast<const uint4*>(bt + bi);
-      const uint4 lv = *reinterpret_cast<const uint4*>(bt + bi + 64);
-      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, lw[4] = {lv.x, lv.y, lv.z, lv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = (_Float16)(__uint_as_float(hw[e] << 16) + __uint_as_float(lw[e] << 16));
-        o[2 * e + 1] = (_Float16)(__uint_as_float(hw[e] & 0xFFFF0000u) + __uint_as_float(lw[e] & 0xFFFF0000u));
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (_Float16)0.0f;
+  // Runs once per wave after its first code requests: the small prefetches,
+  // the staging writes (and any further staging) and the workgroup barrier.
+  auto after_first = [&] {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
+    if (ks == 0) {
+      epi_prefetch_x<E, NC>(p, lane, g, M, pre);
+      epi_prefetch_rope<E, NC>(p, lane, g, M, pre);
     }
-    *reinterpret_cast<half8_t*>(xs + (size_t)m * KR + (k - b0s * 128)) = o;
-    float s8 = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s8 += (float)o[e];
-    x8[idx] = s8;
-  }
-  __syncthreads();
+    stage_store(0);
+    for (int base = SP * NT; base < nstage; base += SP * NT) {
+      stage_load(base);
+      stage_store(base);
+    }
+    __syncthreads();
+  };
 
   float y[kQ4MaxRows];
 #pragma unroll
   for (int m = 0; m < kQ4MaxRows; ++m) y[m] = 0.f;
-  if (active) {
-    const int qq = lane >> 4;
-    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    for (int b = kb0; b < kb1; b += U) {
-      if (b != kb0) issue(b);
+  const int qq = lane >> 4;
+  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  // One batch of U code blocks from block b: straight-line loads (slots past
+  // the wave's last block re-read it and are skipped), then the blocks in order.
+  auto batch = [&](int b, bool first) {
+    u32x4_t cv[U];
+    uint32_t sv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (b + u < kb1) {
-          half2_t qv[16];
-          const uint32_t cw[4] = {cv[u][0], cv[u][1], cv[u][2], cv[u][3]};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const uint32_t t = ((cw[j] >> (4 * c)) & 0x000F000Fu) | 0x64006400u;
-              qv[4 * j + c] = __builtin_bit_cast(half2_t, t) - k1024;
-            }
-          const half2_t szh = __builtin_bit_cast(half2_t, sv[u]);
-          const float s = (float)szh[0], z = (float)szh[1];
-          const int xoff = (b + u - b0s) * 128 + 32 * qq;
-#pragma unroll
-          for (int m = 0; m < kQ4MaxRows; ++m) {
-            if (m < M) {
-              const half8_t* xp = reinterpret_cast<const half8_t*>(xs + (size_t)m * KR + xoff);
-              const float4 xq = *reinterpret_cast<const float4*>(x8 + (size_t)m * k8n + (xoff >> 3));
-              float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const half8_t xv = xp[v];
-                a0 = __builtin_amdgcn_fdot2(qv[4 * v], half2_t{xv[0], xv[1]}, a0, false);
-                a1 = __builtin_amdgcn_fdot2(qv[4 * v + 1], half2_t{xv[2], xv[3]}, a1, false);
-                a0 = __builtin_amdgcn_fdot2(qv[4 * v + 2], half2_t{xv[4], xv[5]}, a0, false);
-                a1 = __builtin_amdgcn_fdot2(qv[4 * v + 3], half2_t{xv[6], xv[7]}, a1, false);
-              }
-              const float xsum = ((xq.x + xq.y) + xq.z) + xq.w;
-              y[m] = fmaf(s, (a0 + a1) - z * xsum, y[m]);
-            }
-          }
-        }
+    for (int u = 0; u < U; ++u) {
+      const int bb = b + u < kb1 ? b + u : kb1 - 1;
+      cv[u] = __builtin_nontemporal_load(cp + (size_t)bb * 64);
+      sv[u] = __builtin_nontemporal_load(sp + (size_t)bb * 32);
     }
+    if (first) after_first();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (b + u >= kb1) break;
+      half2_t qv[16];
+      const uint32_t cw[4] = {cv[u][0], cv[u][1], cv[u][2], cv[u][3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t t = ((cw[j] >> (4 * c)) & 0x000F000Fu) | 0x64006400u;
+          qv[4 * j + c] = __builtin_bit_cast(half2_t, t) - k1024;
+        }
+      const half2_t szh = __builtin_bit_cast(half2_t, sv[u]);
+      const float s = (float)szh[0], z = (float)szh[1];
+      const int xoff = (b + u - b0s) * 128 + 32 * qq;
+#pragma unroll
+      for (int m = 0; m < kQ4MaxRows; ++m) {
+        if (m < M) {
+          const half8_t* xp = reinterpret_cast<const half8_t*>(xs + (size_t)m * KR + xoff);
+          const float4 xq = *reinterpret_cast<const float4*>(x8 + (size_t)m * k8n + (xoff >> 3));
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const half8_t xv = xp[v];
+            a0 = __builtin_amdgcn_fdot2(qv[4 * v], half2_t{xv[0], xv[1]}, a0, false);
+            a1 = __builtin_amdgcn_fdot2(qv[4 * v + 1], half2_t{xv[2], xv[3]}, a1, false);
+            a0 = __builtin_amdgcn_fdot2(qv[4 * v + 2], half2_t{xv[4], xv[5]}, a0, false);
+            a1 = __builtin_amdgcn_fdot2(qv[4 * v + 3], half2_t{xv[6], xv[7]}, a1, false);
+          }
+          const float xsum = ((xq.x + xq.y) + xq.z) + xq.w;
+          y[m] = fmaf(s, (a0 + a1) - z * xsum, y[m]);
+        }
+      }
+    }
+  };
+
+  stage_load(0);
+  if (n <= 0) {
+    after_first();
+  } else {
+    // the first batch is peeled: the staging registers are dead after it
+    batch(kb0, true);
+    for (int b = kb0 + U; b < kb1; b += U) batch(b, false);
   }
   if constexpr (kNorm) norm_finish<RPW, NW>(p, w, lane, M, ssv, rsc);
   // the four quarters of a row (lanes i, i+16, i+32, i+48), then the waves
