@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
 #define SD_Q4_GU 2, 4, 8
 #endif
 #ifndef SD_Q4_DOWN
-#define SD_Q4_DOWN 4, 12
+#define SD_Q4_DOWN 4, 10
 #endif
 template <int R, int W, int T>
 constexpr int Q4Rows() { return R; }
