@@ -43,12 +43,24 @@ __device__ __forceinline__ bf16_bits f2bf(float f) {
   return __builtin_bit_cast(bf16_bits, (__bf16)f);
 }
 
+// Activation operand tiles: one 1 KiB tile per (column tile t, k-block of
+// 32 inputs) holds rows 8t..8t+7 as MFMA operand B; operand column col
+// carries row col / 2, its hi part in even and its lo part in odd columns.
+// The lane of column col and k-quarter s reads the 16-byte slot
+// btile_slot(col, s) = 16 (col / 4) + 4 s + col % 4: every group of four
+// lanes reads one 64-byte segment, and rows 2j and 2j + 1 fill bytes
+// 256 j .. 256 j + 255, so a pass of M < 8 rows touches the first
+// 256 ceil(M / 2) bytes of the tile.
+constexpr int kBtileLo = 8;   // bf16 elements from a hi part to its lo part
+
+__device__ __forceinline__ int btile_slot(int col, int s) { return 16 * (col >> 2) + 4 * s + (col & 3); }
+
 // Position of activation (row m, input k) inside an activation tile buffer,
-// in bf16 units; the "lo" element sits 8 lanes (64 bf16) further.
+// in bf16 units; the "lo" element sits kBtileLo further.
 __device__ __forceinline__ size_t btile_index(int KB, int m, int k) {
   int t = m >> 3, c = m & 7;
   int kb = k >> 5, s = (k >> 3) & 3, e = k & 7;
-  return ((size_t)(t * KB + kb) * kTileU16) + (size_t)((s * 16 + c) * 8 + e);
+  return ((size_t)(t * KB + kb) * kTileU16) + (size_t)(btile_slot(2 * c, s) * 8 + e);
 }
 
 __device__ __forceinline__ void btile_put(bf16_bits* tiles, int KB, int m, int k, float v) {
@@ -56,7 +68,7 @@ __device__ __forceinline__ void btile_put(bf16_bits* tiles, int KB, int m, int k
   bf16_bits hi = f2bf(v);
   bf16_bits lo = f2bf(v - bf2f(hi));
   tiles[i] = hi;
-  tiles[i + 64] = lo;
+  tiles[i + kBtileLo] = lo;
 }
 
 // Cross-lane moves within 16-lane rows (DPP); control words of the GFX9
@@ -74,8 +86,8 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Value of lane (l ^ 8): swaps the hi and lo halves of an MFMA result row.
-__device__ __forceinline__ float swap8(float v) { return dpp_f<0x128>(v); }
+// Value of lane (l ^ 1): the lo column next to a hi column of an MFMA result.
+__device__ __forceinline__ float swap1(float v) { return dpp_f<0xB1>(v); }
 
 // Wave-wide sum / max: a fixed tree inside each 16-lane row, then the four
 // row results in lane order.  Every lane gets the same value.

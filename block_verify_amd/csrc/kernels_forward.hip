@@ -189,7 +189,7 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 // register array makes the compiler wait on it), then `issued` once when it
 // is the wave's first batch, then the products in k order.
 template <int NT, int R, typename Issued>
-__device__ __forceinline__ void mfma_batch(const i32x4_t* a, const i32x4_t* b, size_t tstride, int i,
+__device__ __forceinline__ void mfma_batch(const i32x4_t* a, const i32x4_t* const (&b)[NT], int i,
                                            f32x4_t (&acc)[NT], bool first, Issued& issued) {
   i32x4_t av[R];
   i32x4_t bv[R][NT];
@@ -198,7 +198,7 @@ __device__ __forceinline__ void mfma_batch(const i32x4_t* a, const i32x4_t* b, s
 #pragma unroll
   for (int u = 0; u < R; ++u)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bv[u][t] = b[t * tstride + (size_t)(i + u) * 64];
+    for (int t = 0; t < NT; ++t) bv[u][t] = b[t][(size_t)(i + u) * 64];
   if (first) {
     // the scheduling barriers keep the weight requests ahead of whatever
     // `issued` requests (the compiler would otherwise hoist those small
@@ -217,11 +217,11 @@ __device__ __forceinline__ void mfma_batch(const i32x4_t* a, const i32x4_t* b, s
 
 // The last r < U tiles of a wave's range, as a batch of exactly r.
 template <int NT, int U, typename Issued>
-__device__ __forceinline__ void mfma_tail(const i32x4_t* a, const i32x4_t* b, size_t tstride, int i, int r,
+__device__ __forceinline__ void mfma_tail(const i32x4_t* a, const i32x4_t* const (&b)[NT], int i, int r,
                                           f32x4_t (&acc)[NT], bool first, Issued& issued) {
   if constexpr (U > 1) {
-    if (r == U - 1) mfma_batch<NT, (U > 1 ? U - 1 : 1)>(a, b, tstride, i, acc, first, issued);
-    else mfma_tail<NT, (U > 1 ? U - 1 : 1)>(a, b, tstride, i, r, acc, first, issued);
+    if (r == U - 1) mfma_batch<NT, (U > 1 ? U - 1 : 1)>(a, b, i, acc, first, issued);
+    else mfma_tail<NT, (U > 1 ? U - 1 : 1)>(a, b, i, r, acc, first, issued);
   }
 }
 
@@ -230,21 +230,25 @@ __device__ __forceinline__ void mfma_tail(const i32x4_t* a, const i32x4_t* b, si
 // L2-resident).  Tiles travel as 32-bit integer vectors (bit-cast to bf16
 // only at the MFMA).  kb0/kb1 are wave-uniform, so every branch here is a
 // scalar one.  `issued` runs once, right after the first batch of loads has
-// been requested (also when the wave has no k-blocks).
+// been requested (also when the wave has no k-blocks).  bslot[t] is the
+// lane's 16-byte slot in the activation tiles of column tile t.
 template <int NT, int U, typename Issued>
 __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, const bf16x8_t* __restrict__ B, int KB,
-                                            int kb0, int kb1, int lane, f32x4_t (&acc)[NT], Issued&& issued) {
+                                            int kb0, int kb1, int lane, const int (&bslot)[NT], f32x4_t (&acc)[NT],
+                                            Issued&& issued) {
   const i32x4_t* a = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
-  const i32x4_t* b = reinterpret_cast<const i32x4_t*>(B) + (size_t)kb0 * 64 + lane;
-  const size_t tstride = (size_t)KB * 64;
+  const i32x4_t* b[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    b[t] = reinterpret_cast<const i32x4_t*>(B) + (size_t)(t * KB + kb0) * 64 + bslot[t];
   const int n = kb1 - kb0;
   if (n <= 0) {
     issued();
     return;
   }
   int i = 0;
-  for (; i + U <= n; i += U) mfma_batch<NT, U>(a, b, tstride, i, acc, i == 0, issued);
-  if (i < n) mfma_tail<NT, U>(a, b, tstride, i, n - i, acc, i == 0, issued);
+  for (; i + U <= n; i += U) mfma_batch<NT, U>(a, b, i, acc, i == 0, issued);
+  if (i < n) mfma_tail<NT, U>(a, b, i, n - i, acc, i == 0, issued);
 }
 
 // The same stream for a workgroup of R row groups that share the k-split:
@@ -258,13 +262,15 @@ __device__ __forceinline__ void mfma_stream(const bf16x8_t* __restrict__ A, cons
 template <int NT, int U, int R, typename Issued>
 __device__ __forceinline__ void mfma_stream_shared(const bf16x8_t* __restrict__ A, bool active,
                                                    const bf16x8_t* __restrict__ B, int KB, int kb0, int kb1, int nmax,
-                                                   int rg, int lane, f32x4_t (&acc)[NT], i32x4_t (*bsh)[NT][64],
-                                                   Issued&& issued) {
+                                                   int rg, int lane, const int (&bslot)[NT], f32x4_t (&acc)[NT],
+                                                   i32x4_t (*bsh)[NT][64], Issued&& issued) {
   static_assert(U % R == 0, "each wave loads an equal share of a batch");
   constexpr int US = U / R;
   const i32x4_t* a = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
-  const i32x4_t* b = reinterpret_cast<const i32x4_t*>(B) + (size_t)kb0 * 64 + lane;
-  const size_t tstride = (size_t)KB * 64;
+  const i32x4_t* b[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    b[t] = reinterpret_cast<const i32x4_t*>(B) + (size_t)(t * KB + kb0) * 64 + bslot[t];
   const int n = kb1 - kb0;   // equal for the R waves of this k-range
   for (int i = 0; i < nmax; i += U) {
     if (i > 0) __syncthreads();   // the previous batch's tiles have been read
@@ -275,7 +281,7 @@ __device__ __forceinline__ void mfma_stream_shared(const bf16x8_t* __restrict__ 
       for (int j = 0; j < US; ++j) {
         const int u = rg + R * j, kb = i + u < n ? i + u : n - 1;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bs[j][t] = b[t * tstride + (size_t)kb * 64];
+        for (int t = 0; t < NT; ++t) bs[j][t] = b[t][(size_t)kb * 64];
       }
     i32x4_t av[U];
     if (active && n > 0)
@@ -368,24 +374,33 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   const int s0 = (int)((unsigned)sidx * uk / un), s1 = (int)((unsigned)(sidx + 1) * uk / un);
   const unsigned span = (unsigned)(s1 - s0);
   const int kb0 = s0 + (int)((unsigned)ks * span / WK), kb1 = s0 + (int)((unsigned)(ks + 1) * span / WK);
+  // the lane's activation slot per column tile: operand columns past the
+  // tile's rows read row 0's slot of the same part (their products are never
+  // used), so a pass of M rows fetches 256 ceil(M / 2) bytes of each tile
+  int bslot[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = lane & 15;
+    bslot[t] = btile_slot((col >> 1) < M - 8 * t ? col : (col & 1), lane >> 4);
+  }
   if constexpr (kShareB) {
     const int nmax = (int)((span + WK - 1) / WK);
     const int gg = g < n_groups ? g : 0;
-    mfma_stream_shared<NT, U, WG_ROWS>(A + (size_t)gg * KB * 64, g < n_groups, B, KB, kb0, kb1, nmax, rg, lane, acc,
-                                       bsh[ks], prefetch);
+    mfma_stream_shared<NT, U, WG_ROWS>(A + (size_t)gg * KB * 64, g < n_groups, B, KB, kb0, kb1, nmax, rg, lane, bslot,
+                                       acc, bsh[ks], prefetch);
   } else if (g < n_groups) {
-    mfma_stream<NT, U>(A + (size_t)g * KB * 64, B, KB, kb0, kb1, lane, acc, prefetch);
+    mfma_stream<NT, U>(A + (size_t)g * KB * 64, B, KB, kb0, kb1, lane, bslot, acc, prefetch);
   } else {
     prefetch();
   }
   if constexpr (kNorm) norm_finish<RPW, NW>(p, w, lane, M, ssv, rsc);
-  // hi + lo (columns c and c+8) in registers, then the waves' partials in LDS
+  // hi + lo (columns 2c and 2c + 1) in registers, then the waves' partials in LDS
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float v = acc[t][r] + swap8(acc[t][r]);
-      if ((lane & 15) < 8) red[w][4 * (lane >> 4) + r][t * 8 + (lane & 15)] = v;
+      const float v = acc[t][r] + swap1(acc[t][r]);
+      if ((lane & 1) == 0) red[w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
     }
   __syncthreads();
   // fixed-order reduction over the k-split waves

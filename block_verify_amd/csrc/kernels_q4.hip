@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
       if (k >= q.K) k = 0;   // the block past K reads a valid tile and stores zeros
       const size_t bi = btile_index(p.KB, m, k);
       hv[j] = *reinterpret_cast<const uint4*>(bt + bi);
-      lv[j] = *reinterpret_cast<const uint4*>(bt + bi + 64);
+      lv[j] = *reinterpret_cast<const uint4*>(bt + bi + kBtileLo);
     }
   };
   auto stage_store = [&](int base) {
