@@ -325,11 +325,12 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
                                                                  const bf16x8_t* __restrict__ B, int KB, int n_groups,
                                                                  int rows, int nsplit_arg, GemvParams p) {
   EpiPre<NT * 8> pre;
-  // the gate word (the length stands in for a null gate) and the cache
-  // position are requested together, before any branch
-  const int gv = *(gate ? gate : d_len);
+  // the cache position is waited on only in the epilogue prefetch; without
+  // a gate the weight stream starts without waiting on any load
   if constexpr (E == Epi::QKV) pre.pos0 = *d_len;
-  if (gate && gv == 0) return;
+  if (gate) {
+    if (*gate == 0) return;
+  }
   constexpr int NW = WG_ROWS * WK;
   constexpr int NC = NT * 8;        // activation rows covered
   constexpr int RPW = (NC + NW - 1) / NW;   // norm rows per wave (NC covers every row)
