@@ -348,8 +348,14 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = w / WK, ks = w % WK;
   const int nsplit = (E == Epi::PARTIAL) ? nsplit_arg : 1;
-  const int sidx = (E == Epi::PARTIAL) ? (int)(blockIdx.x % nsplit) : 0;
-  const int g = (E == Epi::PARTIAL) ? (int)(blockIdx.x / nsplit) : (int)(blockIdx.x * WG_ROWS + rg);
+  // split-K: the splits of row group g are workgroups 8 (nsplit (g / 8) + s)
+  // + g % 8, eight apart, so round-robin dispatch over the eight XCDs puts
+  // a row group's producers and finisher on one XCD (and the producers
+  // first); the launch rounds the row groups up to a multiple of 8
+  const unsigned slot = blockIdx.x >> 3;
+  const int sidx = (E == Epi::PARTIAL) ? (int)(slot % (unsigned)nsplit) : 0;
+  const int g = (E == Epi::PARTIAL) ? (int)((slot / (unsigned)nsplit) * 8 + (blockIdx.x & 7))
+                                    : (int)(blockIdx.x * WG_ROWS + rg);
   const int M = rows;
 
   // Right after the first weight requests (which need only the preloaded
@@ -855,7 +861,7 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
     p.part = reinterpret_cast<float*>(ws + pl.part);
     p.nsplit = kOSplit;
     p.cnt = reinterpret_cast<int32_t*>(ws + pl.cnt);
-    launch_gemv<NT, 1, CfgO::WK, CfgO::template U<NT>, Epi::PARTIAL>(p.n_groups * kOSplit, s, p);
+    launch_gemv<NT, 1, CfgO::WK, CfgO::template U<NT>, Epi::PARTIAL>((p.n_groups + 7) / 8 * 8 * kOSplit, s, p);
   } else
     launch_gemv<NT, CfgO::WG_ROWS, CfgO::WK, CfgO::template U<NT>, Epi::RESID>(
         (p.n_groups + CfgO::WG_ROWS - 1) / CfgO::WG_ROWS, s, p);
@@ -878,7 +884,7 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.cnt = reinterpret_cast<int32_t*>(ws + pl.cnt);   // the last split finishes the residual
   if (q4) launch_q4_linear(Q4Linear::DOWN, p, L.q_wdown, L.s_wdown, d.F, s);
   else
-    launch_gemv<NT, 1, CfgDown::WK, CfgDown::template U<NT>, Epi::PARTIAL>(p.n_groups * kDownSplit, s, p);
+    launch_gemv<NT, 1, CfgDown::WK, CfgDown::template U<NT>, Epi::PARTIAL>((p.n_groups + 7) / 8 * 8 * kDownSplit, s, p);
 }
 
 template <int NT>
