@@ -187,18 +187,21 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // One batch of exactly R tiles: straight-line loads (a guarded load into a
 // register array makes the compiler wait on it), then `issued` once when it
-// is the wave's first batch, then the products in k order.
+// is the wave's first batch, then the products in k order.  The activation
+// tiles (cache hits) are requested before the weight tiles: the load
+// counter completes in request order, so the product of tile u then waits
+// for weight tiles 0..u only, not for the whole batch.
 template <int NT, int R, typename Issued>
 __device__ __forceinline__ void mfma_batch(const i32x4_t* a, const i32x4_t* const (&b)[NT], int i,
                                            f32x4_t (&acc)[NT], bool first, Issued& issued) {
   i32x4_t av[R];
   i32x4_t bv[R][NT];
 #pragma unroll
-  for (int u = 0; u < R; ++u) av[u] = __builtin_nontemporal_load(a + (size_t)(i + u) * 64);
-#pragma unroll
   for (int u = 0; u < R; ++u)
 #pragma unroll
     for (int t = 0; t < NT; ++t) bv[u][t] = b[t][(size_t)(i + u) * 64];
+#pragma unroll
+  for (int u = 0; u < R; ++u) av[u] = __builtin_nontemporal_load(a + (size_t)(i + u) * 64);
   if (first) {
     // the scheduling barriers keep the weight requests ahead of whatever
     // `issued` requests (the compiler would otherwise hoist those small
