@@ -648,11 +648,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
 // lane l owns head dim 64 * blockIdx.y + l and wave w the chunks c = w, w + 4,
 // ...  The partial loads of the first batch of chunks and the first
 // statistics are issued before the cache length arrives (entries past the
-// row's chunk count are read but never used).  The chunk statistics go to
-// LDS and every thread forms the same weights in chunk order; each wave sums
-// its chunks in increasing order, then the four wave sums are added in wave
-// order and divided by the normaliser (summed in chunk order).  Every order
-// depends only on the row's own position.
+// row's chunk count are read but never used).  Thread t owns chunks t,
+// t + 256, ...: it stores their statistics in LDS, the row maximum is a
+// workgroup maximum (exact in any order), and it forms its chunks' weights
+// and their part of the normaliser (its chunks in increasing order, then a
+// fixed tree over the wave and the waves in order).  Each wave sums its
+// chunks' weighted partials in increasing order, then the four wave sums are
+// added in wave order and divided by the normaliser.  Every order depends
+// only on the row's own position.
 constexpr int kMaxMergeChunks = 1024;
 constexpr int kMergeWaves = 4;
 
@@ -663,6 +666,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
     bf16_bits* __restrict__ ob) {
   __shared__ float sm[kMaxMergeChunks], sw[kMaxMergeChunks], sl[kMaxMergeChunks];
   __shared__ float wsum[kMergeWaves][64];
+  __shared__ float wred[kMergeWaves], wl[kMergeWaves];
   const int gv = *(gate ? gate : d_len);   // requested with the length, before any branch
   const int len = *d_len;
   const int m = blockIdx.x / nq, hq = blockIdx.x % nq;
@@ -691,15 +695,32 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
   int pos = len + m;
   if (pos >= max_len) pos = max_len - 1;
   const int nch = pos / kAttnChunk + 1;
-  if ((int)threadIdx.x < nch) { sm[threadIdx.x] = m0; sl[threadIdx.x] = l0; }
+  // thread t owns chunks t, t + NT, ...: their statistics go to LDS and its
+  // running max to a wave maximum (a maximum is exact in any order)
+  float mloc = -INFINITY;
+  if ((int)threadIdx.x < nch) { sm[threadIdx.x] = m0; sl[threadIdx.x] = l0; mloc = m0; }
   for (int c = threadIdx.x + NT; c < nch; c += NT) {
-    sm[c] = ml[(size_t)c * rstride * 2];
+    const float mc = ml[(size_t)c * rstride * 2];
+    sm[c] = mc;
     sl[c] = ml[(size_t)c * rstride * 2 + 1];
+    mloc = fmaxf(mloc, mc);
   }
+  mloc = warp_max(mloc);
+  if (lane == 0) wred[w] = mloc;
   __syncthreads();
-  float mx = -INFINITY;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, sm[c]);
-  for (int c = threadIdx.x; c < nch; c += NT) sw[c] = (sm[c] == -INFINITY) ? 0.f : __expf(sm[c] - mx);
+  float mx = wred[0];
+#pragma unroll
+  for (int v = 1; v < kMergeWaves; ++v) mx = fmaxf(mx, wred[v]);
+  // chunk weights, and the normaliser: each thread's chunks in increasing
+  // order, then a fixed tree over the wave and the waves in order
+  float lloc = 0.f;
+  for (int c = threadIdx.x; c < nch; c += NT) {
+    const float e = (sm[c] == -INFINITY) ? 0.f : __expf(sm[c] - mx);
+    sw[c] = e;
+    lloc = fmaf(e, sl[c], lloc);
+  }
+  lloc = warp_sum(lloc);
+  if (lane == 0) wl[w] = lloc;
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
@@ -722,8 +743,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
   wsum[w][lane] = acc;
   __syncthreads();
   if (w == 0) {
-    float L = 0.f;
-    for (int c = 0; c < nch; ++c) L = fmaf(sw[c], sl[c], L);
+    float L = wl[0];
+#pragma unroll
+    for (int v = 1; v < kMergeWaves; ++v) L += wl[v];
     float o = 0.f;
 #pragma unroll
     for (int v = 0; v < kMergeWaves; ++v) o += wsum[v][lane];
