@@ -862,7 +862,14 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   // query tiles of 16 rows per kv head, spread over up to kAttnTileSplit
   // workgroups per chunk (each tile's arithmetic is the same either way)
   const int ntq = (a.rows * d.group() + 15) / 16;
-  dim3 ag(pl.max_chunks, d.nkv, ntq < kAttnTileSplit ? ntq : kAttnTileSplit);
+  // With a chunk workgroup per CU or more (a long cache), a chunk's query
+  // tiles stay in as few workgroups as their LDS allows, which then read the
+  // chunk's K and V once; with fewer chunks the tiles are spread over up to
+  // kAttnTileSplit workgroups for parallelism.
+  const int ts_min = (ntq + kAttnMaxWgTiles - 1) / kAttnMaxWgTiles;
+  int ts = pl.max_chunks * d.nkv >= 256 ? ts_min : (ntq < kAttnTileSplit ? ntq : kAttnTileSplit);
+  if (ts < ts_min) ts = ts_min;
+  dim3 ag(pl.max_chunks, d.nkv, ts);
   if (d.hd == 128) {
     attn_chunk_kernel<128><<<ag, 64 * kAttnWaves, 0, s>>>(a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l),
                                                            a.rows, a.c->max_len, a.c->lp, d.group(), att_o, att_ml,
