@@ -760,7 +760,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
 // them requested before any is used), then a wave reduction and the waves in
 // order.
 // ---------------------------------------------------------------------------
-constexpr int kLmrThreads = 1024, kLmrWaves = kLmrThreads / 64, kLmrPer = 4;
+constexpr int kLmrThreads = 1024, kLmrWaves = kLmrThreads / 64, kLmrPer = 5;   // 5120 partials: a 151936- or 152064-entry vocabulary in two-row-group workgroups stays in registers
 
 __global__ __launch_bounds__(kLmrThreads) void lm_reduce_kernel(const float* __restrict__ part, int n_wg, int rows,
                                                                 int32_t* __restrict__ argmax_out,
