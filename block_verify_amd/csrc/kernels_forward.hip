@@ -413,7 +413,53 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
       if ((lane & 1) == 0) red[w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
     }
   __syncthreads();
-  // fixed-order reduction over the k-split waves
+  if constexpr (E == Epi::SWIGLU) {
+    // the epilogue wave sums the k-split partials of its own entries, in the
+    // order of the reduction below, and needs no second pass through LDS
+    if (ks != 0 || g >= n_groups) return;
+    const int KBo = p.F >> 5;
+    for (int idx = lane; idx < 8 * M; idx += 64) {
+      const int i = idx & 7, m = idx >> 3;
+      float gt = 0.f, up = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < WK; ++s2) {
+        gt += red[rg * WK + s2][i][m];
+        up += red[rg * WK + s2][i + 8][m];
+      }
+      const float r = rsc[m];
+      gt *= r;
+      up *= r;
+      btile_put(p.hb_out, KBo, m, 8 * g + i, gt / (1.0f + __expf(-gt)) * up);
+    }
+    return;
+  } else if constexpr (E != Epi::LMHEAD) {
+    // one wave per row group: it sums the k-split partials of the group (in
+    // the order of the reduction below) into its first wave's slot, which
+    // then serves as the group's finished products
+    if (ks != 0 || g >= n_groups) return;
+    constexpr int kE = (16 * NC + 63) / 64;
+    float v[kE];
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < 16 * NC) {
+        const int i = idx / NC, m = idx % NC;
+        v[j] = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < WK; ++s2) v[j] += red[rg * WK + s2][i][m];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < 16 * NC) red[rg * WK][idx / NC][idx % NC] = v[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    gemv_epilogue<WG_ROWS, NC, E>(p, red + rg * (WK - 1), rsc, pre, w, lane, rg, 0, g, sidx, M);
+    return;
+  }
+  // fixed-order reduction over the k-split waves (whole-workgroup epilogue)
   for (int idx = threadIdx.x; idx < WG_ROWS * 16 * NC; idx += blockDim.x) {
     int rr = idx / (16 * NC), rem = idx % (16 * NC), i = rem / NC, m = rem % NC;
     float v = 0.f;
