@@ -342,7 +342,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   constexpr bool kShareB = WG_ROWS > 1 && U % WG_ROWS == 0 && WK * U * NT * 1024 <= 48 * 1024;
   __shared__ i32x4_t bsh[kShareB ? WK : 1][kShareB ? U : 1][NT][64];
   __shared__ float red[NW][16][NC + 1];
-  __shared__ float fin[WG_ROWS][16][NC + 1];
+  __shared__ float fin[E == Epi::LMHEAD ? WG_ROWS : 1][16][NC + 1];   // whole-workgroup epilogue only
   __shared__ float rsc[kMaxRows];
 
   const int lane = threadIdx.x & 63;

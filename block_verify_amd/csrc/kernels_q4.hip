@@ -114,7 +114,6 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
   constexpr int NT = 64 * NW;
   extern __shared__ __align__(16) unsigned char q4_lds[];
   __shared__ float red[NW][16][NC + 1];
-  __shared__ float fin[WG_ROWS][16][NC + 1];
   __shared__ float rsc[kMaxRows];
 
   const int lane = threadIdx.x & 63;
@@ -280,15 +279,29 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p
     if (lane < 16 && m < M) red[w][lane][m] = v;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < WG_ROWS * 16 * M; idx += blockDim.x) {
-    int rr = idx / (16 * M), rem = idx % (16 * M), i = rem / M, m = rem % M;
-    float v = 0.f;
+  // one wave per row group sums the group's k-split partials (in wave
+  // order) into its first wave's slot and runs the epilogue from there
+  if (ks != 0 || g >= p.n_groups) return;
+  constexpr int kE = (16 * kQ4MaxRows + 63) / 64;
+  float v[kE];
 #pragma unroll
-    for (int s2 = 0; s2 < WK; ++s2) v += red[rr * WK + s2][i][m];
-    fin[rr][i][m] = v;
+  for (int j = 0; j < kE; ++j) {
+    const int idx = lane + 64 * j;
+    if (idx < 16 * M) {
+      const int i = idx / M, m = idx % M;
+      v[j] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < WK; ++s2) v[j] += red[rg * WK + s2][i][m];
+    }
   }
-  __syncthreads();
-  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, pre, w, lane, rg, ks, g, sidx, M);
+#pragma unroll
+  for (int j = 0; j < kE; ++j) {
+    const int idx = lane + 64 * j;
+    if (idx < 16 * M) red[rg * WK][idx / M][idx % M] = v[j];
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  gemv_epilogue<WG_ROWS, NC, E>(p, red + rg * (WK - 1), rsc, pre, w, lane, rg, 0, g, sidx, M);
 }
 
 // Launch shapes (row groups per workgroup, k-split waves, code blocks in
