@@ -157,6 +157,10 @@ struct specdec_round {
   hipStream_t cap_stream;
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
+  // the whole round as one graph, replayed when no per-term events are
+  // recorded (one launch per round instead of four)
+  hipGraph_t fused_graph;
+  hipGraphExec_t fused_exec;
 };
 
 extern "C" {
@@ -455,6 +459,8 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   r->prompt_len = 0;
   r->calls = 0;
   r->cap_stream = nullptr;
+  r->fused_graph = nullptr;
+  r->fused_exec = nullptr;
   if (q.events && q.n_events < 5) { delete r; return SPECDEC_EINVAL; }
   r->tplan = ws_plan(d, rows, q.target_cache->max_len);
   if (q.ws_bytes < r->tplan.total) { delete r; return SPECDEC_ECAPACITY; }
@@ -508,6 +514,8 @@ void specdec_round_destroy(specdec_round* r) {
   if (!r) return;
   for (auto x : r->execs) (void)hipGraphExecDestroy(x);
   for (auto g : r->graphs) (void)hipGraphDestroy(g);
+  if (r->fused_exec) (void)hipGraphExecDestroy(r->fused_exec);
+  if (r->fused_graph) (void)hipGraphDestroy(r->fused_graph);
   if (r->cap_stream) (void)hipStreamDestroy(r->cap_stream);
   delete r;
 }
@@ -606,6 +614,10 @@ int specdec_round_graph(specdec_round* r) {
   for (auto g : r->graphs) (void)hipGraphDestroy(g);
   r->execs.clear();
   r->graphs.clear();
+  if (r->fused_exec) (void)hipGraphExecDestroy(r->fused_exec);
+  if (r->fused_graph) (void)hipGraphDestroy(r->fused_graph);
+  r->fused_exec = nullptr;
+  r->fused_graph = nullptr;
   for (int seg = 0; seg < 4; ++seg) {
     e = hipStreamBeginCapture(r->cap_stream, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) break;
@@ -620,11 +632,27 @@ int specdec_round_graph(specdec_round* r) {
     r->graphs.push_back(g);
     r->execs.push_back(x);
   }
+  if (e == hipSuccess) {
+    // the four segments back to back in one capture
+    e = hipStreamBeginCapture(r->cap_stream, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      hipError_t e2 = hipSuccess;
+      for (int seg = 0; seg < 4 && e2 == hipSuccess; ++seg) e2 = enqueue_segment(r, r->cap_stream, seg);
+      hipGraph_t g = nullptr;
+      e = hipStreamEndCapture(r->cap_stream, &g);
+      if (e2 != hipSuccess) e = e2;
+      if (e == hipSuccess) e = hipGraphInstantiate(&r->fused_exec, g, nullptr, nullptr, 0);
+      if (g && e == hipSuccess) r->fused_graph = g;
+      else if (g) (void)hipGraphDestroy(g);
+    }
+  }
   if (e != hipSuccess) {
     for (auto x : r->execs) (void)hipGraphExecDestroy(x);
     for (auto g : r->graphs) (void)hipGraphDestroy(g);
     r->execs.clear();
     r->graphs.clear();
+    if (r->fused_exec) (void)hipGraphExecDestroy(r->fused_exec);
+    r->fused_exec = nullptr;
   }
   return hip_status(e);
 }
@@ -632,6 +660,16 @@ int specdec_round_graph(specdec_round* r) {
 int specdec_round_graph_launch(specdec_round* r, int32_t n_rounds, void* stream) {
   if (!r || r->execs.size() != 4 || n_rounds < 0) return SPECDEC_EINVAL;
   hipStream_t s = (hipStream_t)stream;
+  const specdec_round_desc& q = r->desc;
+  const bool timed = q.events && (q.n_events / 5) * 5 > 0;
+  if (!timed && r->fused_exec) {
+    for (int i = 0; i < n_rounds; ++i) {
+      ++r->calls;
+      hipError_t e = hipGraphLaunch(r->fused_exec, s);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    return SPECDEC_OK;
+  }
   for (int i = 0; i < n_rounds; ++i) {
     const long call = r->calls++;
     hipError_t e = hipSuccess;

@@ -253,17 +253,20 @@ int specdec_round_reset(specdec_round* r, int32_t n_target, void* stream);
  * n_committed >= n_target the round's kernels return without work. */
 int specdec_verify_round(specdec_round* r, void* stream);
 
-/* Capture the round (exactly the work of specdec_verify_round) as four HIP
- * graphs owned by the round handle: round start + draft provision, block
- * verify, acceptance + trim, repair.  Every dynamic value a round uses
- * (lengths, tokens, counters) lives in device memory, so one set of graphs
- * serves every position.  Captures on an internal stream; no device memory
- * is allocated. */
+/* Capture the round (exactly the work of specdec_verify_round) as HIP
+ * graphs owned by the round handle: four segment graphs (round start +
+ * draft provision, block verify, acceptance + trim, repair) and one graph
+ * of the whole round.  Every dynamic value a round uses (lengths, tokens,
+ * counters) lives in device memory, so one set of graphs serves every
+ * position.  Captures on an internal stream; no device memory is
+ * allocated. */
 int specdec_round_graph(specdec_round* r);
 
-/* Enqueue `n_rounds` rounds on `stream` as replays of the four graphs.  The
- * per-term events of the ring (if configured) are recorded between the
- * graphs, exactly as specdec_verify_round records them. */
+/* Enqueue `n_rounds` rounds on `stream` as graph replays.  With a per-term
+ * event ring configured, each round replays the four segment graphs with the
+ * ring's events recorded between them, exactly as specdec_verify_round
+ * records them; without one, each round is one launch of the whole-round
+ * graph (the same kernels, one launch instead of four). */
 int specdec_round_graph_launch(specdec_round* r, int32_t n_rounds, void* stream);
 
 /* Device views of a round's internal buffers, for inspection by tests:

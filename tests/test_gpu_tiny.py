@@ -192,6 +192,45 @@ def test_graph_replay_commits_the_same_tokens(env, gpu_ar, schedule):
     assert r.ws.error_bits() == 0
 
 
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_timed_graph_replay_records_terms(env, gpu_ar, schedule):
+    """With a ring of per-term events the round replays as four graphs with the
+    events between them (without one, as a single graph): the same tokens, and
+    five ordered timestamps per round."""
+    import ctypes
+    from block_verify_amd.synth import make_draft_table
+    b = env["b"]
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    n_ev = 5 * (N_NEW + 1)
+    evs = (ctypes.c_void_p * n_ev)()
+    for i in range(n_ev):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreateWithFlags(ctypes.byref(e), 0) == 0
+        evs[i] = e.value
+    table = make_draft_table(np.array(gpu_ar), env["shape"].vocab, 0.4)
+    r = b.Round(env["model"], K, schedule=schedule, table=table, max_len=512, events=evs, n_events=n_ev)
+    r.prefill(env["prompt"])
+    r.capture()
+    c0 = r.calls()
+    st, toks = r.run(N_NEW, graph=True)
+    torch.cuda.synchronize()
+    assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+    assert r.calls() - c0 >= st.round
+    for c in range(c0, r.calls()):
+        base = (c % (N_NEW + 1)) * 5
+        for i in range(4):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[base + i], evs[base + i + 1]) == 0
+            assert ms.value >= 0.0
+    assert r.ws.error_bits() == 0
+    del r
+    for i in range(n_ev):
+        hip.hipEventDestroy(evs[i])
+
+
 def test_spec_no_bonus(env, gpu_ar):
     from block_verify_amd.synth import make_draft_table
     b = env["b"]
