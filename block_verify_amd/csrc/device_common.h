@@ -89,6 +89,15 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // Value of lane (l ^ 1): the lo column next to a hi column of an MFMA result.
 __device__ __forceinline__ float swap1(float v) { return dpp_f<0xB1>(v); }
 
+// Sum over each 16-lane row in a fixed tree; every lane of the row gets it.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return v;
+}
+
 // Wave-wide sum / max: a fixed tree inside each 16-lane row, then the four
 // row results in lane order.  Every lane gets the same value.
 __device__ __forceinline__ float warp_sum(float v) {

@@ -157,8 +157,9 @@ __device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane,
 }
 
 // Residual epilogue of 16 outputs (one row group g) x M rows: x += y,
-// the next norm's operand tiles of x * gain and the group's sum of squares.
-// f[i][m] holds y on entry and the new x on exit; pre holds x and the gains.
+// the next norm's operand tiles of x * gain and the group's sum of squares
+// (the 16 lanes of a row sum in a fixed tree).  f[i][m] holds y; pre holds
+// x and the gains.
 template <int NC>
 __device__ __forceinline__ void resid_epilogue(const GemvParams& p, float (*f)[NC + 1], const EpiPre<NC>& pre, int lane,
                                                int g, int M) {
@@ -166,21 +167,18 @@ __device__ __forceinline__ void resid_epilogue(const GemvParams& p, float (*f)[N
 #pragma unroll
   for (int j = 0; j < EpiPre<NC>::kX; ++j) {
     const int idx = lane + 64 * j;
-    if (idx < 16 * M) {
-      const int i = idx & 15, m = idx >> 4, n = 16 * g + i;
+    const bool ok = idx < 16 * M;
+    const int i = idx & 15, m = idx >> 4, n = 16 * g + i;
+    float sq = 0.f;
+    if (ok) {
       const float xn = pre.xv[j] + f[i][m];
       p.x[(size_t)m * p.H + n] = xn;
-      f[i][m] = xn;
       btile_put(p.xb_out, KBo, m, n, xn * pre.gain);
+      sq = xn * xn;
     }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  for (int m = lane; m < M; m += 64) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s = fmaf(f[i][m], f[i][m], s);
-    p.ss_out[(size_t)m * NP + g] = s;
+    // lanes 16 m' .. 16 m' + 15 of this pass hold row m' + 4 j
+    sq = row16_sum(sq);
+    if (ok && i == 0) p.ss_out[(size_t)m * NP + g] = sq;
   }
 }
 
