@@ -518,7 +518,9 @@ constexpr int kAttnWaves = kAttnChunk / 16;   // waves per chunk workgroup: 16 k
 constexpr int kAttnTileSplit = SD_ATTN_TILE_SPLIT;   // workgroups sharing one chunk's query tiles
 constexpr int kAttnMaxWgTiles = (kQTiles + kAttnTileSplit - 1) / kAttnTileSplit;   // query tiles per workgroup
 
-template <int HD>
+// MAXT: query tiles a workgroup may hold (sizes the query staging in
+// registers and LDS); the launch picks the smallest that covers its tiles.
+template <int HD, int MAXT>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
     const int32_t* gate, const int32_t* __restrict__ d_len, const bf16_bits* __restrict__ qb,
     const bf16_bits* __restrict__ Kc, const bf16_bits* __restrict__ Vt, int rows, int max_len, int lp, int G,
@@ -534,7 +536,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
   constexpr int DTW = (DT + NW - 1) / NW;       // output tiles per wave
   constexpr int KB2 = C / 32;                   // 32-key blocks of P^T
   __shared__ __attribute__((aligned(16))) float Pl[16][C + 4];
-  __shared__ i32x4_t qs[kAttnMaxWgTiles][KBH * 2][64];
+  static_assert(MAXT >= 1 && MAXT <= kAttnMaxWgTiles, "query tiles per workgroup");
+  __shared__ i32x4_t qs[MAXT][KBH * 2][64];
   const int c = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -551,13 +554,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
   // chunk), staged once per workgroup in LDS: each wave loads a share
   const int t0 = blockIdx.z, TS = gridDim.z;
   if (t0 >= NTq) return;
-  const int ntw = (NTq - t0 + TS - 1) / TS;   // tiles of this workgroup (<= kAttnMaxWgTiles)
+  const int ntw = (NTq - t0 + TS - 1) / TS;   // tiles of this workgroup (<= MAXT)
   const i32x4_t* qh = reinterpret_cast<const i32x4_t*>(qb + qtile_head(h, HD));
   // this wave's share of the query tile parts, requested before the K/V rows
   // and written to LDS once every load of the wave is in flight
   // (unconditional loads, parts past the workgroup's tiles re-read part 0:
   // guarded loads into a register array would each be waited on)
-  constexpr int QPW = (kAttnMaxWgTiles * KBH * 2 + NW - 1) / NW;
+  constexpr int QPW = (MAXT * KBH * 2 + NW - 1) / NW;
   i32x4_t qreg[QPW];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
@@ -878,6 +881,23 @@ static void launch_gemv(int wgs, hipStream_t s, const GemvParams& p) {
                                                                       p.rows, p.nsplit, p);
 }
 
+// The chunk kernel instantiated for the smallest tile capacity (1, 2 or 4)
+// that holds the workgroup's wt query tiles.
+template <int HD>
+static void launch_attn(int wt, dim3 grid, hipStream_t s, const int32_t* gate, const int32_t* d_len,
+                        const bf16_bits* qb, const bf16_bits* Kc, const bf16_bits* Vt, int rows, int max_len, int lp,
+                        int G, float* o_part, float* ml_part, int max_chunks) {
+  if (wt <= 1)
+    attn_chunk_kernel<HD, 1><<<grid, 64 * kAttnWaves, 0, s>>>(gate, d_len, qb, Kc, Vt, rows, max_len, lp, G, o_part,
+                                                              ml_part, max_chunks);
+  else if (wt <= 2)
+    attn_chunk_kernel<HD, 2><<<grid, 64 * kAttnWaves, 0, s>>>(gate, d_len, qb, Kc, Vt, rows, max_len, lp, G, o_part,
+                                                              ml_part, max_chunks);
+  else
+    attn_chunk_kernel<HD, kAttnMaxWgTiles><<<grid, 64 * kAttnWaves, 0, s>>>(gate, d_len, qb, Kc, Vt, rows, max_len,
+                                                                            lp, G, o_part, ml_part, max_chunks);
+}
+
 template <int NT>
 static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   const Dims& d = a.m->d;
@@ -916,16 +936,15 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   int ts = pl.max_chunks * d.nkv >= 256 ? ts_min : (ntq < kAttnTileSplit ? ntq : kAttnTileSplit);
   if (ts < ts_min) ts = ts_min;
   dim3 ag(pl.max_chunks, d.nkv, ts);
+  const int wt = (ntq + ts - 1) / ts;   // query tiles per workgroup
   if (d.hd == 128) {
-    attn_chunk_kernel<128><<<ag, 64 * kAttnWaves, 0, s>>>(a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l),
-                                                           a.rows, a.c->max_len, a.c->lp, d.group(), att_o, att_ml,
-                                                           pl.max_chunks);
+    launch_attn<128>(wt, ag, s, a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l), a.rows, a.c->max_len,
+                     a.c->lp, d.group(), att_o, att_ml, pl.max_chunks);
     attn_merge_kernel<128><<<dim3(a.rows * d.nq, 2), 64 * kMergeWaves, 0, s>>>(
         a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
   } else {
-    attn_chunk_kernel<64><<<ag, 64 * kAttnWaves, 0, s>>>(a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l),
-                                                          a.rows, a.c->max_len, a.c->lp, d.group(), att_o, att_ml,
-                                                          pl.max_chunks);
+    launch_attn<64>(wt, ag, s, a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l), a.rows, a.c->max_len,
+                    a.c->lp, d.group(), att_o, att_ml, pl.max_chunks);
     attn_merge_kernel<64><<<dim3(a.rows * d.nq, 1), 64 * kMergeWaves, 0, s>>>(
         a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
   }
