@@ -101,6 +101,24 @@ def test_block_forward_rows(env, rows):
     assert ws.error_bits() == 0
 
 
+@pytest.mark.parametrize("rows", [1, 5, 9])
+def test_long_cache_launch_shapes_give_the_same_logits(env, rows):
+    """A cache long enough for a chunk workgroup per CU switches the attention to
+    one workgroup per chunk (query tiles kept together); the arithmetic of every
+    tile is unchanged, so the logits equal those of a short cache bit for bit."""
+    say(f"tiny long cache rows={rows}")
+    toks = np.random.default_rng(100 + rows).integers(0, env["shape"].vocab, rows)
+    out = []
+    for max_len in (512, 8448):
+        cache, ws = _fresh(env, max_len)
+        _gpu_prefill(env, cache, ws, env["prompt"])
+        logits, am, lse = _gpu_forward(env, cache, ws, toks)
+        assert cache.length() == P + rows and ws.error_bits() == 0
+        out.append((logits, am, lse))
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1], out[1][1]) and np.array_equal(out[0][2], out[1][2])
+
+
 def test_batch_invariance_block_equals_single_steps(env):
     """Rows of an M=5 block equal five M=1 steps bit for bit (logits and cache)."""
     toks = np.array([5, 77, 4095, 0, 1234])
