@@ -95,6 +95,10 @@ constexpr int kMaxSplit = 8;
 #endif
 constexpr int kDownSplit = SD_DOWN_SPLIT;
 constexpr int kQ4DownSplit = 4;
+// With two K splits the producer takes kSplit0Share / 64 of the k-blocks
+// (the finisher, which waits for its partials, the rest), as long as the
+// finisher's waves still stream their share in one batch.
+constexpr unsigned kSplit0Share = 30;
 
 // Workspace plan for one model.
 struct WsPlan {

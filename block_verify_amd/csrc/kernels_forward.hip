@@ -36,7 +36,7 @@ namespace sd {
 #define SD_CFG_GU 1, 8, 6
 #endif
 #ifndef SD_CFG_DOWN
-#define SD_CFG_DOWN 1, 8, 18
+#define SD_CFG_DOWN 1, 8, 19
 #endif
 #ifndef SD_CFG_LM
 #define SD_CFG_LM 2, 2, 12
@@ -381,7 +381,17 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   // 32-bit unsigned arithmetic: every term is small (split index < 8,
   // k-blocks < 2^16), and a 64-bit division costs hundreds of instructions
   const unsigned uk = (unsigned)KB, un = (unsigned)nsplit;
-  const int s0 = (int)((unsigned)sidx * uk / un), s1 = (int)((unsigned)(sidx + 1) * uk / un);
+  int s0 = (int)((unsigned)sidx * uk / un), s1 = (int)((unsigned)(sidx + 1) * uk / un);
+  if (E == Epi::PARTIAL && nsplit == 2) {
+    // the producer's smaller share is in memory by the time the finisher
+    // has streamed its larger one (when that still fits one batch per wave
+    // of the one-tile launch shape: the cut depends on the matrix only, never
+    // on the row count)
+    const unsigned sa = uk * kSplit0Share / 64u;
+    const unsigned cut = (uk - sa + WK - 1) / WK <= (unsigned)CfgDown::template U<1> ? sa : uk / 2u;
+    s0 = sidx == 0 ? 0 : (int)cut;
+    s1 = sidx == 0 ? (int)cut : (int)uk;
+  }
   const unsigned span = (unsigned)(s1 - s0);
   const int kb0 = s0 + (int)((unsigned)ks * span / WK), kb1 = s0 + (int)((unsigned)(ks + 1) * span / WK);
   // the lane's activation slot per column tile: operand columns past the
