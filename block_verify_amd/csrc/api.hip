@@ -130,6 +130,12 @@ RoundWsPlan round_ws_plan(int V, int k) {
   p.ssum = take((size_t)n_slices(V) * 4);
   p.sw = take((size_t)n_slices(V) * 8);
   p.sctl = take(4 * 4);
+  p.t_lse = take(K1 * 4);
+  p.tsmax = take(K1 * n_slices(V) * 4);
+  p.tssum = take(K1 * n_slices(V) * 4);
+  p.hcnt = take((size_t)n_slices(V) * kTruncBins * 4);
+  p.hmass = take((size_t)n_slices(V) * kTruncBins * 8);
+  p.trunc = take(sizeof(TruncState));
   p.draft_argmax = take(4);
   p.rows_logits = take(K1 * V * 4);
   p.saved_logits = take((size_t)V * 4);
@@ -142,7 +148,7 @@ RoundWsPlan round_ws_plan(int V, int k) {
 }
 
 hipError_t launch_copy_last(const FwdArgs& a, float* logits_dst, int32_t* argmax_dst, float* lse_dst);
-hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStream_t s);
+hipError_t launch_advance(int32_t* d_len, int rows, int max_len, const int32_t* gate, hipStream_t s);
 
 }  // namespace sd
 
@@ -428,7 +434,7 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   const specdec_round_desc& q = *desc;
   if (q.k < 1 || q.k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
   if (q.state_cap <= 0) return SPECDEC_EINVAL;
-  if (q.mode != SPECDEC_GREEDY && q.mode != SPECDEC_STOCHASTIC) return SPECDEC_EINVAL;
+  if (q.mode != SPECDEC_GREEDY && q.mode != SPECDEC_STOCHASTIC && q.mode != SPECDEC_RELAXED) return SPECDEC_EINVAL;
   if (q.schedule != SPECDEC_SCHEDULE_A && q.schedule != SPECDEC_SCHEDULE_B) return SPECDEC_EINVAL;
   if (q.draft_source < SPECDEC_DRAFT_TABLE || q.draft_source > SPECDEC_DRAFT_Q4_SELF) return SPECDEC_EINVAL;
   const Dims& d = q.target->d;
@@ -437,7 +443,13 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   if (q.schedule == SPECDEC_SCHEDULE_B && !q.bonus) return SPECDEC_EINVAL;
   if (q.mode == SPECDEC_STOCHASTIC && (q.schedule != SPECDEC_SCHEDULE_A || q.draft_source != SPECDEC_DRAFT_NOISY_SELF))
     return SPECDEC_EUNSUPPORTED;
-  if (q.mode == SPECDEC_GREEDY && q.draft_source == SPECDEC_DRAFT_NOISY_SELF) return SPECDEC_EINVAL;
+  if (q.mode != SPECDEC_STOCHASTIC && q.draft_source == SPECDEC_DRAFT_NOISY_SELF) return SPECDEC_EINVAL;
+  if (q.mode == SPECDEC_STOCHASTIC) {
+    if (!(q.temperature > 0.f) || !isfinite(q.temperature)) return SPECDEC_EINVAL;
+    if (q.top_k < 0 || q.top_k > d.V || !(q.top_p > 0.f && q.top_p <= 1.f)) return SPECDEC_EINVAL;
+    if (((q.top_k > 0 && q.top_k < d.V) || q.top_p < 1.f) && d.V > (1 << kKeyIndexBits)) return SPECDEC_EUNSUPPORTED;
+  }
+  if (q.mode == SPECDEC_RELAXED && !(q.relax_delta >= 0.f)) return SPECDEC_EINVAL;
   if ((q.draft_source == SPECDEC_DRAFT_TABLE || q.draft_source == SPECDEC_DRAFT_MODEL) &&
       (!q.d_draft_table || q.table_len <= 0))
     return SPECDEC_EINVAL;
@@ -495,6 +507,12 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   v.ssum = reinterpret_cast<float*>(w + rp.ssum);
   v.sw = reinterpret_cast<double*>(w + rp.sw);
   v.sctl = reinterpret_cast<int32_t*>(w + rp.sctl);
+  v.t_lse = reinterpret_cast<float*>(w + rp.t_lse);
+  v.tsmax = reinterpret_cast<float*>(w + rp.tsmax);
+  v.tssum = reinterpret_cast<float*>(w + rp.tssum);
+  v.hcnt = reinterpret_cast<int32_t*>(w + rp.hcnt);
+  v.hmass = reinterpret_cast<double*>(w + rp.hmass);
+  v.trunc = reinterpret_cast<TruncState*>(w + rp.trunc);
   v.t_len = q.target_cache->d_len;
   v.d_len = q.draft_source == SPECDEC_DRAFT_MODEL ? q.draft_cache->d_len : nullptr;
   v.err = static_cast<int32_t*>(q.d_ws);
@@ -506,6 +524,10 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   v.k = q.k; v.V = d.V; v.bonus = q.bonus ? 1 : 0; v.schedule = q.schedule; v.draft_source = q.draft_source;
   v.mode = q.mode;
   v.state_cap = q.state_cap;
+  v.inv_t = q.mode == SPECDEC_STOCHASTIC ? 1.0f / q.temperature : 1.0f;
+  v.top_k = q.mode == SPECDEC_STOCHASTIC ? q.top_k : 0;
+  v.top_p = q.mode == SPECDEC_STOCHASTIC ? q.top_p : 1.0f;
+  v.relax_delta = q.mode == SPECDEC_RELAXED ? q.relax_delta : 0.0f;
   *out = r;
   return SPECDEC_OK;
 }
@@ -716,6 +738,8 @@ static hipError_t enqueue_segment(specdec_round* r, hipStream_t s, int seg) {
     if (!B) {
       e = fwd(r, false, v.repair_tok, 1, v.saved_logits, v.repair_argmax, v.repair_lse, rep, s);
       if (e == hipSuccess) e = launch_repair_done(v, s);
+      // without the bonus a fully accepted round keeps its last verify row as saved_next
+      if (e == hipSuccess && !q.bonus) e = launch_copy_saved(v, s);
     }
     if (e == hipSuccess && q.draft_source == SPECDEC_DRAFT_MODEL)
       e = fwd(r, true, v.repair_tok, 1, v.draft_logits, v.draft_argmax, nullptr, rep, s);

@@ -70,7 +70,7 @@ constexpr int kOSplit = SD_O_SPLIT;   // K splits of the O projection (1: one wo
 static_assert(kOSplit <= kMaxSplit && (kOSplit == 1 || CfgO::WG_ROWS == 1), "O split-K shape");
 
 
-hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStream_t s);
+hipError_t launch_advance(int32_t* d_len, int rows, int max_len, const int32_t* gate, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Packing (setup): row-major bf16 -> MFMA weight tiles.
@@ -824,8 +824,8 @@ constexpr int kLmrThreads = 1024, kLmrWaves = kLmrThreads / 64, kLmrPer = 5;   /
 __global__ __launch_bounds__(kLmrThreads) void lm_reduce_kernel(const float* __restrict__ part, int n_wg, int rows,
                                                                 int32_t* __restrict__ argmax_out,
                                                                 float* __restrict__ lse_out,
-                                                                int32_t* __restrict__ d_len, int32_t* err,
-                                                                const int32_t* gate) {
+                                                                int32_t* __restrict__ d_len, int max_len,
+                                                                int32_t* err, const int32_t* gate) {
   if (gate && *gate == 0) return;
   const int m = blockIdx.x;
   const float* pp = part + (size_t)m * n_wg * 3;
@@ -878,7 +878,8 @@ __global__ __launch_bounds__(kLmrThreads) void lm_reduce_kernel(const float* __r
     for (int v = 0; v < kLmrWaves; ++v) tot += ss[v];
     if (argmax_out) argmax_out[m] = gidx;
     if (lse_out) lse_out[m] = gmax + logf(tot);
-    if (m == 0) *d_len += rows;
+    // a forward past the capacity (flagged by the embedding) leaves the length as it was
+    if (m == 0 && *d_len + rows <= max_len) *d_len += rows;
   }
 }
 
@@ -1013,7 +1014,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
   base.nq = d.nq; base.nkv = d.nkv; base.hd = d.hd; base.F = d.F; base.V = d.V;
   for (int l = 0; l < d.L; ++l) launch_gemvs_layer<NT>(a, l, base);
 
-  if (a.skip_head) return launch_advance(a.c->d_len, a.rows, a.gate, s);
+  if (a.skip_head) return launch_advance(a.c->d_len, a.rows, a.c->max_len, a.gate, s);
   GemvParams p = base;
   p.A = a.m->lm_head; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.V / 16;
   p.ss_in = ss; p.logits = a.logits;
@@ -1021,7 +1022,8 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
   p.lm_part = lm_part;
   int wgs = (p.n_groups + CfgLM::WG_ROWS - 1) / CfgLM::WG_ROWS;
   launch_gemv<NT, CfgLM::WG_ROWS, CfgLM::WK, CfgLM::template U<NT>, Epi::LMHEAD>(wgs, s, p);
-  lm_reduce_kernel<<<a.rows, kLmrThreads, 0, s>>>(lm_part, wgs, a.rows, a.argmax, a.lse, a.c->d_len, err, a.gate);
+  lm_reduce_kernel<<<a.rows, kLmrThreads, 0, s>>>(lm_part, wgs, a.rows, a.argmax, a.lse, a.c->d_len, a.c->max_len,
+                                                  err, a.gate);
   return hipGetLastError();
 }
 
@@ -1053,13 +1055,13 @@ hipError_t launch_trim(int32_t* d_len, int32_t new_len, const int32_t* d_base, i
   return hipGetLastError();
 }
 
-__global__ void advance_kernel(int32_t* d_len, int rows, const int32_t* gate) {
+__global__ void advance_kernel(int32_t* d_len, int rows, int max_len, const int32_t* gate) {
   if (gate && *gate == 0) return;
-  if (threadIdx.x == 0) *d_len += rows;
+  if (threadIdx.x == 0 && *d_len + rows <= max_len) *d_len += rows;
 }
 
-hipError_t launch_advance(int32_t* d_len, int rows, const int32_t* gate, hipStream_t s) {
-  advance_kernel<<<1, 64, 0, s>>>(d_len, rows, gate);
+hipError_t launch_advance(int32_t* d_len, int rows, int max_len, const int32_t* gate, hipStream_t s) {
+  advance_kernel<<<1, 64, 0, s>>>(d_len, rows, max_len, gate);
   return hipGetLastError();
 }
 

@@ -67,6 +67,7 @@ __global__ void round_start_kernel(RoundDev r) {
   int open = st->n_committed < st->n_target;
   r.flags[kFlagOpen] = open;
   r.flags[kFlagRepair] = open;
+  r.flags[kFlagCopySaved] = 0;
   if (!open) return;
   const int base = r.schedule == SPECDEC_SCHEDULE_B ? 1 : 0;
   if (base) r.block[0] = st->last_tok;
@@ -84,18 +85,29 @@ __global__ void round_start_kernel(RoundDev r) {
 }
 
 // ---------------------------------------------------------------------------
-// Greedy acceptance + trim.
+// Greedy acceptance + trim (exact, or relaxed by a logit gap).
 // ---------------------------------------------------------------------------
 __global__ void accept_greedy_kernel(RoundDev r) {
   if (threadIdx.x != 0) return;
   if (r.flags[kFlagOpen] == 0) return;
   specdec_round_state* st = r.state;
-  const int k = r.k;
+  const int k = r.k, V = r.V;
   const bool B = r.schedule == SPECDEC_SCHEDULE_B;
   const int32_t* d = r.block + (B ? 1 : 0);
   auto v = [&](int j) -> int32_t { return B ? r.rows_argmax[j] : (j == 0 ? st->saved_argmax : r.rows_argmax[j - 1]); };
+  // target logits at draft j's position
+  auto row = [&](int j) -> const float* {
+    return B ? r.rows_logits + (size_t)j * V : (j == 0 ? r.saved_logits : r.rows_logits + (size_t)(j - 1) * V);
+  };
+  auto passes = [&](int j) -> bool {
+    if (r.mode != SPECDEC_RELAXED) return d[j] == v(j);
+    if (d[j] < 0 || d[j] >= V) return false;
+    const float* z = row(j);
+    const float gap = z[v(j)] - z[d[j]];   // in fp32, as the logits are stored
+    return gap <= r.relax_delta;
+  };
   int m = 0;
-  while (m < k && d[m] == v(m)) ++m;
+  while (m < k && passes(m)) ++m;
   const bool emit_c = (m < k) || r.bonus;
   int n = st->n_committed;
   int32_t* toks = reinterpret_cast<int32_t*>(st + 1);
@@ -116,6 +128,7 @@ __global__ void accept_greedy_kernel(RoundDev r) {
     st->last_tok = d[k - 1];
     st->saved_argmax = r.rows_argmax[k - 1];   // rows[k-1] becomes saved_next, no repair
     st->saved_lse = r.rows_lse[k - 1];
+    r.flags[kFlagCopySaved] = 1;
   }
   st->n_committed = n;
   st->m_last = m;
@@ -267,10 +280,11 @@ __device__ __forceinline__ T block_reduce_256(T v, T* sh, bool is_max) {
   return r;
 }
 
-// Weight modes of the sampler.
-enum { kWDraft = 0, kWResidual = 1, kWTarget = 2 };
+// Weight modes of the sampler (kWNone: the round draws no last token).
+enum { kWDraft = 0, kWResidual = 1, kWTarget = 2, kWNone = 3 };
 
-// Noisy self-draft, step j: x = z + noise[n0 + j] into q_logits[j]; slice stats.
+// Noisy self-draft, step j: x = z + noise[n0 + j] into q_logits[j]; slice
+// stats of x / T.
 __global__ __launch_bounds__(kSliceThreads) void draft_stats_kernel(RoundDev r, const float* __restrict__ z, int j) {
   if (r.flags[kFlagOpen] == 0) return;
   __shared__ float shf[kSliceThreads];
@@ -287,8 +301,9 @@ __global__ __launch_bounds__(kSliceThreads) void draft_stats_kernel(RoundDev r, 
     const int i = sl * kSliceElems + e * kSliceThreads + threadIdx.x;
     xv[e] = -INFINITY;
     if (i < V) {
-      xv[e] = z[i] + nz[i];
-      qz[i] = xv[e];
+      const float x = z[i] + nz[i];
+      qz[i] = x;
+      xv[e] = x * r.inv_t;
     }
     mx = fmaxf(mx, xv[e]);
   }
@@ -300,58 +315,108 @@ __global__ __launch_bounds__(kSliceThreads) void draft_stats_kernel(RoundDev r, 
   if (threadIdx.x == 0) { r.smax[sl] = mx; r.ssum[sl] = se; }
 }
 
-// log-sum-exp of a row from its slice stats (slice order; same value in every workgroup).
-__device__ float combine_lse(const RoundDev& r, int S, float* shf) {
+// log-sum-exp of a row from its S slice stats (slice order; same value in every workgroup).
+__device__ float combine_lse(const float* smax, const float* ssum, int S, float* shf) {
   float mx = -INFINITY;
-  for (int s2 = threadIdx.x; s2 < S; s2 += kSliceThreads) mx = fmaxf(mx, r.smax[s2]);
+  for (int s2 = threadIdx.x; s2 < S; s2 += kSliceThreads) mx = fmaxf(mx, smax[s2]);
   mx = block_reduce_256(mx, shf, true);
   float l = 0.f;
-  for (int s2 = threadIdx.x; s2 < S; s2 += kSliceThreads) l += r.ssum[s2] * expf(r.smax[s2] - mx);
+  for (int s2 = threadIdx.x; s2 < S; s2 += kSliceThreads) l += ssum[s2] * expf(smax[s2] - mx);
   l = block_reduce_256(l, shf, false);
   return mx + logf(l);
 }
 
-// The sampling weight of entry i for the current mode.
+// Tempered target rows (temperature != 1): slice stats of z / T for row 0
+// (saved_next) and rows 1..k (the verify rows), then each row's log-sum-exp.
+__global__ __launch_bounds__(kSliceThreads) void tempered_stats_kernel(RoundDev r) {
+  if (r.flags[kFlagOpen] == 0) return;
+  __shared__ float shf[kSliceThreads];
+  const int V = r.V, sl = blockIdx.x, row = blockIdx.y, S = gridDim.x;
+  const float* z = row == 0 ? r.saved_logits : r.rows_logits + (size_t)(row - 1) * V;
+  float xv[kPerThread];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = sl * kSliceElems + e * kSliceThreads + threadIdx.x;
+    xv[e] = i < V ? z[i] * r.inv_t : -INFINITY;
+    mx = fmaxf(mx, xv[e]);
+  }
+  mx = block_reduce_256(mx, shf, true);
+  float se = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) se += (xv[e] == -INFINITY) ? 0.f : expf(xv[e] - mx);
+  se = block_reduce_256(se, shf, false);
+  if (threadIdx.x == 0) { r.tsmax[row * S + sl] = mx; r.tssum[row * S + sl] = se; }
+}
+
+__global__ __launch_bounds__(kSliceThreads) void tempered_lse_kernel(RoundDev r, int S) {
+  if (r.flags[kFlagOpen] == 0) return;
+  __shared__ float shf[kSliceThreads];
+  const int row = blockIdx.x;
+  const float l = combine_lse(r.tsmax + row * S, r.tssum + row * S, S, shf);
+  if (threadIdx.x == 0) r.t_lse[row] = l;
+}
+
+// The sampling weight of entry i for the current mode, as an fp32 value
+// (every kernel that needs it computes it the same way).
 struct SampleRows {
   const float* lp; float lp_lse;   // target row (residual / bonus)
   const float* lq; float lq_lse;   // draft row (draft sample / residual)
+  float inv_t;                     // 1 / temperature
+  uint64_t thresh;                 // truncation: entries whose key is below are dropped (0: none)
   int mode;
 };
+__device__ __forceinline__ float raw_weight(const SampleRows& w, int i) {
+  if (w.mode == kWDraft) return expf(w.lq[i] * w.inv_t - w.lq_lse);
+  if (w.mode == kWTarget) return expf(w.lp[i] * w.inv_t - w.lp_lse);
+  return fmaxf(0.f, expf(w.lp[i] * w.inv_t - w.lp_lse) - expf(w.lq[i] * w.inv_t - w.lq_lse));
+}
+__device__ __forceinline__ uint64_t trunc_key(float wv, int i) {
+  return ((uint64_t)__float_as_uint(wv) << kKeyIndexBits) | (uint64_t)((1 << kKeyIndexBits) - 1 - i);
+}
 __device__ __forceinline__ double sample_weight(const SampleRows& w, int i) {
-  if (w.mode == kWDraft) return (double)expf(w.lq[i] - w.lq_lse);
-  if (w.mode == kWTarget) return (double)expf(w.lp[i] - w.lp_lse);
-  return (double)fmaxf(0.f, expf(w.lp[i] - w.lp_lse) - expf(w.lq[i] - w.lq_lse));
+  const float v = raw_weight(w, i);
+  if (w.thresh != 0 && trunc_key(v, i) < w.thresh) return 0.0;
+  return (double)v;
 }
 
-__device__ SampleRows accept_rows(const RoundDev& r, int m, int mode) {
+// The accept step's sampling rows for accepted count m and weight mode:
+// target row m (saved_next for m = 0), draft row m (residual only).
+__device__ SampleRows accept_rows(const RoundDev& r, int m, int mode, uint64_t thresh) {
   const specdec_round_state* st = r.state;
+  const bool tempered = r.inv_t != 1.0f;
   SampleRows w;
   w.lp = m == 0 ? r.saved_logits : r.rows_logits + (size_t)(m - 1) * r.V;
-  w.lp_lse = m == 0 ? st->saved_lse : r.rows_lse[m - 1];
+  w.lp_lse = tempered ? r.t_lse[m] : (m == 0 ? st->saved_lse : r.rows_lse[m - 1]);
   w.lq = r.q_logits + (size_t)(m < r.k ? m : 0) * r.V;
   w.lq_lse = r.q_lse[m < r.k ? m : 0];
+  w.inv_t = r.inv_t;
+  w.thresh = thresh;
   w.mode = mode;
   return w;
 }
 
 // Slice sums of the sampling weights.  j >= 0: draft step j (log-sum-exp of
 // the noisy row first, stored in q_lse[j]); j < 0: the accept step's row and
-// mode from sctl.
-__global__ __launch_bounds__(kSliceThreads) void slice_weights_kernel(RoundDev r, int j) {
+// mode from sctl, truncated when `masked`.
+__global__ __launch_bounds__(kSliceThreads) void slice_weights_kernel(RoundDev r, int j, int masked) {
   if (r.flags[kFlagOpen] == 0) return;
   __shared__ float shf[kSliceThreads];
   __shared__ double shd[kSliceThreads];
   const int V = r.V, sl = blockIdx.x;
   SampleRows w;
   if (j >= 0) {
-    const float lse = combine_lse(r, gridDim.x, shf);
+    const float lse = combine_lse(r.smax, r.ssum, gridDim.x, shf);
     if (sl == 0 && threadIdx.x == 0) r.q_lse[j] = lse;
     w.lq = r.q_logits + (size_t)j * V;
     w.lq_lse = lse;
     w.lp = nullptr; w.lp_lse = 0.f;
+    w.inv_t = r.inv_t;
+    w.thresh = 0;
     w.mode = kWDraft;
   } else {
-    w = accept_rows(r, r.sctl[0], r.sctl[1]);
+    if (r.sctl[1] == kWNone) return;
+    w = accept_rows(r, r.sctl[0], r.sctl[1], masked ? r.trunc->thresh : 0);
   }
   double acc = 0.0;
 #pragma unroll
@@ -446,6 +511,8 @@ __global__ __launch_bounds__(kSliceThreads) void draft_select_kernel(RoundDev r,
   w.lq = r.q_logits + (size_t)j * r.V;
   w.lq_lse = r.q_lse[j];
   w.lp = nullptr; w.lp_lse = 0.f;
+  w.inv_t = r.inv_t;
+  w.thresh = 0;
   w.mode = kWDraft;
   const float u = philox_uniform(r.seed, (uint64_t)r.state->round, (uint64_t)j, 0);
   const int tok = select_index(r, w, n_slices(r.V), u, -1.0, shd, shi);
@@ -453,44 +520,164 @@ __global__ __launch_bounds__(kSliceThreads) void draft_select_kernel(RoundDev r,
 }
 
 // Modified rejection sampling over the k drafts of the round (schedule A):
-// p_1 = softmax(saved_next), p_(j+1) = softmax(rows[j]), q_j as drawn.
+// p_1 = softmax(saved_next / T), p_(j+1) = softmax(rows[j] / T), q_j as drawn.
 // Decides m (accept while u_j < min(1, p_j(d_j) / (q_j(d_j) + 1e-10))) and
-// which row the resample uses: the residual of row m, or the bonus row.
+// which row the last token is drawn from: the residual of row m, the bonus
+// row, or none (full acceptance without the bonus).
 __global__ void accept_decide_kernel(RoundDev r) {
   if (r.flags[kFlagOpen] == 0) return;
   if (threadIdx.x != 0) return;
   specdec_round_state* st = r.state;
   const int k = r.k, V = r.V;
+  const bool tempered = r.inv_t != 1.0f;
   int m = 0;
   for (; m < k; ++m) {
     const float* lp = m == 0 ? r.saved_logits : r.rows_logits + (size_t)(m - 1) * V;
-    const float lp_lse = m == 0 ? st->saved_lse : r.rows_lse[m - 1];
+    const float lp_lse = tempered ? r.t_lse[m] : (m == 0 ? st->saved_lse : r.rows_lse[m - 1]);
     const float* lq = r.q_logits + (size_t)m * V;
     const int x = r.block[m];
-    const float px = expf(lp[x] - lp_lse), qx = expf(lq[x] - r.q_lse[m]);
+    const float px = expf(lp[x] * r.inv_t - lp_lse), qx = expf(lq[x] * r.inv_t - r.q_lse[m]);
     const float ratio = fminf(1.0f, px / (qx + 1e-10f));
     const float ua = philox_uniform(r.seed, (uint64_t)st->round, (uint64_t)m, 1);
     if (r.dbg) { r.dbg[2 * m] = ratio; r.dbg[2 * m + 1] = ua; }
     if (!(ua < ratio)) break;
   }
+  const int mode = m < k ? kWResidual : (r.bonus ? kWTarget : kWNone);
   r.sctl[0] = m;
-  r.sctl[1] = m < k ? kWResidual : kWTarget;
+  r.sctl[1] = mode;
+  TruncState* ts = r.trunc;
+  ts->prefix = 0;
+  ts->need = 0;
+  ts->target = 0.0;
+  ts->kthresh = 0;
+  ts->thresh = 0;
+  ts->active = mode != kWNone;
+}
+
+// Truncation, first step: the untruncated total decides the residual's
+// fallback to p (mass <= 1e-10) before anything is cut.
+__global__ void trunc_begin_kernel(RoundDev r, int S) {
+  if (r.flags[kFlagOpen] == 0) return;
+  if (threadIdx.x != 0 || r.sctl[1] == kWNone) return;
+  double total = 0.0;
+  for (int s2 = 0; s2 < S; ++s2) total += r.sw[s2];
+  if (r.sctl[1] == kWResidual && !(total > 1e-10)) r.sctl[1] = kWTarget;
+}
+
+// Radix-select pass `pass` of stage `stage` (0: top-k by count, 1: top-p by
+// mass): per-slice histograms of the current key digit over the candidates
+// (keys that match the resolved prefix; in the top-p stage also at or above
+// the top-k threshold).  Each bin's mass is its thread's sum over the
+// slice's entries in index order.
+__global__ __launch_bounds__(kSliceThreads) void trunc_hist_kernel(RoundDev r, int pass, int stage) {
+  if (r.flags[kFlagOpen] == 0 || r.trunc->active == 0) return;
+  __shared__ uint16_t dig[kSliceElems];
+  __shared__ float wv[kSliceElems];
+  const int V = r.V, sl = blockIdx.x, t = threadIdx.x;
+  const TruncState& ts = *r.trunc;
+  const SampleRows w = accept_rows(r, r.sctl[0], r.sctl[1], 0);
+  const int shift = 8 * (kTruncPasses - 1 - pass), hi = shift + 8;
+  const uint64_t prefix = ts.prefix, kth = stage == 1 ? ts.kthresh : 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int li = e * kSliceThreads + t, i = sl * kSliceElems + li;
+    uint16_t d = 0xFFFF;
+    float v = 0.f;
+    if (i < V) {
+      v = raw_weight(w, i);
+      const uint64_t key = trunc_key(v, i);
+      if ((key >> hi) == (prefix >> hi) && key >= kth) d = (uint16_t)((key >> shift) & 0xFF);
+    }
+    dig[li] = d;
+    wv[li] = v;
+  }
+  __syncthreads();
+  int cnt = 0;
+  double mass = 0.0;
+  for (int li = 0; li < kSliceElems; ++li)
+    if (dig[li] == t) { ++cnt; mass += (double)wv[li]; }
+  r.hcnt[sl * kTruncBins + t] = cnt;
+  r.hmass[sl * kTruncBins + t] = mass;
+}
+
+// Radix-select resolve: bins summed over slices in slice order; the digit
+// whose bin holds the top_k-th largest key (stage 0) or where the running
+// mass from the top reaches top_p of the candidates' mass (stage 1).
+__global__ __launch_bounds__(kTruncBins) void trunc_resolve_kernel(RoundDev r, int pass, int stage, int S) {
+  if (r.flags[kFlagOpen] == 0 || r.trunc->active == 0) return;
+  __shared__ long long bc[kTruncBins];
+  __shared__ double bm[kTruncBins];
+  const int b = threadIdx.x;
+  long long c = 0;
+  double ms = 0.0;
+  for (int s2 = 0; s2 < S; ++s2) {
+    c += r.hcnt[s2 * kTruncBins + b];
+    ms += r.hmass[s2 * kTruncBins + b];
+  }
+  bc[b] = c;
+  bm[b] = ms;
+  __syncthreads();
+  if (b != 0) return;
+  TruncState& ts = *r.trunc;
+  const int shift = 8 * (kTruncPasses - 1 - pass);
+  if (pass == 0) {
+    ts.prefix = 0;
+    if (stage == 0) {
+      ts.need = r.top_k;
+    } else {
+      double total = 0.0;
+      for (int i = 0; i < kTruncBins; ++i) total += bm[i];
+      ts.target = (double)r.top_p * total;
+    }
+  }
+  int digit = -1;
+  if (stage == 0) {
+    long long cum = 0;
+    for (int i = kTruncBins - 1; i >= 0; --i) {
+      if (cum + bc[i] >= ts.need) { digit = i; ts.need -= cum; break; }
+      cum += bc[i];
+    }
+  } else {
+    double cum = 0.0;
+    for (int i = kTruncBins - 1; i >= 0; --i) {
+      if (bc[i] > 0 && cum + bm[i] >= ts.target) { digit = i; ts.target -= cum; break; }
+      cum += bm[i];
+    }
+  }
+  if (digit < 0) {   // rounding kept the running mass below the target: keep every candidate
+    for (int i = 0; i < kTruncBins; ++i)
+      if (bc[i] > 0) { digit = i; break; }
+    if (stage == 1) ts.target = 0.0;
+  }
+  if (digit < 0) digit = 0;
+  ts.prefix |= (uint64_t)digit << shift;
+  if (pass == kTruncPasses - 1) {
+    ts.thresh = ts.prefix;
+    if (stage == 0) ts.kthresh = ts.prefix;
+  }
 }
 
 // The resample (or bonus) and the commit: tokens, lengths, repair token.
-__global__ __launch_bounds__(kSliceThreads) void accept_select_kernel(RoundDev r) {
+__global__ __launch_bounds__(kSliceThreads) void accept_select_kernel(RoundDev r, int truncated) {
   if (r.flags[kFlagOpen] == 0) return;
   __shared__ double shd[kSliceThreads];
   __shared__ int shi[kSliceThreads];
   __shared__ double total;
   specdec_round_state* st = r.state;
-  const int k = r.k, m = r.sctl[0];
+  const int k = r.k, m = r.sctl[0], mode = r.sctl[1];
   const float ur = philox_uniform(r.seed, (uint64_t)st->round, 0, 2);
-  int c = select_index(r, accept_rows(r, m, r.sctl[1]), n_slices(r.V), ur, r.sctl[1] == kWResidual ? 1e-10 : -1.0,
-                       shd, shi);
-  if (c < 0) {   // residual mass <= 1e-10: sample p of that row (one workgroup, rare)
-    const SampleRows wp = accept_rows(r, m, kWTarget);
-    c = block_sample<kSliceThreads>([&](int i) { return sample_weight(wp, i); }, r.V, ur, shd, &total);
+  int c = -1;
+  if (mode != kWNone) {
+    if (truncated) {
+      c = select_index(r, accept_rows(r, m, mode, r.trunc->thresh), n_slices(r.V), ur, -1.0, shd, shi);
+    } else {
+      c = select_index(r, accept_rows(r, m, mode, 0), n_slices(r.V), ur, mode == kWResidual ? 1e-10 : -1.0, shd,
+                       shi);
+      if (c < 0) {   // residual mass <= 1e-10: sample p of that row (one workgroup, rare)
+        const SampleRows wp = accept_rows(r, m, kWTarget, 0);
+        c = block_sample<kSliceThreads>([&](int i) { return sample_weight(wp, i); }, r.V, ur, shd, &total);
+      }
+    }
   }
   if (threadIdx.x == 0) {
     int n = st->n_committed;
@@ -499,18 +686,35 @@ __global__ __launch_bounds__(kSliceThreads) void accept_select_kernel(RoundDev r
       if (n < st->cap) toks[n] = r.block[j]; else raise_error(r.err, kErrOutput);
       ++n;
     }
-    if (n < st->cap) toks[n] = c; else raise_error(r.err, kErrOutput);
-    ++n;
+    if (mode != kWNone) {
+      if (n < st->cap) toks[n] = c; else raise_error(r.err, kErrOutput);
+      ++n;
+      st->last_tok = c;
+      *r.t_len -= (k - m);
+      r.flags[kFlagRepair] = 1;
+    } else {
+      // all k drafts kept, no bonus: the cache keeps them, the last verify
+      // row becomes saved_next and no repair forward runs
+      st->last_tok = r.block[k - 1];
+      st->saved_argmax = r.rows_argmax[k - 1];
+      st->saved_lse = r.rows_lse[k - 1];
+      r.flags[kFlagRepair] = 0;
+      r.flags[kFlagCopySaved] = 1;
+    }
     st->n_committed = n;
     st->m_last = m;
     st->accepted_total += m;
-    st->last_tok = c;
     st->round += 1;
-    *r.t_len -= (k - m);
-    r.flags[kFlagRepair] = 1;
     r.repair_tok[0] = c;
     if (r.dbg) { r.dbg[2 * kMaxK] = ur; r.dbg[2 * kMaxK + 1] = __int_as_float(m); }
   }
+}
+
+// saved_next = the last verify row (a fully accepted round without bonus).
+__global__ void copy_saved_kernel(RoundDev r) {
+  if (r.flags[kFlagOpen] == 0 || r.flags[kFlagCopySaved] == 0) return;
+  const float* src = r.rows_logits + (size_t)(r.k - 1) * r.V;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < r.V; i += gridDim.x * blockDim.x) r.saved_logits[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -522,17 +726,33 @@ hipError_t launch_repair_done(const RoundDev& r, hipStream_t s) { repair_done_ke
 hipError_t launch_rewind(const RoundDev& r, int32_t* len, int n, hipStream_t s) { rewind_kernel<<<1, 64, 0, s>>>(r, len, n); return hipGetLastError(); }
 hipError_t launch_snapshot(const RoundDev& r, const int32_t* last, hipStream_t s) { snapshot_kernel<<<64, 256, 0, s>>>(r, last); return hipGetLastError(); }
 hipError_t launch_reset(const RoundDev& r, int32_t n_target, hipStream_t s) { reset_kernel<<<64, 256, 0, s>>>(r, n_target); return hipGetLastError(); }
+hipError_t launch_copy_saved(const RoundDev& r, hipStream_t s) { copy_saved_kernel<<<64, 256, 0, s>>>(r); return hipGetLastError(); }
 hipError_t launch_draft_sample(const RoundDev& r, const float* z, int j, hipStream_t s) {
   const int S = n_slices(r.V);
   draft_stats_kernel<<<S, kSliceThreads, 0, s>>>(r, z, j);
-  slice_weights_kernel<<<S, kSliceThreads, 0, s>>>(r, j);
+  slice_weights_kernel<<<S, kSliceThreads, 0, s>>>(r, j, 0);
   draft_select_kernel<<<1, kSliceThreads, 0, s>>>(r, j);
   return hipGetLastError();
 }
 hipError_t launch_accept_stochastic(const RoundDev& r, hipStream_t s) {
+  const int S = n_slices(r.V);
+  if (r.inv_t != 1.0f) {
+    tempered_stats_kernel<<<dim3(S, r.k + 1), kSliceThreads, 0, s>>>(r);
+    tempered_lse_kernel<<<r.k + 1, kSliceThreads, 0, s>>>(r, S);
+  }
   accept_decide_kernel<<<1, 64, 0, s>>>(r);
-  slice_weights_kernel<<<n_slices(r.V), kSliceThreads, 0, s>>>(r, -1);
-  accept_select_kernel<<<1, kSliceThreads, 0, s>>>(r);
+  slice_weights_kernel<<<S, kSliceThreads, 0, s>>>(r, -1, 0);
+  const bool tk = r.top_k > 0 && r.top_k < r.V, tp = r.top_p < 1.0f;
+  if (tk || tp) {
+    trunc_begin_kernel<<<1, 64, 0, s>>>(r, S);
+    for (int stage = tk ? 0 : 1; stage <= (tp ? 1 : 0); ++stage)
+      for (int pass = 0; pass < kTruncPasses; ++pass) {
+        trunc_hist_kernel<<<S, kSliceThreads, 0, s>>>(r, pass, stage);
+        trunc_resolve_kernel<<<1, kTruncBins, 0, s>>>(r, pass, stage, S);
+      }
+    slice_weights_kernel<<<S, kSliceThreads, 0, s>>>(r, -1, 1);
+  }
+  accept_select_kernel<<<1, kSliceThreads, 0, s>>>(r, (tk || tp) ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecdec
 OK, EINVAL, ECAPACITY, ESHAPE, EHIP, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 DERR_CAPACITY, DERR_TRIM, DERR_NONFINITE, DERR_TABLE, DERR_OUTPUT, DERR_SYNC = 1, 2, 4, 8, 16, 32
 W_BF16, W_Q4G64 = 0, 1
-GREEDY, STOCHASTIC = 0, 1
+GREEDY, STOCHASTIC, RELAXED = 0, 1, 2
 SCHEDULE_A, SCHEDULE_B = 0, 1
 DRAFT_TABLE, DRAFT_MODEL, DRAFT_NOISY_SELF, DRAFT_Q4_SELF = 0, 1, 2, 3
 MAX_ROWS = 32
@@ -63,7 +63,8 @@ class RoundDesc(C.Structure):
                 ("philox_seed", C.c_uint64), ("d_state", C.c_void_p), ("d_ws", C.c_void_p),
                 ("ws_bytes", C.c_size_t), ("d_draft_ws", C.c_void_p), ("draft_ws_bytes", C.c_size_t),
                 ("d_round_ws", C.c_void_p), ("round_ws_bytes", C.c_size_t), ("state_cap", C.c_int32),
-                ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int32)]
+                ("events", C.POINTER(C.c_void_p)), ("n_events", C.c_int32), ("temperature", C.c_float),
+                ("top_k", C.c_int32), ("top_p", C.c_float), ("relax_delta", C.c_float)]
 
 
 def load_library(path: str = _LIB_PATH) -> C.CDLL:
@@ -280,7 +281,8 @@ class Round:
     def __init__(self, target: Model, k: int, *, mode=GREEDY, bonus=True, schedule=SCHEDULE_A,
                  draft_source=DRAFT_TABLE, table: np.ndarray | None = None, draft: Model | None = None,
                  noise: np.ndarray | None = None, seed: int = 3, max_len: int, cap: int = 1024, device="cuda",
-                 events=None, n_events: int = 0):
+                 events=None, n_events: int = 0, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                 relax_delta: float = 0.0):
         L = lib()
         self.target, self.draft, self.k = target, draft, k
         self.schedule, self.mode, self.draft_source = schedule, mode, draft_source
@@ -316,6 +318,7 @@ class Round:
             d.d_draft_ws, d.draft_ws_bytes = self.dws.mem.data_ptr(), self.dws.nbytes
         d.d_round_ws, d.round_ws_bytes = self.rws.data_ptr(), self.rws.numel()
         d.state_cap = cap
+        d.temperature, d.top_k, d.top_p, d.relax_delta = temperature, top_k, top_p, relax_delta
         if events is not None:
             d.events = C.cast(events, C.POINTER(C.c_void_p))
             d.n_events = n_events

@@ -67,7 +67,13 @@ enum {
 };
 
 enum { SPECDEC_W_BF16 = 0, SPECDEC_W_Q4G64 = 1 };
-enum { SPECDEC_GREEDY = 0, SPECDEC_STOCHASTIC = 1 };
+/* Acceptance rules.  GREEDY: a draft passes when it is the target's argmax
+ * ("SpecDec-Context-Scaling 项目解读", sections 3 and 3.1).  STOCHASTIC:
+ * modified rejection sampling (wmrh.cn explainer, section 2.2).  RELAXED: a
+ * draft passes when its target logit trails the target's top-1 logit by at
+ * most relax_delta (same SpecDec page, section 7.2; lossy: the output is no
+ * longer the target's greedy decode). */
+enum { SPECDEC_GREEDY = 0, SPECDEC_STOCHASTIC = 1, SPECDEC_RELAXED = 2 };
 enum { SPECDEC_SCHEDULE_A = 0, SPECDEC_SCHEDULE_B = 1 };
 enum { SPECDEC_DRAFT_TABLE = 0, SPECDEC_DRAFT_MODEL = 1, SPECDEC_DRAFT_NOISY_SELF = 2, SPECDEC_DRAFT_Q4_SELF = 3 };
 
@@ -201,8 +207,10 @@ typedef struct {
   const specdec_model* draft;   /* DRAFT_MODEL: independent draft; DRAFT_Q4_SELF: substitute draft; else NULL */
   specdec_cache* draft_cache;   /* DRAFT_MODEL only (own cache); NULL otherwise */
   int32_t k;                    /* drafts per round, 1..SPECDEC_MAX_K (DRAFT_Q4_SELF: the depth D) */
-  int32_t mode;                 /* SPECDEC_GREEDY | SPECDEC_STOCHASTIC */
-  int32_t bonus;                /* 1: bonus token on full acceptance */
+  int32_t mode;                 /* SPECDEC_GREEDY | SPECDEC_STOCHASTIC | SPECDEC_RELAXED */
+  int32_t bonus;                /* 1: bonus token on full acceptance; 0: a fully accepted round
+                                   commits the k drafts only, and the last verify row becomes the
+                                   next round's saved_next (schedule A only) */
   int32_t schedule;             /* SPECDEC_SCHEDULE_A | SPECDEC_SCHEDULE_B */
   int32_t draft_source;         /* SPECDEC_DRAFT_* */
   const int32_t* d_draft_table; /* TABLE / MODEL: drafts by generated index, int32 [table_len] */
@@ -222,6 +230,20 @@ typedef struct {
   int32_t n_events;             /* ring size (>= 5); each round records 5 events in order:
                                    start, after draft provision, after verify, after accept,
                                    after repair; round i uses entries 5*i .. 5*i+4 modulo the ring */
+  /* STOCHASTIC only (wmrh.cn explainer, sections 3.3, 4.2 and 8): draft and
+   * target distributions are softmax(logits / temperature); the accept test
+   * and the residual run on these untruncated distributions; top_k / top_p
+   * truncate only the distribution the round's last token is drawn from (the
+   * residual after a rejection, the bonus row after full acceptance): entries
+   * ranked by weight (ties: lower index first), the first top_k kept, then
+   * the shortest leading run of those holding top_p of their mass.
+   * temperature > 0 (1: plain softmax); top_k 0 = off, else 1..vocab;
+   * top_p in (0, 1], 1 = off.  Truncation needs vocab <= 2^18
+   * (SPECDEC_EUNSUPPORTED beyond). */
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  float relax_delta;            /* RELAXED only: the logit gap to the top-1 a draft may have (>= 0) */
 } specdec_round_desc;
 
 int specdec_round_state_bytes(int32_t cap, size_t* bytes);

@@ -1,4 +1,6 @@
-"""Oracle acceptance rules: greedy longest prefix and modified rejection sampling.
+"""Oracle acceptance rules: greedy longest prefix, the relaxed (Delta-logit)
+variant, and modified rejection sampling with temperature and post-acceptance
+truncation.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -11,13 +13,30 @@ the target's own token at position m+1; on full acceptance the bonus token
 comes from rows[k-1] (the "bonus-aware" variant of section 3; the standard
 variant without bonus is a flag).
 
-Stochastic rule, the wmrh.cn explainer section 2.2 and "mini-infer系统实战-13"
-(smarter.xin), section on modified rejection sampling: accept a draft x with
-probability min(1, p(x)/q(x)); on the first rejection resample from
-norm(max(0, p - q)) and stop; if all k pass, sample a bonus token from the
-distribution of the last verify row.  The guards follow the mini-infer page's
-sampler: q(x) + 1e-10 in the ratio, a strict ``u < ratio`` test, and a
-fallback to p when the residual mass is <= 1e-10.
+Relaxed rule, same page, section 7.2: a draft passes when its target logit
+is within Delta of the target's top-1 logit at that position.  The rest of
+the round (first failure -> the target's own token, bonus on full
+acceptance) is the greedy rule's.  The output is no longer the target's
+greedy decode.
+
+Stochastic rule, the wmrh.cn explainer, section 2.2: a draft x drawn from q
+is kept with probability min(1, p(x) / q(x)); at the first rejection a token
+is drawn from norm(max(0, p - q)) and the round stops; when all k drafts are
+kept a bonus token is drawn from the last verify row.  Written here as
+vectors: the k ratios at once, then the first index whose uniform is not
+below its ratio.  Numerical guards are this project's choices: 1e-10 added
+to q(x) in the ratio (a draft with q(x) = 0 cannot have been drawn, so only
+rounding reaches it), a strict ``u < ratio`` test, and p itself as the
+resampling distribution when the residual mass is <= 1e-10 (rejection then
+happened through rounding alone, where p ~ q).
+
+Temperature and truncation, the wmrh.cn explainer, sections 3.3, 4.2 and 8:
+draft and target use the same temperature T (p = softmax(z / T)); the
+accept/reject step runs on the tempered, untruncated distributions; top-k /
+top-p truncation is applied afterwards, to the distribution the round's last
+token is drawn from (the residual on a rejection, the bonus row on full
+acceptance).  With top_k = 0 (off) and top_p = 1 the round's output follows
+the tempered target distribution exactly.
 
 Sampling is by inverse CDF: the smallest index i whose running sum (float64,
 index order) exceeds u times the total.  Argmax ties go to the lowest index.
@@ -68,8 +87,32 @@ def greedy_accept_logits(saved_next: np.ndarray, rows: np.ndarray, drafts, bonus
     return greedy_accept(v, drafts, bonus)
 
 
-def softmax(logits: np.ndarray) -> np.ndarray:
-    x = np.asarray(logits, dtype=np.float64)
+def relaxed_accept(logit_rows, drafts, delta: float, bonus: bool = True):
+    """Delta-logit relaxed acceptance.
+
+    logit_rows: k+1 target logit rows, row j at draft j's position, row k the
+    bonus position.  Draft j passes when max(row_j) - row_j[d_j] <= delta,
+    evaluated in the rows' own floating-point type.  Returns (m, committed).
+    """
+    drafts = [int(d) for d in drafts]
+    k = len(drafts)
+    if len(logit_rows) != k + 1:
+        raise ValueError("need k+1 logit rows")
+    m = 0
+    while m < k:
+        row = np.asarray(logit_rows[m])
+        gap = row[argmax_lowest(row)] - row[drafts[m]]
+        if not gap <= row.dtype.type(delta):
+            break
+        m += 1
+    if m < k:
+        return m, drafts[:m] + [argmax_lowest(logit_rows[m])]
+    return k, drafts + ([argmax_lowest(logit_rows[k])] if bonus else [])
+
+
+def softmax(logits: np.ndarray, temperature: float = 1.0) -> np.ndarray:
+    """softmax(z / T) in float64."""
+    x = np.asarray(logits, dtype=np.float64) / float(temperature)
     e = np.exp(x - x.max())
     return e / e.sum()
 
@@ -81,6 +124,36 @@ def sample_inverse_cdf(weights: np.ndarray, u: float) -> int:
     return min(i, c.shape[0] - 1)
 
 
+def cdf_margin(weights: np.ndarray, u: float, i: int) -> float:
+    """How far u * total lies from the CDF steps that bound index i, relative to the total
+    (a sample whose margin is small may flip under a small change of the weights)."""
+    c = np.cumsum(np.asarray(weights, dtype=np.float64))
+    t = u * c[-1]
+    lo = c[i - 1] if i > 0 else 0.0
+    return float(min(abs(t - lo), abs(t - c[i])) / c[-1])
+
+
+def truncate(weights: np.ndarray, top_k: int = 0, top_p: float = 1.0) -> np.ndarray:
+    """Top-k, then top-p, truncation of non-negative weights (not renormalised).
+
+    Entries are ranked by weight, larger first, ties by lower index.  top_k
+    keeps the first top_k of that order (0: all).  top_p then keeps the
+    shortest leading run of the survivors whose mass reaches top_p times the
+    survivors' mass (1: all).  Dropped entries get weight 0.
+    """
+    w = np.asarray(weights, dtype=np.float64)
+    order = np.lexsort((np.arange(w.shape[0]), -w))      # weight desc, index asc
+    n = w.shape[0] if top_k <= 0 else min(int(top_k), w.shape[0])
+    keep = order[:n]
+    if top_p < 1.0:
+        c = np.cumsum(w[keep])
+        n2 = int(np.searchsorted(c, top_p * c[-1], side="left")) + 1
+        keep = keep[:min(n2, keep.shape[0])]
+    out = np.zeros_like(w)
+    out[keep] = w[keep]
+    return out
+
+
 def accept_ratio(p: np.ndarray, q: np.ndarray, x: int) -> float:
     return min(1.0, float(p[x]) / (float(q[x]) + RATIO_EPS))
 
@@ -89,31 +162,46 @@ def residual(p: np.ndarray, q: np.ndarray) -> np.ndarray:
     return np.maximum(0.0, np.asarray(p, np.float64) - np.asarray(q, np.float64))
 
 
-def stochastic_accept(p_rows, q_rows, drafts, u_accept, u_resample: float, bonus: bool = True):
+def stochastic_accept(p_rows, q_rows, drafts, u_accept, u_resample: float, bonus: bool = True,
+                      top_k: int = 0, top_p: float = 1.0):
     """Modified rejection sampling over one round.
 
     p_rows: k+1 target distributions; p_rows[j] is the target's distribution
     at draft j's position, p_rows[k] the bonus distribution.
     q_rows: k draft distributions (q_rows[j] is what drafts[j] was drawn from).
     u_accept: k uniforms for the accept tests; u_resample: one uniform for the
-    residual (or bonus) sample.
-    Returns (m, committed, info) with info = per-draft ratios and the reason
-    the round stopped.
+    residual (or bonus) sample.  top_k / top_p truncate that last sample's
+    distribution only.
+    Returns (m, committed, info); info holds the ratios of the drafts examined,
+    the uniforms, the reason the round stopped, the residual mass and the
+    (truncated, unnormalised) weights the last token was drawn from.
     """
     drafts = [int(d) for d in drafts]
     k = len(drafts)
-    ratios = []
-    for j in range(k):
-        a = accept_ratio(p_rows[j], q_rows[j], drafts[j])
-        ratios.append(a)
-        if u_accept[j] < a:
-            continue
-        w = residual(p_rows[j], q_rows[j])
+    P = np.asarray(p_rows, dtype=np.float64)
+    Q = np.asarray(q_rows, dtype=np.float64)
+    if P.shape[0] != k + 1 or Q.shape[0] != k:
+        raise ValueError("need k+1 target rows and k draft rows")
+    j = np.arange(k)
+    p_d, q_d = P[j, drafts], Q[j, drafts]
+    ratios = np.minimum(1.0, p_d / (q_d + RATIO_EPS))
+    kept = np.asarray(u_accept, dtype=np.float64)[:k] < ratios
+    m = k if kept.all() else int(np.argmin(kept))          # first index that fails
+    info = {"ratios": [float(r) for r in ratios[:min(m + 1, k)]],
+            "u_accept": [float(u) for u in np.asarray(u_accept)[:k]], "u_resample": float(u_resample),
+            "sample_weights": None}
+    if m < k:
+        w = residual(P[m], Q[m])
         s = float(w.sum())
-        src = w if s > RESIDUAL_EPS else np.asarray(p_rows[j], np.float64)
+        full = w if s > RESIDUAL_EPS else P[m]
+        src = truncate(full, top_k, top_p)
         c = sample_inverse_cdf(src, u_resample)
-        return j, drafts[:j] + [c], {"ratios": ratios, "stop": "reject", "residual_mass": s}
+        info.update(stop="reject", residual_mass=s, sample_weights=src, source_weights=full)
+        return m, drafts[:m] + [c], info
     if not bonus:
-        return k, drafts, {"ratios": ratios, "stop": "full"}
-    c = sample_inverse_cdf(p_rows[k], u_resample)
-    return k, drafts + [c], {"ratios": ratios, "stop": "bonus"}
+        info.update(stop="full")
+        return k, drafts, info
+    src = truncate(P[k], top_k, top_p)
+    c = sample_inverse_cdf(src, u_resample)
+    info.update(stop="bonus", sample_weights=src, source_weights=P[k])
+    return k, drafts + [c], info

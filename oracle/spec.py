@@ -50,6 +50,7 @@ class SpecTrace:
     draft_calls: int = 0
     rounds: int = 0
     stops: list = field(default_factory=list)
+    margins: list = field(default_factory=list)      # stochastic: (accept, sample) closest calls per round
     cache: object = None        # target cache at the end of the run
     draft_cache: object = None  # independent draft's cache, if any
 
@@ -76,8 +77,13 @@ def ar_greedy(w: OracleWeights, prompt, n_new: int, chunk: int = 2048, max_len: 
 def spec_greedy(w: OracleWeights, prompt, n_new: int, k: int, table=None, schedule: str = "A",
                 bonus: bool = True, draft_w: OracleWeights | None = None,
                 q4_draft_w: OracleWeights | None = None, chunk: int = 2048, max_len: int | None = None,
-                check_invariant: bool = True) -> SpecTrace:
-    """Greedy speculative decoding, schedule A or B (see the module docstring)."""
+                check_invariant: bool = True, relax_delta: float | None = None) -> SpecTrace:
+    """Greedy speculative decoding, schedule A or B (see the module docstring).
+
+    relax_delta: None for the exact greedy rule, else the Delta of the relaxed
+    rule ("SpecDec-Context-Scaling 项目解读", section 7.2), which then decides
+    every round on the target's logit rows.
+    """
     prompt = np.asarray(prompt)
     P = prompt.shape[0]
     cap = max_len or (P + n_new + 2 * k + 2)
@@ -123,12 +129,15 @@ def spec_greedy(w: OracleWeights, prompt, n_new: int, k: int, table=None, schedu
         if schedule == "A":
             rows = forward(w, tc, drafts)
             tr.target_calls += 1
-            v = [acc.argmax_lowest(saved)] + [acc.argmax_lowest(r) for r in rows]
+            logit_rows = [saved] + list(rows)
         else:
             rows = forward(w, tc, [pending] + drafts)
             tr.target_calls += 1
-            v = [acc.argmax_lowest(r) for r in rows]
-        m, com = acc.greedy_accept(v, drafts, bonus)
+            logit_rows = list(rows)
+        if relax_delta is None:
+            m, com = acc.greedy_accept([acc.argmax_lowest(r) for r in logit_rows], drafts, bonus)
+        else:
+            m, com = acc.relaxed_accept(logit_rows, drafts, relax_delta, bonus)
         # ---- trim + repair ------------------------------------------------------
         if schedule == "A":
             if m < k or bonus:
@@ -162,9 +171,65 @@ def spec_greedy(w: OracleWeights, prompt, n_new: int, k: int, table=None, schedu
     return tr
 
 
+def draft_sample(q_logit_row, seed: int, rnd: int, slot: int, temperature: float = 1.0) -> int:
+    """The noisy self-draft's token for slot j of round rnd: drawn from
+    softmax(q_logit_row / T) by inverse CDF with the Philox uniform of
+    (round rnd, slot j, draft stream)."""
+    u = philox.uniform(seed, rnd, slot, philox.STREAM_DRAFT)
+    return acc.sample_inverse_cdf(acc.softmax(q_logit_row, temperature), u)
+
+
+def draft_samples(q_logits, seed: int, rnd: int, temperature: float = 1.0):
+    """draft_sample over the k draft logit rows of one round."""
+    return [draft_sample(z, seed, rnd, j, temperature) for j, z in enumerate(q_logits)]
+
+
+def round_uniforms(seed: int, rnd: int, k: int):
+    """The accept uniforms u_1..u_k and the resample / bonus uniform of round rnd."""
+    ua = [philox.uniform(seed, rnd, j, philox.STREAM_ACCEPT) for j in range(k)]
+    return ua, philox.uniform(seed, rnd, 0, philox.STREAM_RESAMPLE)
+
+
+def stochastic_round(saved, rows, q_logits, drafts, seed: int, rnd: int, bonus: bool = True,
+                     temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0, uniforms=None):
+    """One round of modified rejection sampling on given logits (schedule A).
+
+    saved: the target's logits at draft 1's position (saved_next, [V]);
+    rows: the k verify rows ([k, V]; rows[j] sits at draft j+2's position,
+    rows[k-1] is the bonus position); q_logits: the k draft logit rows the
+    drafts were drawn from; drafts: the k draft tokens.  The target rows are
+    p_1 = softmax(saved / T), p_(j+1) = softmax(rows[j] / T), the draft rows
+    q_j = softmax(q_logits[j] / T) (wmrh.cn explainer, sections 2.2 and 8).
+    uniforms: (u_accept[k], u_resample) to inject, else the Philox stream of
+    round rnd.  Returns stochastic_accept's (m, committed, info).
+    """
+    k = len(drafts)
+    rows = np.asarray(rows)
+    if rows.shape[0] != k or len(q_logits) != k:
+        raise ValueError("need k verify rows and k draft rows")
+    p_rows = [acc.softmax(saved, temperature)] + [acc.softmax(r, temperature) for r in rows]
+    q_rows = [acc.softmax(z, temperature) for z in q_logits]
+    ua, ur = uniforms if uniforms is not None else round_uniforms(seed, rnd, k)
+    return acc.stochastic_accept(p_rows, q_rows, drafts, ua, ur, bonus, top_k, top_p)
+
+
 def spec_stochastic(w: OracleWeights, prompt, n_new: int, k: int, noise: np.ndarray, seed: int,
-                    chunk: int = 2048, max_len: int | None = None) -> SpecTrace:
-    """Modified rejection sampling with the noisy self-draft, schedule A."""
+                    chunk: int = 2048, max_len: int | None = None, bonus: bool = True, temperature: float = 1.0,
+                    top_k: int = 0, top_p: float = 1.0) -> SpecTrace:
+    """Modified rejection sampling with the noisy self-draft, schedule A.
+
+    tr.margins[r] is round r's pair of closest calls: the smallest distance of
+    an accept uniform from its threshold, and the smallest distance (relative
+    to the total) of a sampling uniform from the CDF steps around the index it
+    picked.
+
+    Round r at n0 committed tokens: z_1 = saved_next, z_j (j > 1) the target's
+    one-token step on d_(j-1) over the shared cache; the draft logits are
+    z_j + noise[n0 + j - 1] (0-based: noise[n0 + j] for slot j); the cache is
+    rewound to t before the k-row verify.  Without the bonus a fully accepted
+    round commits the k drafts only, keeps the cache at t + k and takes the
+    last verify row as the next saved_next (no repair forward).
+    """
     prompt = np.asarray(prompt)
     P = prompt.shape[0]
     tc = OracleCache(w.shape, max_len or (P + n_new + 2 * k + 2))
@@ -176,25 +241,31 @@ def spec_stochastic(w: OracleWeights, prompt, n_new: int, k: int, noise: np.ndar
         n0 = len(committed)
         t = tc.length
         z = saved
-        drafts, q_rows = [], []
+        drafts, q_logits, s_margin = [], [], 1.0
         for j in range(k):
-            q = acc.softmax(np.asarray(z, np.float64) + noise[n0 + j])
-            d = acc.sample_inverse_cdf(q, philox.uniform(seed, rnd, j, philox.STREAM_DRAFT))
+            ql = np.asarray(z, np.float64) + noise[n0 + j]
+            d = draft_sample(ql, seed, rnd, j, temperature)
+            s_margin = min(s_margin, acc.cdf_margin(acc.softmax(ql, temperature),
+                                                    philox.uniform(seed, rnd, j, philox.STREAM_DRAFT), d))
             drafts.append(d)
-            q_rows.append(q)
+            q_logits.append(ql)
             if j + 1 < k:
                 z = forward(w, tc, [d])[0]
                 tr.draft_calls += 1
         tc.trim(t)
         rows = forward(w, tc, drafts)
         tr.target_calls += 1
-        p_rows = [acc.softmax(saved)] + [acc.softmax(r) for r in rows]
-        ua = [philox.uniform(seed, rnd, j, philox.STREAM_ACCEPT) for j in range(k)]
-        ur = philox.uniform(seed, rnd, 0, philox.STREAM_RESAMPLE)
-        m, com, info = acc.stochastic_accept(p_rows, q_rows, drafts, ua, ur)
-        tc.trim(t + m)
-        saved = forward(w, tc, [com[-1]])[0]
-        tr.target_calls += 1
+        m, com, info = stochastic_round(saved, rows, q_logits, drafts, seed, rnd, bonus, temperature, top_k, top_p)
+        a_margin = min([1.0] + [abs(u - a) for u, a in zip(info["u_accept"], info["ratios"])])
+        if info["sample_weights"] is not None:
+            s_margin = min(s_margin, acc.cdf_margin(info["sample_weights"], info["u_resample"], com[-1]))
+        tr.margins.append((a_margin, s_margin))
+        if m == k and not bonus:
+            saved = rows[k - 1]
+        else:
+            tc.trim(t + m)
+            saved = forward(w, tc, [com[-1]])[0]
+            tr.target_calls += 1
         committed += com
         tr.m.append(m)
         tr.drafts.append(drafts)

@@ -87,41 +87,54 @@ def near_cdf_step(weights, u, i):
     return min(abs(t - lo), abs(t - c[min(i, len(c) - 1)])) < BOUNDARY * c[-1]
 
 
-def check_stochastic_round(saved, rows, qz, drafts, m_gpu, com_gpu, seed, rnd):
-    """Replay one schedule-A round of modified rejection sampling in the oracle.
+def near_truncation_boundary(weights, top_k, top_p, band=BOUNDARY):
+    """True when the truncated set of `weights` could change under a relative change of
+    `band`: the top_k-th and next weights nearly tie, or the running mass of the survivors
+    passes top_p of their total within band."""
+    w = np.asarray(weights, np.float64)
+    order = np.lexsort((np.arange(w.shape[0]), -w))
+    near = False
+    if 0 < top_k < w.shape[0]:
+        a, b2 = w[order[top_k - 1]], w[order[top_k]]
+        near |= abs(a - b2) <= band * max(a, 1e-300)
+    if top_p < 1.0:
+        kept = order[:top_k] if 0 < top_k < w.shape[0] else order
+        c = np.cumsum(w[kept])
+        near |= bool(np.any(np.abs(c - top_p * c[-1]) <= band * c[-1]))
+    return near
+
+
+def check_stochastic_round(saved, rows, qz, drafts, m_gpu, com_gpu, seed, rnd, bonus=True, temperature=1.0,
+                           top_k=0, top_p=1.0):
+    """Replay one schedule-A round of modified rejection sampling in the oracle
+    (oracle.spec.draft_sample and oracle.spec.stochastic_round) on the GPU's logits.
 
     saved: target logits before the round ([V]); rows: the k verify rows;
-    qz: the k noisy draft logits the GPU drew from; drafts: the GPU's k draft
+    qz: the k draft logit rows the GPU drew from; drafts: the GPU's k draft
     tokens; m_gpu / com_gpu: the GPU's accepted count and committed tokens.
     Returns the number of boundary exemptions (0 or more); raises on a
     decision that differs away from a boundary.
     """
     from oracle import accept as acc
     from oracle import philox
+    from oracle.spec import draft_sample, stochastic_round
     k = len(drafts)
+    drafts = [int(x) for x in drafts]
     exempt = 0
-    q_rows = [softmax64(qz[j]) for j in range(k)]
     for j in range(k):
-        u = philox.uniform(seed, rnd, j, philox.STREAM_DRAFT)
-        d = acc.sample_inverse_cdf(q_rows[j], u)
-        if d != int(drafts[j]):
-            assert near_cdf_step(q_rows[j], u, int(drafts[j])), f"round {rnd} draft {j}: gpu {drafts[j]} oracle {d}"
+        d = draft_sample(qz[j], seed, rnd, j, temperature)
+        if d != drafts[j]:
+            u = philox.uniform(seed, rnd, j, philox.STREAM_DRAFT)
+            assert near_cdf_step(acc.softmax(qz[j], temperature), u, drafts[j]), \
+                f"round {rnd} draft {j}: gpu {drafts[j]} oracle {d}"
             exempt += 1
-    p_rows = [softmax64(saved)] + [softmax64(r) for r in rows]
-    ua = [philox.uniform(seed, rnd, j, philox.STREAM_ACCEPT) for j in range(k)]
-    ur = philox.uniform(seed, rnd, 0, philox.STREAM_RESAMPLE)
-    m, com, info = acc.stochastic_accept(p_rows, q_rows, [int(x) for x in drafts], ua, ur)
+    m, com, info = stochastic_round(saved, rows, qz, drafts, seed, rnd, bonus, temperature, top_k, top_p)
     if m == m_gpu and list(com) == [int(x) for x in com_gpu]:
         return exempt
-    near_accept = any(abs(ua[j] - info["ratios"][j]) < BOUNDARY for j in range(len(info["ratios"])))
-    if m == m_gpu:
-        j = m
-        src = acc.residual(p_rows[j], q_rows[j]) if j < k else p_rows[k]
-        if j < k and src.sum() <= acc.RESIDUAL_EPS:
-            src = p_rows[j]
-        near_sample = near_cdf_step(src, ur, int(com_gpu[-1]))
-    else:
-        near_sample = False
+    near_accept = any(abs(u - a) < BOUNDARY for u, a in zip(info["u_accept"], info["ratios"]))
+    near_sample = (m == m_gpu and info["sample_weights"] is not None and
+                   (near_cdf_step(info["sample_weights"], info["u_resample"], int(com_gpu[-1])) or
+                    near_truncation_boundary(info["source_weights"], top_k, top_p)))
     assert near_accept or near_sample, f"round {rnd}: gpu m={m_gpu} {list(com_gpu)} oracle m={m} {com}"
     return exempt + 1
 

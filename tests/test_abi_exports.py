@@ -88,3 +88,31 @@ def test_q4_blob_size_and_shape_checks():
     big = b.desc_of(TINY, b.W_Q4G64)
     big.hidden = 8192   # past the hidden limit (and the 4-bit kernel's LDS budget)
     assert L.specdec_weights_bytes(ctypes.byref(big), ctypes.byref(n)) == b.ESHAPE
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """Every field of the ctypes mirrors sits at the offset the C compiler gives it in
+    include/specdec.h (gcc on the host), and the structs have the same size."""
+    import shutil
+    import subprocess
+    from block_verify_amd import lib as b
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    structs = {"specdec_round_desc": b.RoundDesc, "specdec_model_desc": b.ModelDesc,
+               "specdec_round_state": b.RoundState}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    for line in filter(None, out):
+        cname, fname, val = line.split()
+        py = structs[cname]
+        got = ctypes.sizeof(py) if fname == "sizeof" else getattr(py, fname).offset
+        assert got == int(val), (cname, fname, got, val)

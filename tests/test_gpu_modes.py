@@ -1,0 +1,274 @@
+"""GPU parity of the round's acceptance modes on the tiny decoder (through the C ABI):
+modified rejection sampling without the bonus, with a temperature and with top-k /
+top-p truncation of the post-acceptance sample; the relaxed Delta-logit rule; the
+device error bits forced from the host.
+
+Stochastic rounds are replayed in the oracle (oracle.spec.stochastic_round) on the
+GPU's own logits: draft samples and decisions must match except where a uniform
+lies within 1e-6 of a threshold, a CDF step or a truncation boundary (counted).
+The relaxed rule is an exact comparison in fp32 on the GPU's logits.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_logits_close, check_stochastic_round, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+P, N_NEW, K = 128, 16, 4
+
+
+@pytest.fixture(scope="module")
+def env():
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import TINY, SEED_TARGET
+    from block_verify_amd.synth import make_prompt, make_weights
+    from oracle.model import OracleWeights
+    say("modes: building the tiny model")
+    w = make_weights(TINY, SEED_TARGET)
+    return dict(b=b, shape=TINY, w=w, model=b.Model(TINY, w), prompt=make_prompt(TINY.vocab, P),
+                ow=OracleWeights(TINY, w))
+
+
+@pytest.fixture(scope="module")
+def gpu_ar(env):
+    b, S = env["b"], env["shape"]
+    cache, ws = b.Cache(S, 512), b.Workspace(S, 512)
+    n = N_NEW + K + 2
+    toks = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(env["model"], cache, torch.from_numpy(env["prompt"]).cuda(), ws, logits=scratch, argmax=toks[0:1])
+    for i in range(n - 1):
+        b.decode_step(env["model"], cache, toks[i:i + 1], ws, logits=scratch, argmax=toks[i + 1:i + 2])
+    return [int(x) for x in to_np(toks)[:n]]
+
+
+def _stochastic_job(env, noise, seed=3, **kw):
+    """Round by round: saved_next and the verify rows against the oracle's forward
+    (teacher-forced on the GPU's committed tokens), the decisions replayed in the oracle."""
+    from oracle.model import OracleCache, forward, prefill
+    b, S = env["b"], env["shape"]
+    V = S.vocab
+    r = b.Round(env["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=seed,
+                max_len=512, **kw)
+    r.prefill(env["prompt"])
+    r.reset(N_NEW)
+    oc = OracleCache(S, 512)
+    o_saved = prefill(env["ow"], oc, env["prompt"])
+    T = kw.get("temperature", 1.0)
+    bonus = kw.get("bonus", True)
+    exempt, n0, ms, full = 0, 0, [], 0
+    while n0 < N_NEW:
+        saved = to_np(r.debug_view(0)).copy()
+        st0, _ = r.read_state()
+        assert_logits_close(saved, o_saved, f"round {st0.round} saved_next")
+        len0 = r.tcache.length()
+        r.step()
+        st, toks = r.read_state()
+        rows = to_np(r.debug_view(1)).reshape(K + 1, V)[:K].copy()
+        qz = to_np(r.debug_view(2)).reshape(K, V).copy()
+        drafts = [int(x) for x in to_np(r.debug_view(3, torch.int32))[:K]]
+        ol = forward(env["ow"], oc.clone(), drafts)
+        assert_logits_close(rows, ol, f"round {st0.round} verify rows")
+        com = [int(x) for x in toks[n0:st.n_committed]]
+        exempt += check_stochastic_round(saved, rows, qz, drafts, st.m_last, com, seed, st0.round, bonus, T,
+                                         kw.get("top_k", 0), kw.get("top_p", 1.0))
+        if st.m_last == K and not bonus:
+            # all kept, no bonus: k tokens, the cache keeps them, saved_next = last verify row
+            assert len(com) == K and r.tcache.length() == len0 + K
+            full += 1
+            o_saved = forward(env["ow"], oc, com)[-1]
+        else:
+            assert len(com) == st.m_last + 1
+            o_saved = forward(env["ow"], oc, com)[-1]
+        assert r.tcache.length() == P + st.n_committed
+        ms.append(st.m_last)
+        n0 = st.n_committed
+    assert r.ws.error_bits() == 0
+    say(f"stochastic {kw}: {len(ms)} rounds, accepted {ms}, {full} full rounds without bonus, "
+        f"{exempt} boundary exemptions")
+    return exempt, full
+
+
+@pytest.mark.parametrize("kw", [
+    dict(temperature=0.7),
+    dict(temperature=1.3, top_k=20),
+    dict(top_p=0.9),
+    dict(temperature=0.8, top_k=50, top_p=0.8),
+    dict(top_k=1),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_stochastic_temperature_and_truncation_match_oracle(env, kw):
+    from block_verify_amd.synth import make_noise
+    noise = make_noise(N_NEW + 2 * K + 2, env["shape"].vocab)
+    exempt, _ = _stochastic_job(env, noise, **kw)
+    assert exempt <= 1
+
+
+def test_stochastic_without_bonus_matches_oracle(env):
+    """Small noise (0.05 N(0,1)) so most rounds keep every draft: those commit k tokens
+    and hand the last verify row on as saved_next, with no repair forward."""
+    from block_verify_amd.synth import make_noise
+    noise = 0.05 * make_noise(N_NEW + 2 * K + 2, env["shape"].vocab)
+    exempt, full = _stochastic_job(env, noise, bonus=False)
+    assert full >= 1 and exempt <= 1
+
+
+def test_stochastic_job_matches_oracle_job(env):
+    """The whole job against the oracle's own job (oracle.spec.spec_stochastic, same
+    noise and Philox seed): the committed tokens agree up to the first round whose
+    closest call in the oracle is near enough to flip under the GPU's float32 logits: an
+    accept uniform within 1e-3 of its threshold, or a sampling uniform within 1e-5 of the
+    total from a CDF step (a shift common to every probability of a row cancels)."""
+    from block_verify_amd.synth import make_noise
+    from oracle.spec import spec_stochastic
+    b, S = env["b"], env["shape"]
+    noise = make_noise(N_NEW + 2 * K + 2, S.vocab)
+    r = b.Round(env["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=3,
+                max_len=512)
+    r.prefill(env["prompt"])
+    st, toks = r.run(N_NEW)
+    tr = spec_stochastic(env["ow"], env["prompt"], N_NEW, K, noise, seed=3)
+    n0, checked = 0, 0
+    for m, (a_margin, s_margin), stop in zip(tr.m, tr.margins, tr.stops):
+        if a_margin < 1e-3 or s_margin < 1e-5:
+            break
+        n = m + (0 if stop == "full" else 1)
+        assert [int(x) for x in toks[n0:n0 + n]] == tr.tokens[n0:n0 + n], f"round at {n0}"
+        n0 += n
+        checked += 1
+    say(f"stochastic job vs oracle job: {checked} of {tr.rounds} rounds equal before the first close call; "
+        f"gpu {list(toks[:N_NEW])} oracle {tr.tokens}")
+    assert checked >= 1 or tr.margins[0][0] < 1e-3 or tr.margins[0][1] < 1e-5
+
+
+def _relaxed_rows(r, V, sched, saved_before):
+    rows = to_np(r.debug_view(1)).reshape(K + 1, V).copy()
+    return list(rows[:K + 1]) if sched == 1 else [saved_before] + list(rows[:K])
+
+
+@pytest.mark.parametrize("delta", [0.3, 0.9])
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_relaxed_rounds_match_oracle_rule(env, gpu_ar, schedule, delta):
+    """Every round's decision equals the oracle's relaxed rule applied to the GPU's own
+    fp32 logits, bit for bit; the cache keeps prompt + committed positions.  (Tiny-model
+    logits spread ~0.3, so Delta = 0.9 keeps many drafts that are not the argmax.)"""
+    from block_verify_amd.synth import make_draft_table
+    from oracle.accept import relaxed_accept
+    b, S = env["b"], env["shape"]
+    V = S.vocab
+    table = make_draft_table(np.array(gpu_ar), V, 0.5)
+    r = b.Round(env["model"], K, mode=b.RELAXED, relax_delta=delta, schedule=schedule, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    r.reset(N_NEW)
+    n0, relaxed_wins = 0, 0
+    while n0 < N_NEW:
+        saved = to_np(r.debug_view(0)).copy()
+        r.step()
+        st, toks = r.read_state()
+        drafts = [int(x) for x in table[n0:n0 + K]]
+        rows = _relaxed_rows(r, V, schedule, saved)
+        m, com = relaxed_accept(rows, drafts, delta)
+        assert (st.m_last, [int(x) for x in toks[n0:st.n_committed]]) == (m, com)
+        relaxed_wins += sum(1 for j in range(m) if drafts[j] != int(np.argmax(rows[j])))
+        assert r.tcache.length() == P + st.n_committed - (1 if schedule == 1 else 0)
+        n0 = st.n_committed
+    assert r.ws.error_bits() == 0
+    same = next((i for i, (x, y) in enumerate(zip(toks[:N_NEW], gpu_ar)) if int(x) != y), N_NEW)
+    say(f"relaxed schedule {'AB'[schedule]}: {relaxed_wins} drafts kept that are not the argmax; "
+        f"output equals the greedy decode for its first {same} of {N_NEW} tokens")
+
+
+def test_relaxed_zero_delta_is_greedy_and_large_delta_keeps_all(env, gpu_ar):
+    from block_verify_amd.synth import make_draft_table
+    b, S = env["b"], env["shape"]
+    table = make_draft_table(np.array(gpu_ar), S.vocab, 0.4)
+    r = b.Round(env["model"], K, mode=b.RELAXED, relax_delta=0.0, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    st, toks = r.run(N_NEW)
+    assert list(toks[:N_NEW]) == gpu_ar[:N_NEW]
+    r = b.Round(env["model"], K, mode=b.RELAXED, relax_delta=1e30, table=np.full(64, 7, np.int32), max_len=512)
+    r.prefill(env["prompt"])
+    st, toks = r.run(N_NEW)
+    assert st.accepted_total == K * st.round
+    assert r.tcache.length() == P + st.n_committed
+
+
+def test_relaxed_without_bonus_keeps_last_row(env, gpu_ar):
+    """Relaxed, schedule A, no bonus: a fully accepted round commits the k drafts and the
+    next round's first test reads the last verify row (copied to saved_next)."""
+    b, S = env["b"], env["shape"]
+    V = S.vocab
+    r = b.Round(env["model"], K, mode=b.RELAXED, relax_delta=1e30, bonus=False, table=np.full(64, 7, np.int32),
+                max_len=512)
+    r.prefill(env["prompt"])
+    r.reset(N_NEW)
+    r.step()
+    rows = to_np(r.debug_view(1)).reshape(K + 1, V)[:K].copy()
+    st, toks = r.read_state()
+    assert st.n_committed == K and r.tcache.length() == P + K
+    assert [int(x) for x in toks[:K]] == [7] * K
+    assert np.array_equal(to_np(r.debug_view(0)), rows[K - 1])
+    assert r.ws.error_bits() == 0
+
+
+def test_error_bits_forced_from_host(env, gpu_ar):
+    """Device-detected violations set their sticky bits and fault nothing: non-finite
+    logits (an infinite LM-head weight), a draft table read past its end, a full
+    committed-token buffer (the state's capacity word lowered from the host), a forward
+    past the cache capacity (the length stays); a draft model with another vocabulary is
+    refused on the host."""
+    from block_verify_amd.shapes import TINY, SEED_DRAFT
+    from block_verify_amd.synth import make_draft_table, make_weights
+    b, S = env["b"], env["shape"]
+    # non-finite logits
+    w = [t.copy() for t in env["w"]]
+    w[-1][5, 0] = np.uint16(0x7F80)          # +inf in LM-head row 5
+    bad = b.Model(S, w)
+    cache, ws = b.Cache(S, 256), b.Workspace(S, 256)
+    logits = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(bad, cache, torch.from_numpy(env["prompt"]).cuda(), ws, logits=logits)
+    assert ws.error_bits() & b.DERR_NONFINITE
+    # draft table read past its end
+    table = make_draft_table(np.array(gpu_ar), S.vocab, 0.4)[:6]
+    r = b.Round(env["model"], K, table=table, max_len=512)
+    r.prefill(env["prompt"])
+    r.run(N_NEW)
+    assert r.ws.error_bits() & b.DERR_TABLE
+    # committed-token buffer full: the state's capacity word is device memory the caller owns
+    table = make_draft_table(np.array(gpu_ar), S.vocab, 0.0)
+    r = b.Round(env["model"], K, table=table, max_len=512, cap=64)
+    r.prefill(env["prompt"])
+    r.reset(N_NEW)
+    cap_off = b.RoundState.cap.offset // 4
+    r.state[:64].view(torch.int32)[cap_off] = 3
+    r.step()
+    assert r.ws.error_bits() & b.DERR_OUTPUT
+    st, _ = r.read_state()
+    assert st.n_committed == K + 1          # counted, not stored past the buffer
+    # a forward past the capacity leaves the length where it was
+    cache, ws = b.Cache(S, 140), b.Workspace(S, 140)
+    b.prefill(env["model"], cache, torch.from_numpy(env["prompt"]).cuda(), ws)
+    t16 = torch.arange(16, dtype=torch.int32, device="cuda")
+    b.decode_step(env["model"], cache, t16, ws)
+    assert ws.error_bits() & b.DERR_CAPACITY
+    assert cache.length() == P
+    # another vocabulary: refused when the round is created
+    from dataclasses import replace
+    small = replace(TINY, vocab=2048)
+    draft = b.Model(small, make_weights(small, SEED_DRAFT))
+    with pytest.raises(b.SpecdecError, match=r"\[-3\]"):
+        b.Round(env["model"], K, draft_source=b.DRAFT_MODEL, draft=draft, table=table, max_len=512)
+
+
+def test_sampling_arguments_are_checked_on_the_host(env):
+    from block_verify_amd.synth import make_noise
+    b, S = env["b"], env["shape"]
+    noise = make_noise(8, S.vocab)
+    for kw in (dict(temperature=0.0), dict(temperature=-1.0), dict(top_k=-1), dict(top_k=S.vocab + 1),
+               dict(top_p=0.0), dict(top_p=1.5)):
+        with pytest.raises(b.SpecdecError, match=r"\[-1\]"):
+            b.Round(env["model"], K, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise,
+                    max_len=256, **kw)
+    with pytest.raises(b.SpecdecError, match=r"\[-1\]"):
+        b.Round(env["model"], K, mode=b.RELAXED, relax_delta=-0.5, table=np.zeros(64, np.int32), max_len=256)
