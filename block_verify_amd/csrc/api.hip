@@ -762,6 +762,11 @@ int specdec_round_debug_view(const specdec_round* r, int32_t which, void** d_ptr
   return SPECDEC_OK;
 }
 
+int specdec_stream_read(const void* d_buf, size_t bytes, uint32_t* d_sink, void* stream) {
+  if (!d_buf || !d_sink || bytes == 0 || bytes % 16) return SPECDEC_EINVAL;
+  return hip_status(launch_stream_read(d_buf, bytes, d_sink, (hipStream_t)stream));
+}
+
 // Test hook: Philox4x64-10 words for n (counter, key) pairs (device arrays).
 int specdec_philox4x64(const uint64_t* d_ctr, const uint64_t* d_key, int32_t n, uint64_t* d_out, void* stream) {
   if (!d_ctr || !d_key || !d_out || n <= 0) return SPECDEC_EINVAL;

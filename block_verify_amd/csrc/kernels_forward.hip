@@ -1065,6 +1065,32 @@ hipError_t launch_advance(int32_t* d_len, int rows, int max_len, const int32_t* 
   return hipGetLastError();
 }
 
+// Read-bandwidth probe: every 16-byte word of a buffer read once with the
+// non-temporal loads of the weight stream, eight in flight per lane, folded
+// into one word per lane that is stored only if it hits a constant (so the
+// loads stay live without a write stream).
+__global__ __launch_bounds__(256) void stream_read_kernel(const i32x4_t* __restrict__ p, size_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  i32x4_t acc = {0, 0, 0, 0};
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    i32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  const uint32_t x = (uint32_t)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+  if (x == 0x9E3779B9u) sink[0] = x;
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  stream_read_kernel<<<2048, 256, 0, s>>>(static_cast<const i32x4_t*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
+
 // Copy the last row of a forward's outputs (prefill) to the caller's buffers.
 __global__ void copy_last_kernel(const float* __restrict__ logits, const int32_t* __restrict__ argmax,
                                  const float* __restrict__ lse, int rows, int V, float* __restrict__ ldst,

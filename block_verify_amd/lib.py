@@ -33,7 +33,7 @@ EXPORTED = [
     "specdec_prefill", "specdec_round_state_bytes", "specdec_round_ws_bytes", "specdec_round_create",
     "specdec_round_destroy", "specdec_round_prefill", "specdec_round_reset", "specdec_verify_round",
     "specdec_check", "specdec_last_hip_error", "specdec_status_str", "specdec_philox4x64",
-    "specdec_round_graph", "specdec_round_graph_launch", "specdec_round_debug_view",
+    "specdec_round_graph", "specdec_round_graph_launch", "specdec_round_debug_view", "specdec_stream_read",
 ]
 
 
@@ -101,6 +101,7 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
         "specdec_round_graph": (C.c_int, [vp]),
         "specdec_round_graph_launch": (C.c_int, [vp, i32, vp]),
         "specdec_round_debug_view": (C.c_int, [vp, i32, P(vp), P(sz)]),
+        "specdec_stream_read": (C.c_int, [vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -263,6 +264,12 @@ def prefill(model: Model, cache: Cache, tokens: torch.Tensor, ws: Workspace, chu
     check(lib().specdec_prefill(model.handle, cache.handle, tokens.data_ptr(), int(tokens.numel()), chunk,
                                 _ptr(logits), _ptr(argmax), _ptr(lse), ws.mem.data_ptr(), ws.nbytes,
                                 _stream(stream)), "prefill")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of `buf` once (the stream-read ceiling probe)."""
+    check(lib().specdec_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                    _stream(stream)), "stream_read")
 
 
 def philox4x64(counters: np.ndarray, keys: np.ndarray, device="cuda") -> np.ndarray:

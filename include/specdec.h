@@ -312,6 +312,14 @@ int32_t specdec_last_hip_error(void);
 int specdec_philox4x64(const uint64_t* d_ctr, const uint64_t* d_key, int32_t n, uint64_t* d_out, void* stream);
 const char* specdec_status_str(int status);
 
+/* Measurement helper, not a step of the path: read `bytes` (a multiple of
+ * 16) of device memory at d_buf once, with the same non-temporal 16-byte
+ * loads the weight stream uses, on `stream`.  d_sink is a device uint32 the
+ * kernel may write (keeps the loads live).  Timing this read over a buffer
+ * far larger than the caches gives the measured stream-read ceiling that
+ * achieved HBM bandwidth is reported against next to the published peak. */
+int specdec_stream_read(const void* d_buf, size_t bytes, uint32_t* d_sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,3 +49,37 @@ def test_traffic_is_dropped_once_a_hashed_source_changes(tmp_path, monkeypatch):
     assert bench.measured_traffic() is None
     prof.unlink()
     assert bench.measured_traffic() is None
+
+
+def test_acceptance_measures_of_a_table_job():
+    """Round by round with table drafts: a draft passes while it equals the greedy token;
+    accepted/examined counts the first failed draft of each round, accepted/drafted all k."""
+    import bench
+    ar = list(range(100, 140))
+    k = 4
+    m, acc = bench.accept_pattern(list(ar), ar, k, 20)           # every draft right
+    assert m == [4, 4, 4, 4] and acc == {"accepted_over_examined": 1.0, "accepted_over_drafted": 1.0}
+    m, acc = bench.accept_pattern([0] * 40, ar, k, 5)            # every draft wrong
+    assert m == [0] * 5 and acc == {"accepted_over_examined": 0.0, "accepted_over_drafted": 0.0}
+    table = list(ar)
+    table[2] = -1                                                 # round 1 stops at its third draft
+    m, acc = bench.accept_pattern(table, ar, k, 8)
+    assert m == [2, 4]                                           # rounds at n0 = 0 and 3
+    assert acc["accepted_over_examined"] == round(6 / (3 + 4), 4)
+    assert acc["accepted_over_drafted"] == round(6 / 8, 4)
+
+
+def test_protocol_alternates_order_and_times_every_leg():
+    import bench
+    calls = []
+
+    def leg(name):
+        def f(steps):
+            calls.append((name, steps))
+            return 0.5
+        return f
+    out = bench.protocol({"A": leg("A"), "B": leg("B"), "AR": leg("AR")}, steps=3, warmup=1, repeats=4, n_new=64)
+    timed = [c for c in calls if c[1] == 3]
+    assert [c[0] for c in timed] == ["A", "B", "AR", "AR", "B", "A", "A", "B", "AR", "AR", "B", "A"]
+    assert out["B"] == [64 * 3 / 0.5] * 4
+    assert bench.stats([3.0, 1.0, 2.0]) == {"median": 2.0, "min": 1.0, "max": 3.0, "n": 3}
