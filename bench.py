@@ -114,41 +114,52 @@ def gpu_clocks():
         return None
 
 
-def stream_ceiling(b, torch, gib: float = 2.0, n: int = 20):
-    """Measured stream-read ceiling: median GB/s of the library's read probe over a buffer of
-    `gib` GiB (far past the 256 MB memory-side cache)."""
+def stream_ceiling(b, torch, gib: float = 2.0, n: int = 12):
+    """Measured stream-read ceiling: the best launch width's median GB/s of the library's
+    read probe over a buffer of `gib` GiB (far past the 256 MB memory-side cache)."""
     buf = torch.empty(int(gib * (1 << 30)), dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     ev = HipEvents(2 * n)
     stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(3):
-        b.stream_read(buf, sink)
-    for i in range(n):
-        ev.record(2 * i, stream)
-        b.stream_read(buf, sink)
-        ev.record(2 * i + 1, stream)
-    torch.cuda.synchronize()
-    gbs = sorted(buf.numel() / (ev.ms(2 * i, 2 * i + 1) * 1e-3) / 1e9 for i in range(n))
+    per_width = {}
+    for wgs in (1024, 2048, 4096, 8192, 16384):
+        for _ in range(2):
+            b.stream_read(buf, sink, wgs)
+        for i in range(n):
+            ev.record(2 * i, stream)
+            b.stream_read(buf, sink, wgs)
+            ev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+        gbs = sorted(buf.numel() / (ev.ms(2 * i, 2 * i + 1) * 1e-3) / 1e9 for i in range(n))
+        per_width[wgs] = round(gbs[n // 2], 1)
     del buf
-    return {"gbs": round(gbs[n // 2], 1), "min_gbs": round(gbs[0], 1), "max_gbs": round(gbs[-1], 1),
+    best = max(per_width, key=per_width.get)
+    return {"gbs": per_width[best], "workgroups": best, "per_workgroups": per_width,
             "bytes": int(gib * (1 << 30)), "reads": n,
-            "how": "library probe specdec_stream_read: each 16-byte word read once with non-temporal loads"}
+            "how": "library probe specdec_stream_read: each 16-byte word read once with non-temporal loads, "
+                   "256-thread workgroups, 8 loads in flight per lane; median of the reads at each width"}
 
 
-def gpu_ar(b, model, shape, prompt_t, n, max_len, torch):
-    """Greedy AR tokens with the same kernels (M=1 steps chained on the device, eager)."""
+def gpu_ar(b, model, shape, prompt_t, n, max_len, torch, runner_up=False):
+    """Greedy AR tokens with the same kernels (M=1 steps chained on the device, eager).
+    With runner_up, also the second-ranked token of the logits each token came from."""
     cache = b.Cache(shape, max_len)
     ws = b.Workspace(shape, max_len)
     toks = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
-    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
-    b.prefill(model, cache, prompt_t, ws, logits=logits, argmax=toks[0:1])
+    logits = torch.empty((n if runner_up else 1, shape.vocab), dtype=torch.float32, device="cuda")
+    b.prefill(model, cache, prompt_t, ws, logits=logits[0], argmax=toks[0:1])
     for i in range(n - 1):
-        b.decode_step(model, cache, toks[i:i + 1], ws, logits=logits, argmax=toks[i + 1:i + 2])
+        b.decode_step(model, cache, toks[i:i + 1], ws, logits=logits[i + 1 if runner_up else 0],
+                      argmax=toks[i + 1:i + 2])
     torch.cuda.synchronize()
     if ws.error_bits():
         raise RuntimeError(f"AR: device error bits {ws.error_bits()}")
-    return [int(x) for x in toks[:n].cpu().numpy()]
+    out = [int(x) for x in toks[:n].cpu().numpy()]
+    if runner_up:
+        top2 = torch.topk(logits, 2, dim=1).indices[:, 1]
+        return out, [int(x) for x in top2.cpu().numpy()]
+    return out
 
 
 class GraphAR:
@@ -503,7 +514,7 @@ def main():
         run_substitute(args, torch)
         return
     from block_verify_amd.shapes import QWEN_0_5B, QWEN_1_5B as S, SEED_DRAFT, SEED_TARGET
-    from block_verify_amd.synth import make_draft_table, make_noise, make_prompt, make_weights
+    from block_verify_amd.synth import make_draft_table, make_near_miss_table, make_noise, make_prompt, make_weights
 
     k, n_new = 4, args.n_new
     P = args.context
@@ -519,7 +530,7 @@ def main():
     prompt = make_prompt(S.vocab, P)
     prompt_t = torch.from_numpy(prompt).cuda()
 
-    ar_toks = gpu_ar(b, model, S, prompt_t, n_new + k + 2, max_len, torch)
+    ar_toks, runner_up = gpu_ar(b, model, S, prompt_t, n_new + k + 2, max_len, torch, runner_up=True)
     table = make_draft_table(np.array(ar_toks), S.vocab, args.corrupt)
     ar = GraphAR(b, model, S, prompt_t, max_len, torch)
 
@@ -621,19 +632,25 @@ def main():
         legs["all_accept_bonus_2k"]["pages_R_spec_over_ar"] = 0.912
         legs["draft_free_2k"]["pages_spec_over_ar"] = 4.46
         del ljobs
-        # relaxed acceptance (lossy): Delta = 1 logit
-        rj = SpecJob(b, model, prompt, k, n_new, max_len, torch, terms=False, schedule=1, table=table,
-                     mode=b.RELAXED, relax_delta=1.0)
-        rres = protocol({"relaxed": lambda st: rj.timed(st)[0], "AR": ar_leg}, args.steps, args.warmup, 3, n_new)
-        _, outs = rj.timed(1)
-        st, toks = outs[0]
-        toks = [int(x) for x in toks[:n_new]]
-        prefix = next((i for i, (x, y) in enumerate(zip(toks, ar_toks)) if x != y), n_new)
-        legs["relaxed_delta1_2k"] = {**leg_summary(rres["relaxed"], rres["AR"]), "rounds_per_job": st.round,
-                                     "accepted_over_drafted": round(st.accepted_total / (k * st.round), 4),
-                                     "equal_to_ar_prefix_tokens": prefix, "equal_to_ar": prefix == n_new,
-                                     "pages_acceptance_R": {"acceptance": 0.81, "R": 0.714}}
-        del rj
+        # relaxed acceptance (lossy), on drafts that miss by a small logit gap: the corrupted
+        # positions of the headline table carry the target's runner-up token instead
+        near = make_near_miss_table(np.array(ar_toks), np.array(runner_up), args.corrupt)
+        for nm, kw in (("near_miss_greedy_2k", dict(mode=b.GREEDY)),
+                       ("relaxed_delta0.5_2k", dict(mode=b.RELAXED, relax_delta=0.5)),
+                       ("relaxed_delta1_2k", dict(mode=b.RELAXED, relax_delta=1.0))):
+            rj = SpecJob(b, model, prompt, k, n_new, max_len, torch, terms=False, schedule=1, table=near, **kw)
+            rres = protocol({"relaxed": lambda st: rj.timed(st)[0], "AR": ar_leg}, args.steps, args.warmup, 3, n_new)
+            _, outs = rj.timed(1)
+            st, toks = outs[0]
+            toks = [int(x) for x in toks[:n_new]]
+            prefix = next((i for i, (x, y) in enumerate(zip(toks, ar_toks)) if x != y), n_new)
+            legs[nm] = {**leg_summary(rres["relaxed"], rres["AR"]), "rounds_per_job": st.round,
+                        "accepted_over_drafted": round(st.accepted_total / (k * st.round), 4),
+                        "equal_to_ar_prefix_tokens": prefix, "equal_to_ar": prefix == n_new,
+                        "drafts": "table, corrupted positions (p=%.2f) carry the runner-up token" % args.corrupt}
+            if nm.startswith("relaxed_delta1"):
+                legs[nm]["pages_acceptance_R"] = {"acceptance": 0.81, "R": 0.714}
+            del rj
         if not args.no_8k:
             P8 = 8192
             max8 = P8 + n_new + 4 * (k + 2) + 64

@@ -548,7 +548,7 @@ __global__ void accept_decide_kernel(RoundDev r) {
   TruncState* ts = r.trunc;
   ts->prefix = 0;
   ts->need = 0;
-  ts->target = 0.0;
+  ts->target = 0;
   ts->kthresh = 0;
   ts->thresh = 0;
   ts->active = mode != kWNone;
@@ -567,67 +567,80 @@ __global__ void trunc_begin_kernel(RoundDev r, int S) {
 // Radix-select pass `pass` of stage `stage` (0: top-k by count, 1: top-p by
 // mass): per-slice histograms of the current key digit over the candidates
 // (keys that match the resolved prefix; in the top-p stage also at or above
-// the top-k threshold).  Each bin's mass is its thread's sum over the
-// slice's entries in index order.
+// the top-k threshold).  Counts and fixed-point masses are integer LDS
+// atomics, exact in any order.
+__device__ __forceinline__ uint64_t mass_fixed(float w) { return (uint64_t)((double)w * kMassScale); }
+
 __global__ __launch_bounds__(kSliceThreads) void trunc_hist_kernel(RoundDev r, int pass, int stage) {
-  if (r.flags[kFlagOpen] == 0 || r.trunc->active == 0) return;
-  __shared__ uint16_t dig[kSliceElems];
-  __shared__ float wv[kSliceElems];
+  if (r.flags[kFlagOpen] == 0 || r.trunc->active == 0 || (pass > 0 && r.trunc->done)) return;
+  __shared__ int hc[kTruncBins];
+  __shared__ unsigned long long hm[kTruncBins];
   const int V = r.V, sl = blockIdx.x, t = threadIdx.x;
+  hc[t] = 0;
+  hm[t] = 0ull;
   const TruncState& ts = *r.trunc;
   const SampleRows w = accept_rows(r, r.sctl[0], r.sctl[1], 0);
   const int shift = 8 * (kTruncPasses - 1 - pass), hi = shift + 8;
   const uint64_t prefix = ts.prefix, kth = stage == 1 ? ts.kthresh : 0;
+  __syncthreads();
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const int li = e * kSliceThreads + t, i = sl * kSliceElems + li;
-    uint16_t d = 0xFFFF;
-    float v = 0.f;
+    const int i = sl * kSliceElems + e * kSliceThreads + t;
     if (i < V) {
-      v = raw_weight(w, i);
+      const float v = raw_weight(w, i);
       const uint64_t key = trunc_key(v, i);
-      if ((key >> hi) == (prefix >> hi) && key >= kth) d = (uint16_t)((key >> shift) & 0xFF);
+      if ((key >> hi) == (prefix >> hi) && key >= kth) {
+        const int d = (int)((key >> shift) & 0xFF);
+        atomicAdd(&hc[d], 1);
+        if (stage == 1) atomicAdd(&hm[d], (unsigned long long)mass_fixed(v));
+      }
     }
-    dig[li] = d;
-    wv[li] = v;
   }
   __syncthreads();
-  int cnt = 0;
-  double mass = 0.0;
-  for (int li = 0; li < kSliceElems; ++li)
-    if (dig[li] == t) { ++cnt; mass += (double)wv[li]; }
-  r.hcnt[sl * kTruncBins + t] = cnt;
-  r.hmass[sl * kTruncBins + t] = mass;
+  r.hcnt[sl * kTruncBins + t] = hc[t];
+  r.hmass[sl * kTruncBins + t] = hm[t];
 }
 
-// Radix-select resolve: bins summed over slices in slice order; the digit
-// whose bin holds the top_k-th largest key (stage 0) or where the running
-// mass from the top reaches top_p of the candidates' mass (stage 1).
-__global__ __launch_bounds__(kTruncBins) void trunc_resolve_kernel(RoundDev r, int pass, int stage, int S) {
-  if (r.flags[kFlagOpen] == 0 || r.trunc->active == 0) return;
-  __shared__ long long bc[kTruncBins];
-  __shared__ double bm[kTruncBins];
-  const int b = threadIdx.x;
+// Radix-select resolve: bins summed over slices (integers: any order); the
+// digit whose bin holds the top_k-th largest key (stage 0) or where the
+// running mass from the top reaches top_p of the candidates' mass (stage 1).
+constexpr int kResolveThreads = 1024, kResolveParts = kResolveThreads / kTruncBins;
+__global__ __launch_bounds__(kResolveThreads) void trunc_resolve_kernel(RoundDev r, int pass, int stage, int S) {
+  if (r.flags[kFlagOpen] == 0 || r.trunc->active == 0 || (pass > 0 && r.trunc->done)) return;
+  __shared__ long long pc[kResolveParts][kTruncBins];
+  __shared__ unsigned long long pm[kResolveParts][kTruncBins];
+  const int b = threadIdx.x % kTruncBins, part = threadIdx.x / kTruncBins;
   long long c = 0;
-  double ms = 0.0;
-  for (int s2 = 0; s2 < S; ++s2) {
+  unsigned long long ms = 0;
+  for (int s2 = part; s2 < S; s2 += kResolveParts) {
     c += r.hcnt[s2 * kTruncBins + b];
     ms += r.hmass[s2 * kTruncBins + b];
   }
-  bc[b] = c;
-  bm[b] = ms;
+  pc[part][b] = c;
+  pm[part][b] = ms;
   __syncthreads();
-  if (b != 0) return;
+  __shared__ long long bc[kTruncBins];
+  __shared__ unsigned long long bm[kTruncBins];
+  if (threadIdx.x < kTruncBins) {
+    long long cc = 0;
+    unsigned long long mm = 0;
+    for (int q = 0; q < kResolveParts; ++q) { cc += pc[q][b]; mm += pm[q][b]; }
+    bc[b] = cc;
+    bm[b] = mm;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   TruncState& ts = *r.trunc;
   const int shift = 8 * (kTruncPasses - 1 - pass);
   if (pass == 0) {
     ts.prefix = 0;
+    ts.done = 0;
     if (stage == 0) {
       ts.need = r.top_k;
     } else {
-      double total = 0.0;
+      unsigned long long total = 0;
       for (int i = 0; i < kTruncBins; ++i) total += bm[i];
-      ts.target = (double)r.top_p * total;
+      ts.target = (uint64_t)((double)r.top_p * (double)total);
     }
   }
   int digit = -1;
@@ -638,20 +651,26 @@ __global__ __launch_bounds__(kTruncBins) void trunc_resolve_kernel(RoundDev r, i
       cum += bc[i];
     }
   } else {
-    double cum = 0.0;
+    unsigned long long cum = 0;
     for (int i = kTruncBins - 1; i >= 0; --i) {
       if (bc[i] > 0 && cum + bm[i] >= ts.target) { digit = i; ts.target -= cum; break; }
       cum += bm[i];
     }
   }
-  if (digit < 0) {   // rounding kept the running mass below the target: keep every candidate
+  if (digit < 0) {   // the target lies in entries of zero mass: keep every candidate
     for (int i = 0; i < kTruncBins; ++i)
       if (bc[i] > 0) { digit = i; break; }
-    if (stage == 1) ts.target = 0.0;
+    if (stage == 1) ts.target = 0;
   }
   if (digit < 0) digit = 0;
   ts.prefix |= (uint64_t)digit << shift;
-  if (pass == kTruncPasses - 1) {
+  // Settled early when every candidate left in the chosen bin is kept: the
+  // lowest key with this prefix is then the threshold (top-k: the bin's count
+  // is what is still needed; top-p: the bin holds one entry, the last one the
+  // shortest run takes).
+  const bool settled = stage == 0 ? bc[digit] == ts.need : bc[digit] == 1;
+  if (settled || pass == kTruncPasses - 1) {
+    ts.done = 1;
     ts.thresh = ts.prefix;
     if (stage == 0) ts.kthresh = ts.prefix;
   }
@@ -748,7 +767,7 @@ hipError_t launch_accept_stochastic(const RoundDev& r, hipStream_t s) {
     for (int stage = tk ? 0 : 1; stage <= (tp ? 1 : 0); ++stage)
       for (int pass = 0; pass < kTruncPasses; ++pass) {
         trunc_hist_kernel<<<S, kSliceThreads, 0, s>>>(r, pass, stage);
-        trunc_resolve_kernel<<<1, kTruncBins, 0, s>>>(r, pass, stage, S);
+        trunc_resolve_kernel<<<1, kResolveThreads, 0, s>>>(r, pass, stage, S);
       }
     slice_weights_kernel<<<S, kSliceThreads, 0, s>>>(r, -1, 1);
   }

@@ -23,17 +23,21 @@ constexpr int kKeyIndexBits = 18;
 constexpr int kKeyBits = 31 + kKeyIndexBits;
 constexpr int kTruncPasses = (kKeyBits + 7) / 8;
 constexpr int kTruncBins = 256;
+// Bin masses are sums of the fp32 weights in fixed point (units of 2^-60;
+// every weight is at most 1 and their total stays below 2^63), so a bin's
+// mass is the same whatever order its entries are added in.
+constexpr double kMassScale = 1152921504606846976.0;   // 2^60
 // Select state in device memory: the key prefix resolved so far, the count
-// (top-k) or mass (top-p) still to cover below the bins taken, the top-k
-// threshold key (0 when top-k is off) and the final threshold key.
+// (top-k) or mass (top-p, fixed point) still to cover below the bins taken,
+// the top-k threshold key (0 when top-k is off) and the final threshold key.
 struct TruncState {
   uint64_t prefix;
   int64_t need;
-  double target;
+  uint64_t target;
   uint64_t kthresh;
   uint64_t thresh;
   int32_t active;    // 0: no sample this round (or truncation off)
-  int32_t pad;
+  int32_t done;      // the current stage's threshold is settled (later passes of the stage return at once)
 };
 enum { kSnapTLen = 0, kSnapDLen = 1, kSnapArgmax = 2, kSnapLse = 3, kSnapLast = 4, kNumSnap = 8 };
 
@@ -64,7 +68,7 @@ struct RoundDev {
   float* tsmax;            // [(k + 1) * slices] per-slice max of the tempered target rows
   float* tssum;            // [(k + 1) * slices] per-slice sum of exp(x - slice max)
   int32_t* hcnt;           // [slices][kTruncBins] truncation histogram: counts
-  double* hmass;           // [slices][kTruncBins] truncation histogram: masses
+  uint64_t* hmass;         // [slices][kTruncBins] truncation histogram: masses (fixed point)
   TruncState* trunc;       // truncation select state
   int32_t* t_len;
   int32_t* d_len;          // independent draft's cache length, or null

@@ -101,6 +101,18 @@ def make_draft_table(greedy: np.ndarray, vocab: int, corrupt_p: float,
     return np.where(u < corrupt_p, repl, greedy).astype(np.int32)
 
 
+def make_near_miss_table(greedy: np.ndarray, runner_up: np.ndarray, corrupt_p: float,
+                         seed: int = SEED_CORRUPT) -> np.ndarray:
+    """Draft table with the corruption mask of make_draft_table (same seed, same
+    draws), but a corrupted position carries ``runner_up[n]``, the target's
+    second-ranked token there, instead of a uniform random token: drafts that
+    miss the top-1 by a small logit gap."""
+    greedy = np.asarray(greedy, dtype=np.int64)
+    n = greedy.shape[0]
+    u = np.random.default_rng(seed).random(n)
+    return np.where(u < corrupt_p, np.asarray(runner_up, dtype=np.int64)[:n], greedy).astype(np.int32)
+
+
 def make_noise(n_pos: int, vocab: int, seed: int = SEED_NOISE) -> np.ndarray:
     """N(0,1) float32 logit noise, one row per generated position."""
     return np.random.default_rng(seed).standard_normal((n_pos, vocab), dtype=np.float32)

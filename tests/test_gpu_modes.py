@@ -31,17 +31,30 @@ def env():
                 ow=OracleWeights(TINY, w))
 
 
-@pytest.fixture(scope="module")
-def gpu_ar(env):
+def _ar_with_logits(env, n):
     b, S = env["b"], env["shape"]
     cache, ws = b.Cache(S, 512), b.Workspace(S, 512)
-    n = N_NEW + K + 2
     toks = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
-    scratch = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
-    b.prefill(env["model"], cache, torch.from_numpy(env["prompt"]).cuda(), ws, logits=scratch, argmax=toks[0:1])
+    lg = torch.empty((n, S.vocab), dtype=torch.float32, device="cuda")
+    b.prefill(env["model"], cache, torch.from_numpy(env["prompt"]).cuda(), ws, logits=lg[0], argmax=toks[0:1])
     for i in range(n - 1):
-        b.decode_step(env["model"], cache, toks[i:i + 1], ws, logits=scratch, argmax=toks[i + 1:i + 2])
-    return [int(x) for x in to_np(toks)[:n]]
+        b.decode_step(env["model"], cache, toks[i:i + 1], ws, logits=lg[i + 1], argmax=toks[i + 1:i + 2])
+    return [int(x) for x in to_np(toks)[:n]], to_np(lg)
+
+
+@pytest.fixture(scope="module")
+def gpu_ar(env):
+    return _ar_with_logits(env, N_NEW + K + 2)[0]
+
+
+@pytest.fixture(scope="module")
+def near_miss_table(env):
+    """Drafts that miss by a small logit gap: the corrupted positions of the draft table
+    (p = 0.5) carry the target's runner-up token of the GPU's own greedy decode."""
+    from block_verify_amd.synth import make_near_miss_table
+    toks, lg = _ar_with_logits(env, N_NEW + K + 2)
+    runner_up = np.argsort(-lg, axis=1, kind="stable")[:, 1]
+    return make_near_miss_table(np.array(toks), runner_up, 0.5)
 
 
 def _stochastic_job(env, noise, seed=3, **kw):
@@ -147,17 +160,17 @@ def _relaxed_rows(r, V, sched, saved_before):
     return list(rows[:K + 1]) if sched == 1 else [saved_before] + list(rows[:K])
 
 
-@pytest.mark.parametrize("delta", [0.3, 0.9])
+@pytest.mark.parametrize("delta", [0.05, 0.3])
 @pytest.mark.parametrize("schedule", [0, 1])
-def test_relaxed_rounds_match_oracle_rule(env, gpu_ar, schedule, delta):
+def test_relaxed_rounds_match_oracle_rule(env, gpu_ar, near_miss_table, schedule, delta):
     """Every round's decision equals the oracle's relaxed rule applied to the GPU's own
-    fp32 logits, bit for bit; the cache keeps prompt + committed positions.  (Tiny-model
-    logits spread ~0.3, so Delta = 0.9 keeps many drafts that are not the argmax.)"""
-    from block_verify_amd.synth import make_draft_table
+    fp32 logits, bit for bit; the cache keeps prompt + committed positions.  The drafts
+    miss by the runner-up's gap (tenths of a logit on the tiny model), so the relaxed
+    rule keeps drafts that are not the argmax."""
     from oracle.accept import relaxed_accept
     b, S = env["b"], env["shape"]
     V = S.vocab
-    table = make_draft_table(np.array(gpu_ar), V, 0.5)
+    table = near_miss_table
     r = b.Round(env["model"], K, mode=b.RELAXED, relax_delta=delta, schedule=schedule, table=table, max_len=512)
     r.prefill(env["prompt"])
     r.reset(N_NEW)
@@ -175,8 +188,10 @@ def test_relaxed_rounds_match_oracle_rule(env, gpu_ar, schedule, delta):
         n0 = st.n_committed
     assert r.ws.error_bits() == 0
     same = next((i for i, (x, y) in enumerate(zip(toks[:N_NEW], gpu_ar)) if int(x) != y), N_NEW)
-    say(f"relaxed schedule {'AB'[schedule]}: {relaxed_wins} drafts kept that are not the argmax; "
+    say(f"relaxed schedule {'AB'[schedule]} delta {delta}: {relaxed_wins} drafts kept that are not the argmax; "
         f"output equals the greedy decode for its first {same} of {N_NEW} tokens")
+    if delta >= 0.3:
+        assert relaxed_wins >= 1
 
 
 def test_relaxed_zero_delta_is_greedy_and_large_delta_keeps_all(env, gpu_ar):
