@@ -373,6 +373,60 @@ int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t*
   return hip_status(launch_forward(a));
 }
 
+// ---------------------------------------------------------------------------
+// The decode step without a workspace argument, for callers that cannot
+// allocate.  Its scratch is a file-scope device array: each GPU the library
+// runs on holds its own copy until the process ends.  In host code the
+// array's name is not a device address; the address comes from
+// hipGetSymbolAddress once per device (specdec_static_init) and only that
+// pointer is passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+int specdec_static_init(void* stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return SPECDEC_EUNSUPPORTED;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_status(e);
+  if (!ptr) return SPECDEC_EHIP;
+  // the split-K launch sequence numbers and partial tags start at zero
+  zero_fill_kernel<<<1024, 256, 0, (hipStream_t)stream>>>(static_cast<uint4*>(ptr), kStaticScratchBytes / 16);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_status(e);
+  g_scratch_ptr[dev] = ptr;
+  return SPECDEC_OK;
+}
+
+int specdec_decode_step_noalloc(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t rows,
+                                float* d_logits, int32_t* d_argmax, float* d_lse, int32_t* d_err, void* stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices || !g_scratch_ptr[dev]) return SPECDEC_EINVAL;   // specdec_static_init first
+  WsPlan plan;
+  int rc = check_fwd(m, c, rows, kStaticScratchBytes, &plan);   // ECAPACITY past the scratch's size
+  if (rc) return rc;
+  if (!d_tokens || !d_err) return SPECDEC_EINVAL;
+  char* ws = static_cast<char*>(g_scratch_ptr[dev]);
+  FwdArgs a;
+  a.m = m; a.c = c; a.tokens = d_tokens; a.rows = rows;
+  a.logits = d_logits ? d_logits : reinterpret_cast<float*>(ws + plan.logits);
+  a.argmax = d_argmax; a.lse = d_lse; a.ws = ws; a.plan = &plan;
+  a.stream = (hipStream_t)stream; a.gate = nullptr; a.skip_head = false; a.err = d_err;
+  return hip_status(launch_forward(a));
+}
+
 int specdec_prefill(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t n, int32_t chunk,
                     float* d_last_logits, int32_t* d_last_argmax, float* d_last_lse, void* d_ws, size_t ws_bytes,
                     void* stream) {
@@ -511,7 +565,7 @@ int specdec_round_create(const specdec_round_desc* desc, specdec_round** out) {
   v.tsmax = reinterpret_cast<float*>(w + rp.tsmax);
   v.tssum = reinterpret_cast<float*>(w + rp.tssum);
   v.hcnt = reinterpret_cast<int32_t*>(w + rp.hcnt);
-  v.hmass = reinterpret_cast<double*>(w + rp.hmass);
+  v.hmass = reinterpret_cast<uint64_t*>(w + rp.hmass);
   v.trunc = reinterpret_cast<TruncState*>(w + rp.trunc);
   v.t_len = q.target_cache->d_len;
   v.d_len = q.draft_source == SPECDEC_DRAFT_MODEL ? q.draft_cache->d_len : nullptr;
@@ -762,9 +816,9 @@ int specdec_round_debug_view(const specdec_round* r, int32_t which, void** d_ptr
   return SPECDEC_OK;
 }
 
-int specdec_stream_read(const void* d_buf, size_t bytes, uint32_t* d_sink, void* stream) {
-  if (!d_buf || !d_sink || bytes == 0 || bytes % 16) return SPECDEC_EINVAL;
-  return hip_status(launch_stream_read(d_buf, bytes, d_sink, (hipStream_t)stream));
+int specdec_stream_read(const void* d_buf, size_t bytes, int32_t workgroups, uint32_t* d_sink, void* stream) {
+  if (!d_buf || !d_sink || bytes == 0 || bytes % 16 || workgroups < 1 || workgroups > 65536) return SPECDEC_EINVAL;
+  return hip_status(launch_stream_read(d_buf, bytes, workgroups, d_sink, (hipStream_t)stream));
 }
 
 // Test hook: Philox4x64-10 words for n (counter, key) pairs (device arrays).

@@ -121,6 +121,7 @@ struct FwdArgs {
   hipStream_t stream;
   const int32_t* gate;   // optional device flag: when *gate == 0 every kernel returns at once
   bool skip_head;        // prefill chunks before the last: no LM head, only the length advance
+  int32_t* err = nullptr;   // sticky error word; null: the word at the workspace's start
 };
 hipError_t launch_forward(const FwdArgs& a);
 
@@ -144,7 +145,7 @@ hipError_t launch_pack_q4(const void* src, int rows, int K, int kind, int hd, in
 size_t q4_lds_bytes(int rows, int K, int nsplit);
 hipError_t launch_pack(const Dims& d, int index, const void* src, void* blob, const BlobLayout& lay, hipStream_t s);
 hipError_t launch_trim(int32_t* d_len, int32_t new_len, const int32_t* d_base, int32_t* err, hipStream_t s);
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, hipStream_t s);
 
 // Round kernels (kernels_round.hip).
 struct RoundDev;  // defined in api.cpp

@@ -1000,7 +1000,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
   const Dims& d = a.m->d;
   const WsPlan& pl = *a.plan;
   char* ws = a.ws;
-  int32_t* err = reinterpret_cast<int32_t*>(ws + pl.err);
+  int32_t* err = a.err ? a.err : reinterpret_cast<int32_t*>(ws + pl.err);
   float* x = reinterpret_cast<float*>(ws + pl.x);
   bf16_bits* xb = reinterpret_cast<bf16_bits*>(ws + pl.xb);
   float* ss = reinterpret_cast<float*>(ws + pl.ss);
@@ -1086,8 +1086,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const i32x4_t* __restr
   if (x == 0x9E3779B9u) sink[0] = x;
 }
 
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
-  stream_read_kernel<<<2048, 256, 0, s>>>(static_cast<const i32x4_t*>(buf), bytes / 16, sink);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, hipStream_t s) {
+  stream_read_kernel<<<workgroups, 256, 0, s>>>(static_cast<const i32x4_t*>(buf), bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ EXPORTED = [
     "specdec_round_destroy", "specdec_round_prefill", "specdec_round_reset", "specdec_verify_round",
     "specdec_check", "specdec_last_hip_error", "specdec_status_str", "specdec_philox4x64",
     "specdec_round_graph", "specdec_round_graph_launch", "specdec_round_debug_view", "specdec_stream_read",
+    "specdec_decode_step_noalloc", "specdec_static_init",
 ]
 
 
@@ -101,7 +102,9 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
         "specdec_round_graph": (C.c_int, [vp]),
         "specdec_round_graph_launch": (C.c_int, [vp, i32, vp]),
         "specdec_round_debug_view": (C.c_int, [vp, i32, P(vp), P(sz)]),
-        "specdec_stream_read": (C.c_int, [vp, sz, vp, vp]),
+        "specdec_stream_read": (C.c_int, [vp, sz, i32, vp, vp]),
+        "specdec_decode_step_noalloc": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+        "specdec_static_init": (C.c_int, [vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -259,6 +262,18 @@ def decode_step(model: Model, cache: Cache, tokens: torch.Tensor, ws: Workspace,
           "decode_step")
 
 
+def static_init(stream=None) -> None:
+    check(lib().specdec_static_init(_stream(stream)), "static_init")
+
+
+def decode_step_noalloc(model: Model, cache: Cache, tokens: torch.Tensor, err: torch.Tensor, logits=None,
+                        argmax=None, lse=None, rows=None, stream=None) -> None:
+    rows = int(tokens.numel()) if rows is None else rows
+    check(lib().specdec_decode_step_noalloc(model.handle, cache.handle, tokens.data_ptr(), rows, _ptr(logits),
+                                            _ptr(argmax), _ptr(lse), err.data_ptr(), _stream(stream)),
+          "decode_step_noalloc")
+
+
 def prefill(model: Model, cache: Cache, tokens: torch.Tensor, ws: Workspace, chunk: int = MAX_ROWS,
             logits=None, argmax=None, lse=None, stream=None) -> None:
     check(lib().specdec_prefill(model.handle, cache.handle, tokens.data_ptr(), int(tokens.numel()), chunk,
@@ -266,9 +281,9 @@ def prefill(model: Model, cache: Cache, tokens: torch.Tensor, ws: Workspace, chu
                                 _stream(stream)), "prefill")
 
 
-def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 2048, stream=None) -> None:
     """Read every byte of `buf` once (the stream-read ceiling probe)."""
-    check(lib().specdec_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+    check(lib().specdec_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), workgroups, sink.data_ptr(),
                                     _stream(stream)), "stream_read")
 
 

@@ -176,6 +176,29 @@ int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t*
                         float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
                         void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid device allocation): the decode step
+ * above without a workspace argument.  Its scratch (activations, attention
+ * and LM-head partials, split-K hand-off words) is a device array of
+ * 128 MiB inside the library, one per GPU, held until the process ends; a
+ * forward whose workspace (specdec_workspace_bytes) exceeds it returns
+ * SPECDEC_ECAPACITY.  Device-detected errors are OR-ed into the caller's
+ * device int32 *d_err (required; the caller clears it).  Other arguments as
+ * for specdec_decode_step.  Every call on one GPU shares that GPU's array
+ * and keeps the last call's contents: calls that overlap on one GPU (two
+ * streams, two threads) race; enqueue them on one stream.  No device memory
+ * is allocated or freed.  specdec_static_init must have run on the current
+ * device first (SPECDEC_EINVAL otherwise). */
+int specdec_decode_step_noalloc(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t rows,
+                                float* d_logits, int32_t* d_argmax, float* d_lse, int32_t* d_err, void* stream);
+
+/* Set-up of specdec_decode_step_noalloc on the current device: looks up the
+ * device address of the library's scratch array and clears it (a fill
+ * kernel on `stream`, not captured: call it once per device outside any
+ * graph capture, before the first allocation-free step).  Calling it again
+ * clears the array again. */
+int specdec_static_init(void* stream);
+
 /* Prefill `n` tokens in passes of `chunk` rows (chunk clipped to
  * SPECDEC_MAX_ROWS, or to 4 for a 4-bit model), starting at the current
  * length.  Writes the last row's
@@ -314,11 +337,12 @@ const char* specdec_status_str(int status);
 
 /* Measurement helper, not a step of the path: read `bytes` (a multiple of
  * 16) of device memory at d_buf once, with the same non-temporal 16-byte
- * loads the weight stream uses, on `stream`.  d_sink is a device uint32 the
- * kernel may write (keeps the loads live).  Timing this read over a buffer
- * far larger than the caches gives the measured stream-read ceiling that
- * achieved HBM bandwidth is reported against next to the published peak. */
-int specdec_stream_read(const void* d_buf, size_t bytes, uint32_t* d_sink, void* stream);
+ * loads the weight stream uses, by `workgroups` (1..65536) workgroups of
+ * 256 threads, on `stream`.  d_sink is a device uint32 the kernel may write
+ * (keeps the loads live).  Timing this read over a buffer far larger than
+ * the caches gives the measured stream-read ceiling that achieved HBM
+ * bandwidth is reported against next to the published peak. */
+int specdec_stream_read(const void* d_buf, size_t bytes, int32_t workgroups, uint32_t* d_sink, void* stream);
 
 #ifdef __cplusplus
 }
