@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libspecdec.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "kernels_forward.hip", "kernels_round.hip", "kernels_q4.hip"]
+SOURCES = ["api.hip", "kernels_forward.hip", "kernels_round.hip", "kernels_q4.hip", "kernels_tree.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 arithmetic stays off on the device

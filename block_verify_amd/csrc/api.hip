@@ -106,6 +106,7 @@ WsPlan ws_plan(const Dims& d, int max_rows, int max_len) {
   p.lm_part = take(R * p.lm_wgs * 3 * 4);
   p.toks = take(R * 4 * 2);
   p.logits = take(R * (size_t)d.V * 4);
+  p.tree = take(2 * R * 4);   // tree forward: depth and ancestor mask per row
   p.total = off;
   return p;
 }
@@ -371,6 +372,30 @@ int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t*
   a.argmax = d_argmax; a.lse = d_lse; a.ws = static_cast<char*>(d_ws); a.plan = &plan;
   a.stream = (hipStream_t)stream; a.gate = nullptr; a.skip_head = false;
   return hip_status(launch_forward(a));
+}
+
+int specdec_tree_verify(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents,
+                        int32_t rows, float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
+                        void* stream) {
+  WsPlan plan;
+  int rc = check_fwd(m, c, rows, ws_bytes, &plan);
+  if (rc) return rc;
+  if (!d_tokens || !d_parents || !d_ws) return SPECDEC_EINVAL;
+  FwdArgs a;
+  a.m = m; a.c = c; a.tokens = d_tokens; a.rows = rows;
+  a.logits = d_logits ? d_logits : reinterpret_cast<float*>(static_cast<char*>(d_ws) + plan.logits);
+  a.argmax = d_argmax; a.lse = d_lse; a.ws = static_cast<char*>(d_ws); a.plan = &plan;
+  a.stream = (hipStream_t)stream; a.gate = nullptr; a.skip_head = false; a.parents = d_parents;
+  return hip_status(launch_forward(a));
+}
+
+int specdec_tree_accept(specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents, int32_t rows,
+                        const int32_t* d_argmax, int32_t* d_out_tokens, int32_t* d_out_count, int32_t* d_err,
+                        void* stream) {
+  if (!c || !d_tokens || !d_parents || !d_argmax || !d_out_tokens || !d_out_count || !d_err) return SPECDEC_EINVAL;
+  if (rows < 1 || rows > SPECDEC_MAX_ROWS) return SPECDEC_ECAPACITY;
+  return hip_status(launch_tree_accept(c, d_tokens, d_parents, rows, d_argmax, d_out_tokens, d_out_count, d_err,
+                                       (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -149,6 +149,7 @@ enum : int32_t {
   kErrTable = 8,        // draft table / noise read past its end
   kErrOutput = 16,      // committed-token buffer full
   kErrSync = 32,        // a split-K hand-off waited past its bound
+  kErrTree = 64,        // a tree row's parent is not an earlier row
 };
 
 __device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {

@@ -45,6 +45,7 @@ struct GemvParams {
   const float2* rope;
   const int32_t* d_len;
   int max_len;           // cache capacity (positions)
+  const int32_t* tree_depth;   // tree forward: depth of each row (its RoPE position is pos0 + depth), else null
   int kv_stride;         // padded positions per head (K rows; V^T row length)
   int nq, nkv, hd;
   // RESID
@@ -141,6 +142,8 @@ __device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, in
 
 // QKV: the rotation pairs of this query/key group at positions pos0 + m
 // (idx = 8 m + i, i = lane % 8); pos0 is the cache length read at launch.
+// A tree forward rotates row m by its depth instead (pos0 + depth[m]); its
+// K/V still go to slot pos0 + m.
 template <Epi E, int NC>
 __device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane, int g, int M, EpiPre<NC>& pre) {
   if constexpr (E == Epi::QKV) {
@@ -149,8 +152,11 @@ __device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane,
       const int sub = (g >= qg ? g - qg : g) % (p.hd / 16), half = p.hd / 2;
 #pragma unroll
       for (int j = 0; j < EpiPre<NC>::kR; ++j) {
-        const int idx = lane + 64 * j, m = idx >> 3, pos = pre.pos0 + m;
-        if (m < M && pos < p.max_len) pre.cs[j] = p.rope[(size_t)pos * half + 8 * sub + (idx & 7)];
+        const int idx = lane + 64 * j, m = idx >> 3, slot = pre.pos0 + m;
+        if (m < M && slot < p.max_len) {
+          const int pos = p.tree_depth ? pre.pos0 + p.tree_depth[m] : slot;
+          pre.cs[j] = p.rope[(size_t)pos * half + 8 * sub + (idx & 7)];
+        }
       }
     }
   }

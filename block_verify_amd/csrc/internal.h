@@ -102,7 +102,7 @@ constexpr unsigned kSplit0Share = 30;
 
 // Workspace plan for one model.
 struct WsPlan {
-  size_t err, cnt, x, xb, ss, qb, ob, hb, att_o, att_ml, part, lm_part, toks, logits, total;
+  size_t err, cnt, x, xb, ss, qb, ob, hb, att_o, att_ml, part, lm_part, toks, logits, tree, total;
   int max_rows, nt, max_chunks, lm_wgs;
 };
 WsPlan ws_plan(const Dims& d, int max_rows, int max_len);
@@ -122,6 +122,7 @@ struct FwdArgs {
   const int32_t* gate;   // optional device flag: when *gate == 0 every kernel returns at once
   bool skip_head;        // prefill chunks before the last: no LM head, only the length advance
   int32_t* err = nullptr;   // sticky error word; null: the word at the workspace's start
+  const int32_t* parents = nullptr;   // tree forward: each row's parent row (-1: none), else a causal block
 };
 hipError_t launch_forward(const FwdArgs& a);
 
@@ -146,6 +147,10 @@ size_t q4_lds_bytes(int rows, int K, int nsplit);
 hipError_t launch_pack(const Dims& d, int index, const void* src, void* blob, const BlobLayout& lay, hipStream_t s);
 hipError_t launch_trim(int32_t* d_len, int32_t new_len, const int32_t* d_base, int32_t* err, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, hipStream_t s);
+// Tree acceptance (kernels_tree.hip): longest greedy path, K/V compaction, commit.
+hipError_t launch_tree_accept(const specdec_cache* c, const int32_t* tokens, const int32_t* parents, int rows,
+                              const int32_t* argmax, int32_t* out_tokens, int32_t* out_count, int32_t* err,
+                              hipStream_t s);
 
 // Round kernels (kernels_round.hip).
 struct RoundDev;  // defined in api.cpp

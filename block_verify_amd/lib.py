@@ -18,7 +18,7 @@ from .shapes import ModelShape
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecdec.so")
 
 OK, EINVAL, ECAPACITY, ESHAPE, EHIP, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-DERR_CAPACITY, DERR_TRIM, DERR_NONFINITE, DERR_TABLE, DERR_OUTPUT, DERR_SYNC = 1, 2, 4, 8, 16, 32
+DERR_CAPACITY, DERR_TRIM, DERR_NONFINITE, DERR_TABLE, DERR_OUTPUT, DERR_SYNC, DERR_TREE = 1, 2, 4, 8, 16, 32, 64
 W_BF16, W_Q4G64 = 0, 1
 GREEDY, STOCHASTIC, RELAXED = 0, 1, 2
 SCHEDULE_A, SCHEDULE_B = 0, 1
@@ -34,7 +34,7 @@ EXPORTED = [
     "specdec_round_destroy", "specdec_round_prefill", "specdec_round_reset", "specdec_verify_round",
     "specdec_check", "specdec_last_hip_error", "specdec_status_str", "specdec_philox4x64",
     "specdec_round_graph", "specdec_round_graph_launch", "specdec_round_debug_view", "specdec_stream_read",
-    "specdec_decode_step_noalloc", "specdec_static_init",
+    "specdec_decode_step_noalloc", "specdec_static_init", "specdec_tree_verify", "specdec_tree_accept",
 ]
 
 
@@ -105,6 +105,8 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
         "specdec_stream_read": (C.c_int, [vp, sz, i32, vp, vp]),
         "specdec_decode_step_noalloc": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "specdec_static_init": (C.c_int, [vp]),
+        "specdec_tree_verify": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+        "specdec_tree_accept": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -260,6 +262,20 @@ def decode_step(model: Model, cache: Cache, tokens: torch.Tensor, ws: Workspace,
     check(lib().specdec_decode_step(model.handle, cache.handle, tokens.data_ptr(), rows, _ptr(logits),
                                     _ptr(argmax), _ptr(lse), ws.mem.data_ptr(), ws.nbytes, _stream(stream)),
           "decode_step")
+
+
+def tree_verify(model: Model, cache: Cache, tokens: torch.Tensor, parents: torch.Tensor, ws: Workspace, logits=None,
+                argmax=None, lse=None, stream=None) -> None:
+    check(lib().specdec_tree_verify(model.handle, cache.handle, tokens.data_ptr(), parents.data_ptr(),
+                                    int(tokens.numel()), _ptr(logits), _ptr(argmax), _ptr(lse), ws.mem.data_ptr(),
+                                    ws.nbytes, _stream(stream)), "tree_verify")
+
+
+def tree_accept(cache: Cache, tokens: torch.Tensor, parents: torch.Tensor, argmax: torch.Tensor,
+                out_tokens: torch.Tensor, out_count: torch.Tensor, err: torch.Tensor, stream=None) -> None:
+    check(lib().specdec_tree_accept(cache.handle, tokens.data_ptr(), parents.data_ptr(), int(tokens.numel()),
+                                    argmax.data_ptr(), out_tokens.data_ptr(), out_count.data_ptr(), err.data_ptr(),
+                                    _stream(stream)), "tree_accept")
 
 
 def static_init(stream=None) -> None:

@@ -63,7 +63,8 @@ enum {
   SPECDEC_DERR_NONFINITE = 4,  /* non-finite logits */
   SPECDEC_DERR_TABLE = 8,      /* draft table or noise read past its end */
   SPECDEC_DERR_OUTPUT = 16,    /* committed-token buffer full (tokens dropped) */
-  SPECDEC_DERR_SYNC = 32       /* a split-K hand-off inside a forward waited past its bound */
+  SPECDEC_DERR_SYNC = 32,      /* a split-K hand-off inside a forward waited past its bound */
+  SPECDEC_DERR_TREE = 64       /* a tree row's parent is not an earlier row (the row is taken as a root) */
 };
 
 enum { SPECDEC_W_BF16 = 0, SPECDEC_W_Q4G64 = 1 };
@@ -174,6 +175,33 @@ int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream);
  * (SPECDEC_ECAPACITY beyond). */
 int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t rows,
                         float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
+                        void* stream);
+
+/* Draft-tree verify ("SubSpec" summary, jjl357.github.io, section 4.2: a
+ * context-aware tree of draft tokens verified in one target forward).  A
+ * forward of `rows` (1..SPECDEC_MAX_ROWS) tree nodes at the current length
+ * t: d_parents int32 [rows] holds each row's parent row (an earlier row), or
+ * -1 for a row whose parent is the last cached position.  Row i runs at
+ * position t + depth(i), attends to the cached positions and to its
+ * ancestors-or-self among the rows only, and appends its K/V at slot t + i;
+ * then length += rows.  Outputs and workspace as for specdec_decode_step
+ * (a chain, d_parents = -1, 0, 1, ..., computes exactly the block verify).
+ * A parent that is not an earlier row sets SPECDEC_DERR_TREE. */
+int specdec_tree_verify(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents,
+                        int32_t rows, float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
+                        void* stream);
+
+/* Greedy acceptance of a verified tree (after specdec_tree_verify on the same
+ * tokens / parents, row 0 being the root: the round's pending token).  From
+ * the root, the first child in row order whose token is the target's argmax
+ * (d_argmax [rows], the verify's output) continues the accepted path; the
+ * walk stops at a row with no such child.  The path's K/V move to slots
+ * t+1 .. t+m (every layer), the root stays at slot t, the length becomes
+ * t + 1 + m.  d_out_tokens int32 [rows] receives the path's tokens then the
+ * target's choice at its end (the next pending token), *d_out_count = m + 1.
+ * A length below rows sets SPECDEC_DERR_TRIM in *d_err and changes nothing. */
+int specdec_tree_accept(specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents, int32_t rows,
+                        const int32_t* d_argmax, int32_t* d_out_tokens, int32_t* d_out_count, int32_t* d_err,
                         void* stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, tight

@@ -212,3 +212,56 @@ def test_stochastic_4k_rounds_match_oracle(big):
     say(f"4K stochastic: {len(ms)} rounds, accepted {ms}, {exempt} boundary exemptions, "
         f"{checked} rounds teacher-forced against the oracle")
     assert exempt <= 2
+
+
+def test_tree_verify_and_accept_29_nodes(big):
+    """A draft tree of 4 nodes a level over 7 levels (29 rows with the root, the shape of
+    the context-aware tree with k = 4, D = 7) at 2K: logits against the oracle's
+    tree-causal forward, the accepted path against the oracle rule on the GPU's argmax,
+    and the compacted K/V as bit copies of the tree forward's rows."""
+    from oracle.model import forward
+    from oracle.tree import tree_accept_greedy, tree_forward
+    b, S = big["b"], big["S"]
+    rng = np.random.default_rng(29)
+    pars, level = [-1], [0]
+    for _ in range(7):
+        nxt = []
+        for _ in range(4):
+            pars.append(int(rng.choice(level)))
+            nxt.append(len(pars) - 1)
+        level = nxt
+    n = len(pars)
+    toks = rng.integers(0, S.vocab, n).astype(np.int32)
+    # the root's first child carries the root's argmax, so the path has at least one node
+    oc0 = big["oc"].clone()
+    toks[1] = int(np.argmax(forward(big["ow"], oc0, toks[:1])[0]))
+    t, p = torch.from_numpy(toks).cuda(), torch.from_numpy(np.asarray(pars, np.int32)).cuda()
+    lg = torch.empty((n, S.vocab), dtype=torch.float32, device="cuda")
+    am = torch.empty(n, dtype=torch.int32, device="cuda")
+    b.tree_verify(big["model"], big["cache"], t, p, big["ws"], logits=lg, argmax=am)
+    kk, vv = big["cache"].kv()
+    before = [(kk[l][:, P:P + n].clone(), vv[l][:, P:P + n].clone()) for l in (0, S.n_layers - 1)]
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    b.tree_accept(big["cache"], t, p, am, out, cnt, err)
+    gam = to_np(am)
+    path, com = tree_accept_greedy(toks, pars, list(gam))
+    m = big["cache"].length() - P - 1
+    after = [(kk[l][:, P:P + 1 + m].clone(), vv[l][:, P:P + 1 + m].clone()) for l in (0, S.n_layers - 1)]
+    big["cache"].trim(P, big["ws"])
+    ol = tree_forward(big["ow"], big["oc"].clone(), toks, pars)
+    g = to_np(lg)
+    assert_logits_close(g, ol, "1.5B tree verify (29 rows)")
+    assert np.array_equal(gam, g.argmax(axis=1))
+    exempt = sum(oracle_margin(ol[i]) < MARGIN for i in range(n))
+    for i in range(n):
+        if oracle_margin(ol[i]) >= MARGIN:
+            assert gam[i] == int(np.argmax(ol[i]))
+    assert m == len(path) >= 1 and int(cnt.item()) == len(com)
+    assert [int(x) for x in to_np(out)[:len(com)]] == com and int(err.item()) == 0
+    for (k0, v0), (k1, v1) in zip(before, after):
+        for dst, src in enumerate([0] + path):
+            assert torch.equal(k1[:, dst], k0[:, src]) and torch.equal(v1[:, dst], v0[:, src])
+    assert big["ws"].error_bits() == 0
+    say(f"1.5B tree: path {path}, committed {com}, {exempt} rows with oracle margin < {MARGIN}")
