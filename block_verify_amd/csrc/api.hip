@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <cmath>
+
 #include <new>
 #include <vector>
 
@@ -106,7 +108,7 @@ WsPlan ws_plan(const Dims& d, int max_rows, int max_len) {
   p.lm_part = take(R * p.lm_wgs * 3 * 4);
   p.toks = take(R * 4 * 2);
   p.logits = take(R * (size_t)d.V * 4);
-  p.tree = take(2 * R * 4);   // tree forward: depth and ancestor mask per row
+  p.tree = take((R + R * kTreeWords) * 4);   // tree forward: depth and ancestor mask per row
   p.total = off;
   return p;
 }
@@ -375,27 +377,82 @@ int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t*
 }
 
 int specdec_tree_verify(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents,
-                        int32_t rows, float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
+                        int32_t n, float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
                         void* stream) {
+  if (!m) return SPECDEC_EINVAL;
+  if (n < 1 || n > SPECDEC_MAX_TREE) return SPECDEC_ECAPACITY;
+  const int pass = m->d.wfmt == SPECDEC_W_Q4G64 ? kQ4MaxRows : kMaxRows;
   WsPlan plan;
-  int rc = check_fwd(m, c, rows, ws_bytes, &plan);
+  int rc = check_fwd(m, c, n < pass ? n : pass, ws_bytes, &plan);
   if (rc) return rc;
   if (!d_tokens || !d_parents || !d_ws) return SPECDEC_EINVAL;
-  FwdArgs a;
-  a.m = m; a.c = c; a.tokens = d_tokens; a.rows = rows;
-  a.logits = d_logits ? d_logits : reinterpret_cast<float*>(static_cast<char*>(d_ws) + plan.logits);
-  a.argmax = d_argmax; a.lse = d_lse; a.ws = static_cast<char*>(d_ws); a.plan = &plan;
-  a.stream = (hipStream_t)stream; a.gate = nullptr; a.skip_head = false; a.parents = d_parents;
-  return hip_status(launch_forward(a));
+  // passes of up to `pass` nodes in node order: a node's ancestors are
+  // earlier nodes, so their K/V are in the cache when its pass runs
+  for (int n0 = 0; n0 < n; n0 += pass) {
+    FwdArgs a;
+    a.m = m; a.c = c; a.tokens = d_tokens + n0; a.rows = n - n0 < pass ? n - n0 : pass;
+    a.logits = d_logits ? d_logits + (size_t)n0 * m->d.V
+                        : reinterpret_cast<float*>(static_cast<char*>(d_ws) + plan.logits);
+    a.argmax = d_argmax ? d_argmax + n0 : nullptr;
+    a.lse = d_lse ? d_lse + n0 : nullptr;
+    a.ws = static_cast<char*>(d_ws); a.plan = &plan;
+    a.stream = (hipStream_t)stream; a.gate = nullptr; a.skip_head = false;
+    a.parents = d_parents; a.tree_n0 = n0;
+    rc = hip_status(launch_forward(a));
+    if (rc) return rc;
+  }
+  return SPECDEC_OK;
 }
 
-int specdec_tree_accept(specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents, int32_t rows,
-                        const int32_t* d_argmax, int32_t* d_out_tokens, int32_t* d_out_count, int32_t* d_err,
-                        void* stream) {
+int specdec_tree_accept(specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents, int32_t n,
+                        const int32_t* d_argmax, int32_t* d_out_tokens, int32_t* d_out_count, int32_t* d_root,
+                        int32_t* d_log, int32_t log_cap, int32_t* d_err, void* stream) {
   if (!c || !d_tokens || !d_parents || !d_argmax || !d_out_tokens || !d_out_count || !d_err) return SPECDEC_EINVAL;
-  if (rows < 1 || rows > SPECDEC_MAX_ROWS) return SPECDEC_ECAPACITY;
-  return hip_status(launch_tree_accept(c, d_tokens, d_parents, rows, d_argmax, d_out_tokens, d_out_count, d_err,
-                                       (hipStream_t)stream));
+  if (n < 1 || n > SPECDEC_MAX_TREE) return SPECDEC_ECAPACITY;
+  if (d_log && log_cap < 0) return SPECDEC_EINVAL;
+  return hip_status(launch_tree_accept(c, d_tokens, d_parents, n, d_argmax, d_out_tokens, d_out_count, d_root, d_log,
+                                       d_log ? log_cap : 0, d_err, (hipStream_t)stream));
+}
+
+int specdec_tree_draft(const specdec_model* draft, specdec_cache* c, const int32_t* d_root, int32_t k,
+                       int32_t depth, float temperature, int32_t* d_tokens, int32_t* d_parents, float* d_scores,
+                       void* d_ws, size_t ws_bytes, void* stream) {
+  if (!draft || !c || !d_root || !d_tokens || !d_parents || !d_scores || !d_ws) return SPECDEC_EINVAL;
+  if (k < 1 || k > SPECDEC_MAX_K || k > draft->d.V || depth < 1) return SPECDEC_EINVAL;
+  if (1 + (long)k * depth > SPECDEC_MAX_TREE) return SPECDEC_ECAPACITY;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return SPECDEC_EINVAL;
+  const int pass = draft->d.wfmt == SPECDEC_W_Q4G64 ? kQ4MaxRows : kMaxRows;
+  WsPlan plan;
+  int rc = check_fwd(draft, c, k < pass ? k : pass, ws_bytes, &plan);
+  if (rc) return rc;
+  const int V = draft->d.V;
+  char* ws = static_cast<char*>(d_ws);
+  // the leaves' logits in the first SPECDEC_MAX_K rows of the workspace's
+  // logits region, the selection's partials after them
+  float* leaf = reinterpret_cast<float*>(ws + plan.logits);
+  float* scratch = leaf + (size_t)SPECDEC_MAX_K * V;
+  if (tree_select_scratch_bytes(k, V, k) > (size_t)(kMaxRows - SPECDEC_MAX_K) * V * sizeof(float))
+    return SPECDEC_ECAPACITY;
+  int32_t* saved = reinterpret_cast<int32_t*>(ws + plan.toks);
+  hipStream_t s = (hipStream_t)stream;
+  rc = hip_status(launch_tree_root(d_root, c->d_len, saved, d_tokens, d_parents, d_scores, s));
+  const float inv_t = 1.0f / temperature;
+  for (int st = 0; st < depth && !rc; ++st) {
+    const int r = st == 0 ? 1 : k, n0 = st == 0 ? 0 : 1 + (st - 1) * k;
+    for (int j0 = 0; j0 < r && !rc; j0 += pass) {
+      FwdArgs a;
+      a.m = draft; a.c = c; a.tokens = d_tokens + n0 + j0; a.rows = r - j0 < pass ? r - j0 : pass;
+      a.logits = leaf + (size_t)j0 * V; a.argmax = nullptr; a.lse = nullptr;
+      a.ws = ws; a.plan = &plan; a.stream = s; a.gate = nullptr; a.skip_head = false;
+      a.parents = d_parents; a.tree_n0 = n0 + j0;
+      rc = hip_status(launch_forward(a));
+    }
+    if (!rc)
+      rc = hip_status(launch_tree_select(leaf, r, V, k, inv_t, n0, 1 + st * k, scratch, d_tokens, d_parents, d_scores,
+                                         s));
+  }
+  if (!rc) rc = hip_status(launch_tree_restore(c->d_len, saved, s));
+  return rc;
 }
 
 // ---------------------------------------------------------------------------

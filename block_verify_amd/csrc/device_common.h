@@ -33,6 +33,10 @@ constexpr int kTileU16 = 512;       // bf16 elements per tile
 constexpr int kColsPerTile = 8;     // activation rows per column tile
 constexpr int kMaxRows = 32;        // rows per forward pass
 constexpr int kMaxNT = kMaxRows / kColsPerTile;
+// Draft trees: nodes of one tree (its forwards take at most kMaxRows of them
+// at a time) and the 32-bit words of a node's ancestor mask.
+constexpr int kMaxTreeNodes = 512;
+constexpr int kTreeWords = kMaxTreeNodes / 32;
 
 __device__ __forceinline__ float bf2f(bf16_bits b) {
   return __uint_as_float(((uint32_t)b) << 16);

@@ -45,7 +45,7 @@ struct GemvParams {
   const float2* rope;
   const int32_t* d_len;
   int max_len;           // cache capacity (positions)
-  const int32_t* tree_depth;   // tree forward: depth of each row (its RoPE position is pos0 + depth), else null
+  const int32_t* tree_depth;   // tree forward: per row, its RoPE position minus pos0 (a depth offset), else null
   int kv_stride;         // padded positions per head (K rows; V^T row length)
   int nq, nkv, hd;
   // RESID
@@ -142,8 +142,8 @@ __device__ __forceinline__ void epi_prefetch_x(const GemvParams& p, int lane, in
 
 // QKV: the rotation pairs of this query/key group at positions pos0 + m
 // (idx = 8 m + i, i = lane % 8); pos0 is the cache length read at launch.
-// A tree forward rotates row m by its depth instead (pos0 + depth[m]); its
-// K/V still go to slot pos0 + m.
+// A tree forward rotates row m at pos0 + tree_depth[m] (the tree's base
+// slot plus the node's depth) instead; its K/V still go to slot pos0 + m.
 template <Epi E, int NC>
 __device__ __forceinline__ void epi_prefetch_rope(const GemvParams& p, int lane, int g, int M, EpiPre<NC>& pre) {
   if constexpr (E == Epi::QKV) {

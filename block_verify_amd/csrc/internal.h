@@ -122,7 +122,8 @@ struct FwdArgs {
   const int32_t* gate;   // optional device flag: when *gate == 0 every kernel returns at once
   bool skip_head;        // prefill chunks before the last: no LM head, only the length advance
   int32_t* err = nullptr;   // sticky error word; null: the word at the workspace's start
-  const int32_t* parents = nullptr;   // tree forward: each row's parent row (-1: none), else a causal block
+  const int32_t* parents = nullptr;   // tree forward: each node's parent node (-1: none), else a causal block
+  int tree_n0 = 0;                    // tree forward: the node of row 0 (nodes before it are in the cache)
 };
 hipError_t launch_forward(const FwdArgs& a);
 
@@ -147,10 +148,18 @@ size_t q4_lds_bytes(int rows, int K, int nsplit);
 hipError_t launch_pack(const Dims& d, int index, const void* src, void* blob, const BlobLayout& lay, hipStream_t s);
 hipError_t launch_trim(int32_t* d_len, int32_t new_len, const int32_t* d_base, int32_t* err, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, hipStream_t s);
-// Tree acceptance (kernels_tree.hip): longest greedy path, K/V compaction, commit.
-hipError_t launch_tree_accept(const specdec_cache* c, const int32_t* tokens, const int32_t* parents, int rows,
-                              const int32_t* argmax, int32_t* out_tokens, int32_t* out_count, int32_t* err,
-                              hipStream_t s);
+// Draft trees (kernels_tree.hip): selection of a construction step (the k
+// best (leaf, token) pairs of r leaves' logits), its first and last steps,
+// and the greedy acceptance (longest path, K/V compaction, commit).
+hipError_t launch_tree_select(const float* logits, int r, int V, int k, float inv_t, int n0, int n_new,
+                              float* scratch, int32_t* tokens, int32_t* parents, float* scores, hipStream_t s);
+size_t tree_select_scratch_bytes(int r, int V, int k);
+hipError_t launch_tree_root(const int32_t* root, const int32_t* d_len, int32_t* saved, int32_t* tokens,
+                            int32_t* parents, float* scores, hipStream_t s);
+hipError_t launch_tree_restore(int32_t* d_len, const int32_t* saved, hipStream_t s);
+hipError_t launch_tree_accept(const specdec_cache* c, const int32_t* tokens, const int32_t* parents, int n,
+                              const int32_t* argmax, int32_t* out_tokens, int32_t* out_count, int32_t* root,
+                              int32_t* log, int log_cap, int32_t* err, hipStream_t s);
 
 // Round kernels (kernels_round.hip).
 struct RoundDev;  // defined in api.cpp

@@ -148,36 +148,42 @@ hipError_t launch_pack(const Dims& d, int index, const void* srcv, void* blobv, 
 // Embedding gather: x = E[token]; writes x, the activation tiles of
 // x * gain (first attention norm) and the per-16-feature sums of squares.
 // ---------------------------------------------------------------------------
-// Tree forwards (parents non-null): thread 0 of row m's workgroup walks the
-// row's parent chain and stores its depth and the mask of its ancestors-or-
-// self among the block's rows (a parent must be an earlier row; otherwise the
-// row is flagged and taken as a root).
+// Tree forwards (parents non-null): row m is node n0 + m of a tree whose
+// nodes 0 .. n0 - 1 already sit in the cache (node i at slot base + i, base =
+// length - n0).  Its workgroup stores depth - n0 (so that the row's RoPE
+// position is length + that = base + depth) and the node's ancestors-or-self
+// as a kMaxTreeNodes-bit mask over the tree's nodes; thread w < kTreeWords
+// walks the parent chain for word w.  A parent must be an earlier node:
+// otherwise the row is flagged and taken as a root.
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens, const bf16_bits* __restrict__ E,
                                                     const float* __restrict__ gain, int H, int V, int rows,
                                                     float* __restrict__ x, bf16_bits* __restrict__ xb,
                                                     float* __restrict__ ss, const int32_t* __restrict__ d_len,
                                                     int max_len, int32_t* err, const int32_t* gate,
-                                                    const int32_t* __restrict__ parents, int32_t* __restrict__ tree) {
+                                                    const int32_t* __restrict__ parents, int n0,
+                                                    int32_t* __restrict__ tree) {
   if (gate && *gate == 0) return;
   const int m = blockIdx.x;
-  if (parents && threadIdx.x == 0) {
-    int depth = 0, node = m;
-    uint32_t anc = 1u << m;
-    for (int step = 0; step < kMaxRows; ++step) {
+  if (parents && (int)threadIdx.x < kTreeWords) {
+    const int wd = threadIdx.x, self = n0 + m;
+    int depth = 0, node = self;
+    bool bad = false;
+    uint32_t word = (self >> 5) == wd ? 1u << (self & 31) : 0u;
+    for (int step = 0; step < kMaxTreeNodes; ++step) {
       const int par = parents[node];
       if (par < 0) break;
-      if (par >= node) {
-        raise_error(err, kErrTree);
-        depth = 0;
-        anc = 1u << m;
-        break;
-      }
-      anc |= 1u << par;
+      if (par >= node) { bad = true; break; }
+      if ((par >> 5) == wd) word |= 1u << (par & 31);
       ++depth;
       node = par;
     }
-    tree[m] = depth;
-    tree[kMaxRows + m] = (int32_t)anc;
+    if (bad) {
+      if (wd == 0) raise_error(err, kErrTree);
+      depth = 0;
+      word = (self >> 5) == wd ? 1u << (self & 31) : 0u;
+    }
+    if (wd == 0) tree[m] = depth - n0;
+    tree[kMaxRows + m * kTreeWords + wd] = (int32_t)word;
   }
   int tok = tokens[m];
   if (tok < 0 || tok >= V) {
@@ -558,7 +564,8 @@ template <int HD, int MAXT>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
     const int32_t* gate, const int32_t* __restrict__ d_len, const bf16_bits* __restrict__ qb,
     const bf16_bits* __restrict__ Kc, const bf16_bits* __restrict__ Vt, int rows, int max_len, int lp, int G,
-    float* __restrict__ o_part, float* __restrict__ ml_part, int max_chunks, const uint32_t* __restrict__ tree_anc) {
+    float* __restrict__ o_part, float* __restrict__ ml_part, int max_chunks, const uint32_t* __restrict__ tree_anc,
+    int tree_n0) {
   // the gate word (the length stands in for a null gate) and the length are
   // requested together, before any branch
   const int gv = *(gate ? gate : d_len);
@@ -572,7 +579,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
   __shared__ __attribute__((aligned(16))) float Pl[16][C + 4];
   static_assert(MAXT >= 1 && MAXT <= kAttnMaxWgTiles, "query tiles per workgroup");
   __shared__ i32x4_t qs[MAXT][KBH * 2][64];
-  __shared__ uint32_t sanc[kMaxRows];   // tree forwards: each row's ancestors-or-self among the block
+  __shared__ uint32_t sanc[kMaxRows][kTreeWords];   // tree forwards: each row's ancestors-or-self
   const int c = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -643,7 +650,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
     const int idx = w + NW * j;
     if (idx < ntw * KBH * 2) qs[idx / (KBH * 2)][idx % (KBH * 2)][lane] = qreg[j];
   }
-  if (tree_anc && (int)threadIdx.x < rows) sanc[threadIdx.x] = tree_anc[threadIdx.x];
+  if (tree_anc)
+    for (int i = threadIdx.x; i < rows * kTreeWords; i += blockDim.x) sanc[i / kTreeWords][i % kTreeWords] = tree_anc[i];
+  const int tbase = len - tree_n0;   // tree forwards: the slot of node 0
   float* ob = o_part + ((size_t)h * max_chunks + c) * rstride * HD;
   float* mb = ml_part + ((size_t)h * max_chunks + c) * rstride * 2;
   // the staged query tiles are complete
@@ -671,8 +680,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kidx = key0 + 16 * w + 4 * grp + r;
-        // a block key is visible to the row's ancestors-or-self only in a tree forward
-        const bool vis = !tree_anc || kidx < len || ((sanc[rvalid ? m : 0] >> ((kidx - len) & 31)) & 1u);
+        // in a tree forward a key of the tree (slot tbase + node) is visible to
+        // the node's descendants-or-self only
+        const int bit = (kidx - tbase) & (kMaxTreeNodes - 1);
+        const bool vis = !tree_anc || kidx < tbase || ((sanc[rvalid ? m : 0][bit >> 5] >> (bit & 31)) & 1u);
         const bool ok = rvalid && kidx < T && kidx <= len + m && vis;
         Pl[col][16 * w + 4 * grp + r] = ok ? acc[r] : -INFINITY;
       }
@@ -925,16 +936,16 @@ static void launch_gemv(int wgs, hipStream_t s, const GemvParams& p) {
 template <int HD>
 static void launch_attn(int wt, dim3 grid, hipStream_t s, const int32_t* gate, const int32_t* d_len,
                         const bf16_bits* qb, const bf16_bits* Kc, const bf16_bits* Vt, int rows, int max_len, int lp,
-                        int G, float* o_part, float* ml_part, int max_chunks, const uint32_t* tree_anc) {
+                        int G, float* o_part, float* ml_part, int max_chunks, const uint32_t* tree_anc, int tree_n0) {
   if (wt <= 1)
     attn_chunk_kernel<HD, 1><<<grid, 64 * kAttnWaves, 0, s>>>(gate, d_len, qb, Kc, Vt, rows, max_len, lp, G, o_part,
-                                                              ml_part, max_chunks, tree_anc);
+                                                              ml_part, max_chunks, tree_anc, tree_n0);
   else if (wt <= 2)
     attn_chunk_kernel<HD, 2><<<grid, 64 * kAttnWaves, 0, s>>>(gate, d_len, qb, Kc, Vt, rows, max_len, lp, G, o_part,
-                                                              ml_part, max_chunks, tree_anc);
+                                                              ml_part, max_chunks, tree_anc, tree_n0);
   else
     attn_chunk_kernel<HD, kAttnMaxWgTiles><<<grid, 64 * kAttnWaves, 0, s>>>(gate, d_len, qb, Kc, Vt, rows, max_len,
-                                                                            lp, G, o_part, ml_part, max_chunks, tree_anc);
+                                                                            lp, G, o_part, ml_part, max_chunks, tree_anc, tree_n0);
 }
 
 template <int NT>
@@ -979,12 +990,12 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   const int wt = (ntq + ts - 1) / ts;   // query tiles per workgroup
   if (d.hd == 128) {
     launch_attn<128>(wt, ag, s, a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l), a.rows, a.c->max_len,
-                     a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, tree_anc);
+                     a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, tree_anc, a.tree_n0);
     attn_merge_kernel<128><<<dim3(a.rows * d.nq, 2), 64 * kMergeWaves, 0, s>>>(
         a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
   } else {
     launch_attn<64>(wt, ag, s, a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l), a.rows, a.c->max_len,
-                    a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, tree_anc);
+                    a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, tree_anc, a.tree_n0);
     attn_merge_kernel<64><<<dim3(a.rows * d.nq, 1), 64 * kMergeWaves, 0, s>>>(
         a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
   }
@@ -1037,7 +1048,7 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
 
   int32_t* tree = reinterpret_cast<int32_t*>(ws + pl.tree);
   embed_kernel<<<a.rows, 256, 0, s>>>(a.tokens, a.m->embed, a.m->layers[0].attn_norm, d.H, d.V, a.rows, x, xb, ss,
-                                      a.c->d_len, a.c->max_len, err, a.gate, a.parents, tree);
+                                      a.c->d_len, a.c->max_len, err, a.gate, a.parents, a.tree_n0, tree);
   GemvParams base = {};
   base.tree_depth = a.parents ? tree : nullptr;
   base.rows = a.rows; base.gate = a.gate; base.err = err; base.H = d.H; base.eps = d.eps;

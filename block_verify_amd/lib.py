@@ -25,6 +25,7 @@ SCHEDULE_A, SCHEDULE_B = 0, 1
 DRAFT_TABLE, DRAFT_MODEL, DRAFT_NOISY_SELF, DRAFT_Q4_SELF = 0, 1, 2, 3
 MAX_ROWS = 32
 MAX_K = 16
+MAX_TREE = 512
 
 EXPORTED = [
     "specdec_tensor_count", "specdec_weights_bytes", "specdec_weights_pack", "specdec_model_create",
@@ -35,6 +36,7 @@ EXPORTED = [
     "specdec_check", "specdec_last_hip_error", "specdec_status_str", "specdec_philox4x64",
     "specdec_round_graph", "specdec_round_graph_launch", "specdec_round_debug_view", "specdec_stream_read",
     "specdec_decode_step_noalloc", "specdec_static_init", "specdec_tree_verify", "specdec_tree_accept",
+    "specdec_tree_draft",
 ]
 
 
@@ -106,7 +108,8 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
         "specdec_decode_step_noalloc": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "specdec_static_init": (C.c_int, [vp]),
         "specdec_tree_verify": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
-        "specdec_tree_accept": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+        "specdec_tree_accept": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp]),
+        "specdec_tree_draft": (C.c_int, [vp, vp, vp, i32, i32, C.c_float, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -272,10 +275,25 @@ def tree_verify(model: Model, cache: Cache, tokens: torch.Tensor, parents: torch
 
 
 def tree_accept(cache: Cache, tokens: torch.Tensor, parents: torch.Tensor, argmax: torch.Tensor,
-                out_tokens: torch.Tensor, out_count: torch.Tensor, err: torch.Tensor, stream=None) -> None:
-    check(lib().specdec_tree_accept(cache.handle, tokens.data_ptr(), parents.data_ptr(), int(tokens.numel()),
-                                    argmax.data_ptr(), out_tokens.data_ptr(), out_count.data_ptr(), err.data_ptr(),
-                                    _stream(stream)), "tree_accept")
+                out_tokens: torch.Tensor, out_count: torch.Tensor, err: torch.Tensor, root=None, log=None,
+                n=None, stream=None) -> None:
+    """``log``: int32 [1 + cap] job log (entry 0 counts the tokens stored from entry 1)."""
+    n = int(tokens.numel()) if n is None else n
+    cap = int(log.numel()) - 1 if log is not None else 0
+    check(lib().specdec_tree_accept(cache.handle, tokens.data_ptr(), parents.data_ptr(), n, argmax.data_ptr(),
+                                    out_tokens.data_ptr(), out_count.data_ptr(), _ptr(root), _ptr(log), cap,
+                                    err.data_ptr(), _stream(stream)), "tree_accept")
+
+
+def tree_draft(draft: Model, cache: Cache, root: torch.Tensor, k: int, depth: int, tokens: torch.Tensor,
+               parents: torch.Tensor, scores: torch.Tensor, ws: Workspace, temperature: float = 0.2,
+               stream=None) -> None:
+    n = 1 + k * depth
+    if tokens.numel() < n or parents.numel() < n or scores.numel() < n:
+        raise ValueError(f"tree_draft: outputs need {n} entries")
+    check(lib().specdec_tree_draft(draft.handle, cache.handle, root.data_ptr(), k, depth, float(temperature),
+                                   tokens.data_ptr(), parents.data_ptr(), scores.data_ptr(), ws.mem.data_ptr(),
+                                   ws.nbytes, _stream(stream)), "tree_draft")
 
 
 def static_init(stream=None) -> None:

@@ -64,7 +64,7 @@ enum {
   SPECDEC_DERR_TABLE = 8,      /* draft table or noise read past its end */
   SPECDEC_DERR_OUTPUT = 16,    /* committed-token buffer full (tokens dropped) */
   SPECDEC_DERR_SYNC = 32,      /* a split-K hand-off inside a forward waited past its bound */
-  SPECDEC_DERR_TREE = 64       /* a tree row's parent is not an earlier row (the row is taken as a root) */
+  SPECDEC_DERR_TREE = 64       /* a tree node's parent is not an earlier node (the node is taken as a root) */
 };
 
 enum { SPECDEC_W_BF16 = 0, SPECDEC_W_Q4G64 = 1 };
@@ -177,32 +177,65 @@ int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t*
                         float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
                         void* stream);
 
-/* Draft-tree verify ("SubSpec" summary, jjl357.github.io, section 4.2: a
- * context-aware tree of draft tokens verified in one target forward).  A
- * forward of `rows` (1..SPECDEC_MAX_ROWS) tree nodes at the current length
- * t: d_parents int32 [rows] holds each row's parent row (an earlier row), or
- * -1 for a row whose parent is the last cached position.  Row i runs at
- * position t + depth(i), attends to the cached positions and to its
- * ancestors-or-self among the rows only, and appends its K/V at slot t + i;
- * then length += rows.  Outputs and workspace as for specdec_decode_step
- * (a chain, d_parents = -1, 0, 1, ..., computes exactly the block verify).
- * A parent that is not an earlier row sets SPECDEC_DERR_TREE. */
+/* ------------------------------------------------------------- draft tree
+ * The context-aware draft tree of the "SubSpec" summary (jjl357.github.io,
+ * section 4.2), verified by the target in tree-causal forwards.  Block
+ * layout: node 0 is the root (the round's pending token: the last committed
+ * token, whose K/V is not yet cached), nodes 1 .. n-1 the draft nodes;
+ * d_parents int32 [n] holds each node's parent (an earlier node), -1 for the
+ * root.  At cache length t, node i occupies slot t + i and runs at position
+ * t + depth(i). */
+#define SPECDEC_MAX_TREE 512
+
+/* Tree verify: the target's forward of all n (1..SPECDEC_MAX_TREE) nodes at
+ * the current length t.  Node i attends to the cached positions 0 .. t-1 and
+ * to its ancestors-or-self only, and appends its K/V at slot t + i; then
+ * length = t + n.  The nodes run in passes of up to SPECDEC_MAX_ROWS (4 for
+ * a 4-bit model) in node order, so a tree wider than a pass costs one
+ * weight stream per pass.  d_logits fp32 [n][V], d_argmax int32 [n] and
+ * d_lse fp32 [n] as for specdec_decode_step (any may be NULL; d_argmax is
+ * what specdec_tree_accept reads).  A chain (d_parents = -1, 0, 1, ...)
+ * computes exactly the block verify.  A parent that is not an earlier node
+ * sets SPECDEC_DERR_TREE (the node is taken as a root). */
 int specdec_tree_verify(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents,
-                        int32_t rows, float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
+                        int32_t n, float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
                         void* stream);
 
-/* Greedy acceptance of a verified tree (after specdec_tree_verify on the same
- * tokens / parents, row 0 being the root: the round's pending token).  From
- * the root, the first child in row order whose token is the target's argmax
- * (d_argmax [rows], the verify's output) continues the accepted path; the
- * walk stops at a row with no such child.  The path's K/V move to slots
- * t+1 .. t+m (every layer), the root stays at slot t, the length becomes
- * t + 1 + m.  d_out_tokens int32 [rows] receives the path's tokens then the
- * target's choice at its end (the next pending token), *d_out_count = m + 1.
- * A length below rows sets SPECDEC_DERR_TRIM in *d_err and changes nothing. */
-int specdec_tree_accept(specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents, int32_t rows,
-                        const int32_t* d_argmax, int32_t* d_out_tokens, int32_t* d_out_count, int32_t* d_err,
-                        void* stream);
+/* Greedy acceptance of a verified tree (right after specdec_tree_verify of
+ * the same n nodes, so the length is t + n).  From the root, the first child
+ * in node order whose token is the target's argmax at the current node
+ * continues the accepted path; the walk stops at a node with no such child.
+ * The path's K/V move to slots t+1 .. t+m (every layer), the root stays at
+ * slot t, the length becomes t + 1 + m.  d_out_tokens int32 [n] receives the
+ * path's tokens then the target's choice at its end (the next pending
+ * token), *d_out_count = m + 1.  Optional (NULL to skip): d_root receives
+ * the next pending token; d_log int32 [1 + log_cap] is a job log whose
+ * d_log[0] counts the tokens stored from d_log[1]: the committed tokens are
+ * appended (tokens past log_cap are dropped and set SPECDEC_DERR_OUTPUT).
+ * A length below n sets SPECDEC_DERR_TRIM in *d_err and changes nothing. */
+int specdec_tree_accept(specdec_cache* c, const int32_t* d_tokens, const int32_t* d_parents, int32_t n,
+                        const int32_t* d_argmax, int32_t* d_out_tokens, int32_t* d_out_count, int32_t* d_root,
+                        int32_t* d_log, int32_t log_cap, int32_t* d_err, void* stream);
+
+/* Tree construction by a draft that shares the target's cache (the
+ * substitute draft: same layers, kv heads and head dim).  At the current
+ * length t (every committed token but the pending root *d_root), `depth`
+ * steps: the first feeds the root, each later one the k nodes the previous
+ * step chose (tree-causal, at slots t + node); after each step every (leaf,
+ * token) pair scores the leaf's cumulative log probability plus
+ * log softmax(z / temperature)[token] of the leaf's draft logits z, and the
+ * k best pairs become the next nodes (ties: the lower leaf node, then the
+ * lower token id).  The pages sharpen with temperature 0.2.  Outputs in
+ * block layout, n = 1 + k * depth nodes: d_tokens and d_parents int32 [n],
+ * d_scores fp32 [n] (cumulative log probabilities, 0 at the root; step s
+ * writes nodes 1 + k (s-1) .. k s in rank order).  k in 1..SPECDEC_MAX_K,
+ * n <= SPECDEC_MAX_TREE, temperature finite and > 0.  d_ws is a workspace
+ * of the draft (its leaf logits and the selection's partials live there).
+ * On return the length is t again; the draft's K/V of the fed nodes stay in
+ * the slots past it until the verify of the tree overwrites them. */
+int specdec_tree_draft(const specdec_model* draft, specdec_cache* c, const int32_t* d_root, int32_t k,
+                       int32_t depth, float temperature, int32_t* d_tokens, int32_t* d_parents, float* d_scores,
+                       void* d_ws, size_t ws_bytes, void* stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid device allocation): the decode step

@@ -125,6 +125,21 @@ def compact(cache: OracleCache, t: int, path) -> None:
     cache.length = t + len(rows)
 
 
+def select_children(leaf_rows, leaf_logits, scores, k: int, temperature: float = SHARPEN_T):
+    """One step of the construction ("SubSpec" summary, section 4.2): every (leaf,
+    token) pair scores the leaf's cumulative probability times the leaf's sharpened
+    draft probability of the token; returns the k best as (score, leaf row, token),
+    best first (ties: the lower leaf row, then the lower token id).  ``scores`` maps a
+    row to its cumulative probability."""
+    cand = []
+    for leaf, z in zip(leaf_rows, leaf_logits):
+        s = scores[leaf] * acc.softmax(np.asarray(z, dtype=np.float64), temperature)
+        top = np.argsort(-s, kind="stable")[:k]
+        cand += [(float(s[j]), int(leaf), int(j)) for j in top]
+    cand.sort(key=lambda x: (-x[0], x[1], x[2]))
+    return cand[:k]
+
+
 def build_draft_tree(draft_w: OracleWeights, cache: OracleCache, root: int, k: int, depth: int,
                      temperature: float = SHARPEN_T):
     """The context-aware draft tree ("SubSpec" summary, section 4.2) rooted at `root`
@@ -137,19 +152,13 @@ def build_draft_tree(draft_w: OracleWeights, cache: OracleCache, root: int, k: i
     for _ in range(depth):
         c = cache.clone()
         logits = tree_forward(draft_w, c, tokens, parents)
-        cand = []
-        for leaf in leaves:
-            p = acc.softmax(logits[leaf], temperature)
-            s = score[leaf] * p
-            top = np.argsort(-s, kind="stable")[:k]
-            cand += [(float(s[j]), leaf, int(j)) for j in top]
-        cand.sort(key=lambda x: (-x[0], x[1], x[2]))
-        leaves = []
-        for s_, leaf, tok in cand[:k]:
+        leaves_new = []
+        for s_, leaf, tok in select_children(leaves, [logits[l] for l in leaves], score, k, temperature):
             tokens.append(tok)
             parents.append(leaf)
             score.append(s_)
-            leaves.append(len(tokens) - 1)
+            leaves_new.append(len(tokens) - 1)
+        leaves = leaves_new
     return tokens, parents
 
 
