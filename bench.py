@@ -289,6 +289,104 @@ class SpecJob:
             raise RuntimeError(f"device error bits {self.r.ws.error_bits()}")
 
 
+class TreeJob:
+    """Greedy draft-tree rounds ("SubSpec" summary, section 4.2): the substitute draft
+    builds the context-aware tree on the shared cache, the target verifies it in
+    tree-causal passes and the longest accepted path is committed.  A round is one
+    captured graph of the three calls; the next root and the job log stay on the device,
+    so a job is a fixed number of replays (the round count of a first, eager run)."""
+
+    def __init__(self, b, target, draft, shape, prompt_t, k, depth, n_new, torch):
+        self.b, self.torch, self.k, self.depth, self.n_new = b, torch, k, depth, n_new
+        self.n = n = 1 + k * depth
+        self.P = int(prompt_t.numel())
+        max_len = self.P + n_new + n + 64
+        self.cache = b.Cache(shape, max_len)
+        self.ws = b.Workspace(shape, max_len)
+        b.prefill(target, self.cache, prompt_t[:-1], self.ws)
+        self.root0 = prompt_t[-1:].clone()
+
+        def i32(m):
+            return torch.zeros(m, dtype=torch.int32, device="cuda")
+        self.root, self.toks, self.pars, self.am, self.out = i32(1), i32(n), i32(n), i32(n), i32(n)
+        self.cnt, self.err, self.log = i32(1), i32(1), i32(1 + n_new + n)
+        self.sc = torch.zeros(n, dtype=torch.float32, device="cuda")
+        self.calls = (
+            lambda: b.tree_draft(draft, self.cache, self.root, k, depth, self.toks, self.pars, self.sc, self.ws),
+            lambda: b.tree_verify(target, self.cache, self.toks, self.pars, self.ws, argmax=self.am),
+            lambda: b.tree_accept(self.cache, self.toks, self.pars, self.am, self.out, self.cnt, self.err,
+                                  root=self.root, log=self.log))
+        self.reset()
+        self.rounds, self.accepted = 0, []
+        while int(self.log[0].item()) < n_new:
+            if self.rounds > n_new:
+                raise RuntimeError(f"tree job k={k} D={depth}: no progress (error bits {int(self.err.item())})")
+            for f in self.calls:
+                f()
+            self.rounds += 1
+            self.accepted.append(int(self.cnt.item()) - 1)
+        self.eager_tokens = self.tokens()
+        s = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=s):
+            for f in self.calls:
+                f()
+        self.parts = []
+        for f in self.calls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                f()
+            self.parts.append(g)
+        torch.cuda.synchronize()
+
+    def reset(self):
+        self.cache.trim(self.P - 1, self.ws)
+        self.root.copy_(self.root0)
+        self.log.zero_()
+
+    def tokens(self):
+        self.torch.cuda.synchronize()
+        return [int(x) for x in self.log[1:1 + int(self.log[0].item())].cpu().numpy()]
+
+    def timed(self, steps):
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.reset()
+            for _ in range(self.rounds):
+                self.graph.replay()
+        self.torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def terms(self):
+        """Per-round draft (construction), verify and accept times from the three part
+        graphs with events between them, and the job's span against their sum."""
+        ev = HipEvents(4 * self.rounds)
+        self.reset()
+        self.torch.cuda.synchronize()
+        stream = self.torch.cuda.current_stream().cuda_stream
+        for r in range(self.rounds):
+            for j, g in enumerate(self.parts):
+                ev.record(4 * r + j, stream)
+                g.replay()
+            ev.record(4 * r + 3, stream)
+        self.torch.cuda.synchronize()
+        t = {nm: float(np.mean([ev.ms(4 * r + j, 4 * r + j + 1) for r in range(self.rounds)]))
+             for j, nm in enumerate(("draft", "verify", "accept"))}
+        span = ev.ms(0, 4 * self.rounds - 1)
+        total = sum(ev.ms(4 * r, 4 * r + 3) for r in range(self.rounds))
+        return t, {"span_ms": round(span, 4), "sum_terms_ms": round(total, 4),
+                   "overhead_ms": round(span - total, 4)}
+
+    def check(self, ar_tokens):
+        got = self.tokens()
+        if got[:self.n_new] != list(ar_tokens[:self.n_new]) or self.eager_tokens[:self.n_new] != got[:self.n_new]:
+            raise RuntimeError(f"tree job k={self.k} D={self.depth}: committed tokens differ from the GPU AR decode")
+        if int(self.err.item()) or self.ws.error_bits():
+            raise RuntimeError(f"tree job: device error bits {int(self.err.item())} / {self.ws.error_bits()}")
+
+
 def protocol(legs, steps, warmup, repeats, n_new):
     """Timed regions of `steps` jobs per leg, `repeats` times, in alternating order.
     legs: name -> callable(steps) -> seconds.  Returns name -> tok/s per region."""
@@ -514,7 +612,8 @@ def main():
         run_substitute(args, torch)
         return
     from block_verify_amd.shapes import QWEN_0_5B, QWEN_1_5B as S, SEED_DRAFT, SEED_TARGET
-    from block_verify_amd.synth import make_draft_table, make_near_miss_table, make_noise, make_prompt, make_weights
+    from block_verify_amd.synth import (make_draft_table, make_near_miss_table, make_noise, make_prompt,
+                                        make_q4_draft, make_weights)
 
     k, n_new = 4, args.n_new
     P = args.context
@@ -531,6 +630,7 @@ def main():
     prompt_t = torch.from_numpy(prompt).cuda()
 
     ar_toks, runner_up = gpu_ar(b, model, S, prompt_t, n_new + k + 2, max_len, torch, runner_up=True)
+    log(f"prefill and AR decode of {n_new + k + 2} tokens done")
     table = make_draft_table(np.array(ar_toks), S.vocab, args.corrupt)
     ar = GraphAR(b, model, S, prompt_t, max_len, torch)
 
@@ -556,6 +656,7 @@ def main():
     res = protocol({"A": lambda st: jobs["A"].timed(st)[0], "B": lambda st: jobs["B"].timed(st)[0], "AR": ar_leg},
                    args.steps, args.warmup, args.repeats, n_new)
     ar.check(n_new, ar_toks)
+    log(f"headline regions done: schedule B median {sorted(res['B'])[len(res['B']) // 2]:.1f} tok/s")
     states = {s_: check_tokens(jobs[s_], f"schedule {s_}") for s_ in jobs}
     terms, ident = {}, {}
     for s_ in jobs:
@@ -632,6 +733,7 @@ def main():
         legs["all_accept_bonus_2k"]["pages_R_spec_over_ar"] = 0.912
         legs["draft_free_2k"]["pages_spec_over_ar"] = 4.46
         del ljobs
+        log("diagnostic legs done")
         # relaxed acceptance (lossy), on drafts that miss by a small logit gap: the corrupted
         # positions of the headline table carry the target's runner-up token instead
         near = make_near_miss_table(np.array(ar_toks), np.array(runner_up), args.corrupt)
@@ -651,6 +753,39 @@ def main():
             if nm.startswith("relaxed_delta1"):
                 legs[nm]["pages_acceptance_R"] = {"acceptance": 0.81, "R": 0.714}
             del rj
+            log(f"leg {nm} done")
+        # draft trees: the 4-bit substitute of the target builds the context-aware tree on
+        # the shared cache ("SubSpec" summary, section 4.2); the pages' deep tree is k=6, D=48
+        q4 = b.Model(S, make_q4_draft(S, weights), weight_format=b.W_Q4G64, share=model)
+        torch.cuda.synchronize()
+        chain = SpecJob(b, model, prompt, 7, n_new, max_len + 8, torch, schedule=0, draft_source=b.DRAFT_Q4_SELF,
+                        draft=q4)
+        cres = protocol({"chain": lambda st: chain.timed(st)[0], "AR": ar_leg}, args.steps, args.warmup, 3, n_new)
+        cst = check_tokens(chain, "substitute chain D=7")
+        ct, cid = chain.terms(2)
+        legs["substitute_chain_d7_2k"] = {**leg_summary(cres["chain"], cres["AR"]), "rounds_per_job": cst.round,
+                                          "accepted_total": cst.accepted_total, "terms_ms": ct, "cost_model": cid}
+        del chain
+        log("leg substitute_chain_d7_2k done")
+        for kt, dt in ((4, 7), (6, 48)):
+            tj = TreeJob(b, model, q4, S, prompt_t, kt, dt, n_new, torch)
+            tres = protocol({"tree": tj.timed, "AR": ar_leg}, args.steps, args.warmup, 3, n_new)
+            tj.check(ar_toks)
+            tt, tid = tj.terms()
+            nodes = 1 + kt * dt
+            passes = [min(32, nodes - n0) for n0 in range(0, nodes, 32)]
+            vb_t = sum(verify_bytes(S, P + n_new // 2 + 32 * i, m) for i, m in enumerate(passes))
+            legs[f"tree_k{kt}_d{dt}_2k"] = {
+                **leg_summary(tres["tree"], tres["AR"]), "rounds_per_job": tj.rounds,
+                "accepted_per_round": tj.accepted, "nodes": nodes, "verify_passes": len(passes),
+                "terms_ms": tt, "cost_model": tid,
+                "verify_gbs": round(vb_t / (tt["verify"] * 1e-3) / 1e9, 1),
+                "verify_frac": round(vb_t / (tt["verify"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "draft": "4-bit group-64 substitute of the target (shared embedding, LM head and cache), "
+                         "sharpening temperature 0.2"}
+            del tj
+            log(f"leg tree_k{kt}_d{dt}_2k done")
+        del q4
         if not args.no_8k:
             P8 = 8192
             max8 = P8 + n_new + 4 * (k + 2) + 64
@@ -686,6 +821,7 @@ def main():
                                                                    PEAK_HBM_GBS, 4),
                                   "pages_R_spec_over_ar": 0.522}
             del j8, gar8
+            log("leg context_8k done")
         # stochastic leg at 4K: modified rejection sampling, noisy self-draft
         P4 = 4096
         max4 = P4 + n_new + 4 * (k + 2) + 64
@@ -705,6 +841,7 @@ def main():
                         "accepted_per_round": round(st.accepted_total / max(st.round, 1), 3), "terms_ms": t,
                         "cost_model": idn, "accept_us": round(t["accept"] * 1e3, 1), **kw}
             del sj
+            log(f"leg {nm} done")
         out["legs"] = legs
         out["legs_note"] = ("R = tok/s of the leg / tok/s of the graph-captured AR in the same regions (median of "
                             "per-region ratios); pages_* are the pages' numbers for the same diagnostic on an RTX "

@@ -36,7 +36,7 @@ int dims_from_desc(const specdec_model_desc* d, Dims* o) {
   if (x.nq % x.nkv != 0 || x.nq / x.nkv > 8) return SPECDEC_ESHAPE;
   if (x.H % 32 || x.F % 32 || x.qdim() % 32 || x.V % 16 || x.H % 16) return SPECDEC_ESHAPE;
   // the RMSNorm scale reads at most 256 per-16-feature partials per row
-  if (x.H > 4096 || x.V > (1 << 24)) return SPECDEC_ESHAPE;
+  if (x.H > kMaxHidden || x.V > (1 << 24)) return SPECDEC_ESHAPE;
   if (x.wfmt == SPECDEC_W_Q4G64) {
     if (x.H % 64 || x.qdim() % 64 || x.F % 64) return SPECDEC_ESHAPE;
     // the 4-bit kernel stages up to kQ4MaxRows activation rows of its input range in LDS

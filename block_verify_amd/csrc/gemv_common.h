@@ -75,7 +75,9 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 }
 // Reads of such values: buffer loads with the sc1 cache policy (the same
 // coherence as agent-scope atomic loads, but ordinary loads the compiler
-// may issue back to back).  The descriptor covers 2 GiB from `base`.
+// may issue back to back).  The descriptor covers 2 GiB from `base`; its
+// only user, the split-K partial buffer, is bounded below (byte offsets are
+// 32-bit and must stay under the record count).
 typedef __amdgpu_buffer_rsrc_t agent_rsrc_t;
 constexpr int kCpolSc1 = 16;
 __device__ __forceinline__ agent_rsrc_t agent_rsrc(const void* base) {
@@ -95,6 +97,8 @@ __device__ __forceinline__ u32x2_t load_agent_pair(agent_rsrc_t r, size_t index)
   return __builtin_amdgcn_raw_buffer_load_b64(r, (uint32_t)(index * 8), 0, kCpolSc1);
 }
 constexpr int kHandoffSpins = 1 << 18;   // bound of a finisher's wait for one value
+static_assert((long long)kMaxSplit * kMaxRows * kMaxHidden * 8 < 0x7FFFFFFFLL,
+              "split-K partials must fit one 2 GiB buffer descriptor");
 
 // Wait until this wave's outstanding vector memory operations completed.
 __device__ __forceinline__ void wait_vmem() {

@@ -88,6 +88,7 @@ constexpr int kKvPad = 128;                 // cache positions are padded to a m
 static_assert(kKvPad % kAttnChunk == 0, "chunks tile the padded cache");
 constexpr int kWsHeader = 65536;   // error word + split-K launch sequence numbers
 constexpr int kMaxSplit = 8;
+constexpr int kMaxHidden = 4096;   // the largest hidden size a model may have
 // K splits of the down projection: bf16 (tuned on the verify forward) and
 // 4-bit (bounded by the activations the 4-bit kernel stages in LDS).
 #ifndef SD_DOWN_SPLIT
