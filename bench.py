@@ -408,10 +408,12 @@ def leg_summary(tok_s_list, ar_tok_s_list):
     return {"tok_s": s, "R_spec_over_ar": r}
 
 
-def profile_forwards(b, shape_name, rows, n, context, torch):
+def profile_forwards(b, shape_name, rows, n, context, torch, fill_cache=False):
     """Forward passes of `rows` rows at a `context`-token cache (trimmed back after each),
     timed with hipEvents, then a plain 256 MiB device-to-device copy (calibrates traffic
-    counters)."""
+    counters).  The cache comes from a prefill of seeded prompt ids, or with fill_cache
+    from seeded random K/V (for counter runs, which the prefill's dispatches would
+    lengthen many times over)."""
     from block_verify_amd.shapes import SHAPES, SEED_TARGET, SEED_DRAFT
     from block_verify_amd.synth import make_prompt, make_weights
     shape = SHAPES[shape_name]
@@ -421,7 +423,16 @@ def profile_forwards(b, shape_name, rows, n, context, torch):
     ws = b.Workspace(shape, max_len)
     logits = torch.empty((rows, shape.vocab), dtype=torch.float32, device="cuda")
     prompt_t = torch.from_numpy(make_prompt(shape.vocab, context)).cuda()
-    b.prefill(model, cache, prompt_t, ws, logits=logits[0])
+    if fill_cache:
+        # seeded random K/V (bf16 of N(0, 1)) and the length set to the context: the
+        # forwards read and write what they would after a prefill, without its dispatches
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
+        kv = cache.mem[: cache.kv_bytes()].view(torch.bfloat16)
+        kv.copy_(torch.randn(kv.numel(), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16))
+        cache.len.fill_(context)
+    else:
+        b.prefill(model, cache, prompt_t, ws, logits=logits[0])
     toks = torch.arange(rows, dtype=torch.int32, device="cuda") * 977 + 13
     ev = HipEvents(2 * n)
     stream = torch.cuda.current_stream().cuda_stream
@@ -445,14 +456,16 @@ def profile_forwards(b, shape_name, rows, n, context, torch):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "verify_forward_1.5b_2k_traffic.md")
+TRAFFIC_PROFILE_8K = os.path.join(ROOT, "profiles", "verify_forward_1.5b_8k_traffic.md")
 
 
-def measured_traffic():
-    """HBM bytes per 5-row verify forward at a 2048-token context, from the committed
-    FETCH_SIZE / WRITE_SIZE summary; None once a kernel source it lists has changed."""
+def measured_traffic(path=None):
+    """HBM bytes per 5-row verify forward (at a 2048-token context by default), from the
+    committed FETCH_SIZE / WRITE_SIZE summary; None once a kernel source it lists has
+    changed."""
     import hashlib
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(path or TRAFFIC_PROFILE).read()
     except OSError:
         return None
     val = None
@@ -592,6 +605,8 @@ def main():
                          "device copy of known size for counter calibration")
     ap.add_argument("--shape", default="qwen2.5-1.5b-shape", help="profiling mode: model shape name")
     ap.add_argument("--rows", type=int, default=5, help="profiling mode: rows per forward")
+    ap.add_argument("--fill-cache", action="store_true",
+                    help="profiling mode: random K/V and the length set to the context instead of a prefill")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-8k", action="store_true", help="skip the 8192-token leg")
     ap.add_argument("--no-legs", action="store_true", help="only the headline job (schedules A, B and AR)")
@@ -606,7 +621,7 @@ def main():
     import torch
     from block_verify_amd import lib as b
     if args.forward_only:
-        profile_forwards(b, args.shape, args.rows, args.forward_only, args.context, torch)
+        profile_forwards(b, args.shape, args.rows, args.forward_only, args.context, torch, args.fill_cache)
         return
     if args.substitute_7b:
         run_substitute(args, torch)
@@ -815,7 +830,8 @@ def main():
                                   "terms_ms": t8, "cost_model": id8,
                                   "verify_gbs": round(vb8 / (t8["verify"] * 1e-3) / 1e9, 1),
                                   "verify_frac": round(vb8 / (t8["verify"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                  "verify_bytes": vb8, "draft_step_ms": round(t8["draft"] / k, 4),
+                                  "verify_bytes": vb8, "verify_traffic_at_8192": measured_traffic(TRAFFIC_PROFILE_8K),
+                                  "draft_step_ms": round(t8["draft"] / k, 4),
                                   "draft_step_gbs": round(step_b / (t8["draft"] / k * 1e-3) / 1e9, 1),
                                   "draft_step_frac_of_peak": round(step_b / (t8["draft"] / k * 1e-3) / 1e9 /
                                                                    PEAK_HBM_GBS, 4),

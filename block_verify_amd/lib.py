@@ -220,6 +220,12 @@ class Cache:
     def length(self) -> int:
         return int(self.len.item())
 
+    def kv_bytes(self) -> int:
+        """Bytes of the K and V arrays at the start of the cache memory."""
+        sh = self.shape
+        lp = (self.max_len + 127) // 128 * 128
+        return 2 * sh.n_layers * sh.n_kv_heads * lp * sh.head_dim * 2
+
     def kv(self):
         """bf16 bit views (int16) of the cache: K [L][n_kv][max_len][hd] and V [L][n_kv][max_len][hd].
 
