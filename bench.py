@@ -85,6 +85,22 @@ def verify_bytes(shape, T: int, M: int) -> int:
     return w + kv_pos * (T + M) + kv_pos * M + 4 * shape.vocab * M + 2 * shape.hidden * M
 
 
+def q4_forward_bytes(shape, T: int, M: int) -> int:
+    """Algorithmic HBM bytes of one forward of M rows of the 4-bit substitute at context T:
+    the 4-bit codes and fp16 (scale, zero) pairs of every linear (0.5 + 4/64 bytes per
+    weight), the shared bf16 LM head and norm gains, the K/V as in verify_bytes."""
+    H, F, hd = shape.hidden, shape.ffn, shape.head_dim
+    lin = 0
+    for n_out, k_in in (((shape.n_q_heads + 2 * shape.n_kv_heads) * hd, H), (H, shape.n_q_heads * hd),
+                        (2 * F, H), (H, F)):
+        nb = -(-k_in // 128)
+        lin += n_out * nb * (64 + 8)
+    kv_pos = shape.kv_bytes_per_token()
+    norms = 4 * H * (2 * shape.n_layers + 1)
+    return (shape.n_layers * lin + 2 * shape.vocab * H + norms + kv_pos * (T + M) + kv_pos * M
+            + 4 * shape.vocab * M + 2 * H * M)
+
+
 def stats(xs):
     xs = sorted(float(x) for x in xs)
     return {"median": round(xs[len(xs) // 2], 3), "min": round(xs[0], 3), "max": round(xs[-1], 3), "n": len(xs)}
@@ -408,16 +424,23 @@ def leg_summary(tok_s_list, ar_tok_s_list):
     return {"tok_s": s, "R_spec_over_ar": r}
 
 
-def profile_forwards(b, shape_name, rows, n, context, torch, fill_cache=False):
+def profile_forwards(b, shape_name, rows, n, context, torch, fill_cache=False, q4=False):
     """Forward passes of `rows` rows at a `context`-token cache (trimmed back after each),
     timed with hipEvents, then a plain 256 MiB device-to-device copy (calibrates traffic
     counters).  The cache comes from a prefill of seeded prompt ids, or with fill_cache
     from seeded random K/V (for counter runs, which the prefill's dispatches would
-    lengthen many times over)."""
+    lengthen many times over).  With q4 the forwards are the 4-bit substitute's."""
     from block_verify_amd.shapes import SHAPES, SEED_TARGET, SEED_DRAFT
     from block_verify_amd.synth import make_prompt, make_weights
     shape = SHAPES[shape_name]
-    model = b.Model(shape, make_weights(shape, SEED_DRAFT if "0.5b" in shape_name else SEED_TARGET))
+    weights = make_weights(shape, SEED_DRAFT if "0.5b" in shape_name else SEED_TARGET)
+    model = b.Model(shape, weights)
+    if q4:
+        # the 4-bit substitute of the model (its embedding and LM head shared)
+        from block_verify_amd.synth import make_q4_draft
+        target = model
+        model = b.Model(shape, make_q4_draft(shape, weights), weight_format=b.W_Q4G64, share=target)
+    del weights
     max_len = context + 256
     cache = b.Cache(shape, max_len)
     ws = b.Workspace(shape, max_len)
@@ -432,7 +455,8 @@ def profile_forwards(b, shape_name, rows, n, context, torch, fill_cache=False):
         kv.copy_(torch.randn(kv.numel(), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16))
         cache.len.fill_(context)
     else:
-        b.prefill(model, cache, prompt_t, ws, logits=logits[0])
+        # a substitute shares the target's cache, which the target prefills
+        b.prefill(target if q4 else model, cache, prompt_t, ws, logits=logits[0])
     toks = torch.arange(rows, dtype=torch.int32, device="cuda") * 977 + 13
     ev = HipEvents(2 * n)
     stream = torch.cuda.current_stream().cuda_stream
@@ -447,9 +471,9 @@ def profile_forwards(b, shape_name, rows, n, context, torch, fill_cache=False):
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    vb = verify_bytes(shape, context, rows)
+    vb = q4_forward_bytes(shape, context, rows) if q4 else verify_bytes(shape, context, rows)
     med = float(np.median(us))
-    print(json.dumps({"mode": "forward-only", "shape": shape_name, "rows": rows, "context": context, "forwards": n,
+    print(json.dumps({"mode": "forward-only", "shape": shape_name, "q4": q4, "rows": rows, "context": context, "forwards": n,
                       "us_per_forward_median": med, "algorithmic_bytes": vb,
                       "gbs": round(vb / (med * 1e-6) / 1e9, 1), "frac_of_peak": round(vb / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                       "copy_bytes": 256 << 20, "error_bits": ws.error_bits()}), flush=True)
@@ -605,6 +629,7 @@ def main():
                          "device copy of known size for counter calibration")
     ap.add_argument("--shape", default="qwen2.5-1.5b-shape", help="profiling mode: model shape name")
     ap.add_argument("--rows", type=int, default=5, help="profiling mode: rows per forward")
+    ap.add_argument("--q4", action="store_true", help="profiling mode: the model's 4-bit substitute runs the forwards")
     ap.add_argument("--fill-cache", action="store_true",
                     help="profiling mode: random K/V and the length set to the context instead of a prefill")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -621,7 +646,7 @@ def main():
     import torch
     from block_verify_amd import lib as b
     if args.forward_only:
-        profile_forwards(b, args.shape, args.rows, args.forward_only, args.context, torch, args.fill_cache)
+        profile_forwards(b, args.shape, args.rows, args.forward_only, args.context, torch, args.fill_cache, args.q4)
         return
     if args.substitute_7b:
         run_substitute(args, torch)

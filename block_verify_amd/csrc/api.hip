@@ -39,10 +39,10 @@ int dims_from_desc(const specdec_model_desc* d, Dims* o) {
   if (x.H > kMaxHidden || x.V > (1 << 24)) return SPECDEC_ESHAPE;
   if (x.wfmt == SPECDEC_W_Q4G64) {
     if (x.H % 64 || x.qdim() % 64 || x.F % 64) return SPECDEC_ESHAPE;
-    // the 4-bit kernel stages up to kQ4MaxRows activation rows of its input range in LDS
-    const size_t lim = 48 * 1024;
-    if (q4_lds_bytes(kQ4MaxRows, x.H, 1) > lim || q4_lds_bytes(kQ4MaxRows, x.qdim(), 1) > lim ||
-        q4_lds_bytes(kQ4MaxRows, x.F, kQ4DownSplit) > lim)
+    // a workgroup of the 4-bit product covers kQ4MaxBlocks blocks of 128 inputs
+    // (kMaxSplit of them for the down projection)
+    if ((x.H + 127) / 128 > kQ4MaxBlocks || (x.qdim() + 127) / 128 > kQ4MaxBlocks ||
+        (x.F + 127) / 128 > kMaxSplit * kQ4MaxBlocks)
       return SPECDEC_ESHAPE;
   }
   *o = x;
@@ -355,7 +355,6 @@ int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream) {
 static int check_fwd(const specdec_model* m, const specdec_cache* c, int32_t rows, size_t ws_bytes, WsPlan* plan) {
   if (!m || !c) return SPECDEC_EINVAL;
   if (rows < 1 || rows > SPECDEC_MAX_ROWS) return SPECDEC_ECAPACITY;
-  if (m->d.wfmt == SPECDEC_W_Q4G64 && rows > kQ4MaxRows) return SPECDEC_ECAPACITY;
   if (m->d.L != c->d.L || m->d.nkv != c->d.nkv || m->d.hd != c->d.hd) return SPECDEC_ESHAPE;
   *plan = ws_plan(m->d, rows, c->max_len);
   if (ws_bytes < plan->total) return SPECDEC_ECAPACITY;
@@ -381,7 +380,7 @@ int specdec_tree_verify(const specdec_model* m, specdec_cache* c, const int32_t*
                         void* stream) {
   if (!m) return SPECDEC_EINVAL;
   if (n < 1 || n > SPECDEC_MAX_TREE) return SPECDEC_ECAPACITY;
-  const int pass = m->d.wfmt == SPECDEC_W_Q4G64 ? kQ4MaxRows : kMaxRows;
+  const int pass = kMaxRows;
   WsPlan plan;
   int rc = check_fwd(m, c, n < pass ? n : pass, ws_bytes, &plan);
   if (rc) return rc;
@@ -421,7 +420,7 @@ int specdec_tree_draft(const specdec_model* draft, specdec_cache* c, const int32
   if (k < 1 || k > SPECDEC_MAX_K || k > draft->d.V || depth < 1) return SPECDEC_EINVAL;
   if (1 + (long)k * depth > SPECDEC_MAX_TREE) return SPECDEC_ECAPACITY;
   if (!(temperature > 0.f) || !std::isfinite(temperature)) return SPECDEC_EINVAL;
-  const int pass = draft->d.wfmt == SPECDEC_W_Q4G64 ? kQ4MaxRows : kMaxRows;
+  const int pass = kMaxRows;
   WsPlan plan;
   int rc = check_fwd(draft, c, k < pass ? k : pass, ws_bytes, &plan);
   if (rc) return rc;
@@ -518,7 +517,6 @@ int specdec_prefill(const specdec_model* m, specdec_cache* c, const int32_t* d_t
   if (!d_tokens || !d_ws || n <= 0 || chunk <= 0) return SPECDEC_EINVAL;
   if (n > c->max_len) return SPECDEC_ECAPACITY;
   if (chunk > SPECDEC_MAX_ROWS) chunk = SPECDEC_MAX_ROWS;
-  if (m->d.wfmt == SPECDEC_W_Q4G64 && chunk > kQ4MaxRows) chunk = kQ4MaxRows;
   char* ws = static_cast<char*>(d_ws);
   for (int off = 0; off < n; off += chunk) {
     int rows = n - off < chunk ? n - off : chunk;

@@ -403,4 +403,82 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
   }
 }
 
+// After the product of a skinny GEMV (bf16 or 4-bit): the hi and lo columns of
+// each accumulator added in registers, the k-split waves' partials through
+// LDS in a fixed order, then the epilogue.  red holds NW = WG_ROWS * WK wave
+// slots; fin (LM head only) one slot per row group.
+template <int NT, int WG_ROWS, int WK, Epi E>
+__device__ __forceinline__ void gemv_finish(const GemvParams& p, const f32x4_t (&acc)[NT], float (*red)[16][NT * 8 + 1],
+                                            float (*fin)[16][NT * 8 + 1], const float* rsc,
+                                            const EpiPre<NT * 8>& pre, int w, int lane, int rg, int ks, int g,
+                                            int sidx, int M, int n_groups) {
+  constexpr int NC = NT * 8;
+  // hi + lo (columns 2c and 2c + 1) in registers, then the waves' partials in LDS
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[t][r] + swap1(acc[t][r]);
+      if ((lane & 1) == 0) red[w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
+    }
+  __syncthreads();
+  if constexpr (E == Epi::SWIGLU) {
+    // the epilogue wave sums the k-split partials of its own entries, in the
+    // order of the reduction below, and needs no second pass through LDS
+    if (ks != 0 || g >= n_groups) return;
+    const int KBo = p.F >> 5;
+    for (int idx = lane; idx < 8 * M; idx += 64) {
+      const int i = idx & 7, m = idx >> 3;
+      float gt = 0.f, up = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < WK; ++s2) {
+        gt += red[rg * WK + s2][i][m];
+        up += red[rg * WK + s2][i + 8][m];
+      }
+      const float r = rsc[m];
+      gt *= r;
+      up *= r;
+      btile_put(p.hb_out, KBo, m, 8 * g + i, gt / (1.0f + __expf(-gt)) * up);
+    }
+    return;
+  } else if constexpr (E != Epi::LMHEAD) {
+    // one wave per row group: it sums the k-split partials of the group (in
+    // the order of the reduction below) into its first wave's slot, which
+    // then serves as the group's finished products
+    if (ks != 0 || g >= n_groups) return;
+    constexpr int kE = (16 * NC + 63) / 64;
+    float v[kE];
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < 16 * NC) {
+        const int i = idx / NC, m = idx % NC;
+        v[j] = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < WK; ++s2) v[j] += red[rg * WK + s2][i][m];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < 16 * NC) red[rg * WK][idx / NC][idx % NC] = v[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    gemv_epilogue<WG_ROWS, NC, E>(p, red + rg * (WK - 1), rsc, pre, w, lane, rg, 0, g, sidx, M);
+    return;
+  }
+  // fixed-order reduction over the k-split waves (whole-workgroup epilogue)
+  for (int idx = threadIdx.x; idx < WG_ROWS * 16 * NC; idx += blockDim.x) {
+    int rr = idx / (16 * NC), rem = idx % (16 * NC), i = rem / NC, m = rem % NC;
+    float v = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < WK; ++s2) v += red[rr * WK + s2][i][m];
+    fin[rr][i][m] = v;
+  }
+  __syncthreads();
+
+  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, pre, w, lane, rg, ks, g, sidx, M);
+}
+
 }  // namespace sd

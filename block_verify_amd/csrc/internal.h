@@ -95,7 +95,7 @@ constexpr int kMaxHidden = 4096;   // the largest hidden size a model may have
 #define SD_DOWN_SPLIT 2
 #endif
 constexpr int kDownSplit = SD_DOWN_SPLIT;
-constexpr int kQ4DownSplit = 4;
+
 // With two K splits the producer takes kSplit0Share / 64 of the k-blocks
 // (the finisher, which waits for its partials, the rest), as long as the
 // finisher's waves still stream their share in one batch.
@@ -134,8 +134,10 @@ hipError_t launch_forward(const FwdArgs& a);
 // group; GATE / UP interleave 8 gate rows and the 8 matching up rows.
 enum PackKind { PACK_PLAIN = 0, PACK_ROPE = 1, PACK_GATE = 2, PACK_UP = 3 };
 
-// 4-bit group-64 linears (kernels_q4.hip).  Rows per pass of a 4-bit model.
-constexpr int kQ4MaxRows = 4;
+// 4-bit group-64 linears (kernels_q4.hip).  One workgroup covers at most
+// kQ4MaxBlocks blocks of 128 inputs of a linear's K (the down projection
+// splits its K over up to kMaxSplit workgroups).
+constexpr int kQ4MaxBlocks = 32;
 // Packed sizes of one 4-bit linear with N outputs and K inputs.
 inline size_t q4_code_bytes(int N, int K) { return (size_t)N * ((K + 127) / 128) * 64; }
 inline size_t q4_scale_bytes(int N, int K) { return (size_t)N * ((K + 127) / 128) * 8; }
@@ -145,7 +147,6 @@ hipError_t launch_q4_linear(Q4Linear which, const GemvParams& p, const uint8_t* 
                             hipStream_t s);
 hipError_t launch_pack_q4(const void* src, int rows, int K, int kind, int hd, int group_base, uint8_t* codes,
                           uint8_t* scales, hipStream_t s);
-size_t q4_lds_bytes(int rows, int K, int nsplit);
 hipError_t launch_pack(const Dims& d, int index, const void* src, void* blob, const BlobLayout& lay, hipStream_t s);
 hipError_t launch_trim(int32_t* d_len, int32_t new_len, const int32_t* d_base, int32_t* err, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, hipStream_t s);

@@ -444,72 +444,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
     prefetch();
   }
   if constexpr (kNorm) norm_finish<RPW, NW>(p, w, lane, M, ssv, rsc);
-  // hi + lo (columns 2c and 2c + 1) in registers, then the waves' partials in LDS
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = acc[t][r] + swap1(acc[t][r]);
-      if ((lane & 1) == 0) red[w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
-    }
-  __syncthreads();
-  if constexpr (E == Epi::SWIGLU) {
-    // the epilogue wave sums the k-split partials of its own entries, in the
-    // order of the reduction below, and needs no second pass through LDS
-    if (ks != 0 || g >= n_groups) return;
-    const int KBo = p.F >> 5;
-    for (int idx = lane; idx < 8 * M; idx += 64) {
-      const int i = idx & 7, m = idx >> 3;
-      float gt = 0.f, up = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < WK; ++s2) {
-        gt += red[rg * WK + s2][i][m];
-        up += red[rg * WK + s2][i + 8][m];
-      }
-      const float r = rsc[m];
-      gt *= r;
-      up *= r;
-      btile_put(p.hb_out, KBo, m, 8 * g + i, gt / (1.0f + __expf(-gt)) * up);
-    }
-    return;
-  } else if constexpr (E != Epi::LMHEAD) {
-    // one wave per row group: it sums the k-split partials of the group (in
-    // the order of the reduction below) into its first wave's slot, which
-    // then serves as the group's finished products
-    if (ks != 0 || g >= n_groups) return;
-    constexpr int kE = (16 * NC + 63) / 64;
-    float v[kE];
-#pragma unroll
-    for (int j = 0; j < kE; ++j) {
-      const int idx = lane + 64 * j;
-      if (idx < 16 * NC) {
-        const int i = idx / NC, m = idx % NC;
-        v[j] = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < WK; ++s2) v[j] += red[rg * WK + s2][i][m];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kE; ++j) {
-      const int idx = lane + 64 * j;
-      if (idx < 16 * NC) red[rg * WK][idx / NC][idx % NC] = v[j];
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    gemv_epilogue<WG_ROWS, NC, E>(p, red + rg * (WK - 1), rsc, pre, w, lane, rg, 0, g, sidx, M);
-    return;
-  }
-  // fixed-order reduction over the k-split waves (whole-workgroup epilogue)
-  for (int idx = threadIdx.x; idx < WG_ROWS * 16 * NC; idx += blockDim.x) {
-    int rr = idx / (16 * NC), rem = idx % (16 * NC), i = rem / NC, m = rem % NC;
-    float v = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < WK; ++s2) v += red[rr * WK + s2][i][m];
-    fin[rr][i][m] = v;
-  }
-  __syncthreads();
-
-  gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, pre, w, lane, rg, ks, g, sidx, M);
+  gemv_finish<NT, WG_ROWS, WK, E>(p, acc, red, fin, rsc, pre, w, lane, rg, ks, g, sidx, M, n_groups);
 }
 
 // ---------------------------------------------------------------------------
@@ -1028,7 +963,7 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.A = L.wdown; p.B = reinterpret_cast<const bf16x8_t*>(hb); p.KB = d.F / 32; p.n_groups = d.H / 16;
   p.x = x; p.gain_next = (l + 1 < d.L) ? a.m->layers[l + 1].attn_norm : a.m->final_norm; p.xb_out = xb; p.ss_out = ss;
   p.part = reinterpret_cast<float*>(ws + pl.part);
-  p.nsplit = q4 ? kQ4DownSplit : kDownSplit;
+  p.nsplit = kDownSplit;   // 4-bit launches size their own splits
   p.cnt = reinterpret_cast<int32_t*>(ws + pl.cnt);   // the last split finishes the residual
   if (q4) launch_q4_linear(Q4Linear::DOWN, p, L.q_wdown, L.s_wdown, d.F, s);
   else
@@ -1070,7 +1005,6 @@ static hipError_t launch_forward_nt(const FwdArgs& a) {
 }
 
 hipError_t launch_forward(const FwdArgs& a) {
-  if (a.m->d.wfmt == SPECDEC_W_Q4G64 && a.rows > kQ4MaxRows) return hipErrorInvalidValue;
   int nt = (a.rows + 7) / 8;
   switch (nt) {
     case 1: return launch_forward_nt<1>(a);

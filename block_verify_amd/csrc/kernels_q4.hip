@@ -6,33 +6,36 @@
 // half-precision scale and zero; the embedding and LM head stay bf16 and are
 // shared with the target.
 //
-// The product is HBM-bound (0.5625 bytes per weight), so no matrix cores:
-// each lane decodes 32 codes per 16-byte load into exact fp16 integers with
-// one and-or per code pair (the codes are or-ed into the mantissa of 1024.0
-// and 1024.0 is subtracted), and accumulates code * x pairs with the fp32
-// two-way dot product.  The zero point is applied once per half group:
-//   sum_i (q_i - z) * s * x_i = s * (sum_i q_i * x_i - z * sum_i x_i),
-// with sum_i x_i taken per 32 inputs from sums of 8 made while the
-// activation rows (at most four) are staged in LDS as fp16; each wave
-// requests its first batch of codes before that staging.  Reductions run in a fixed order, so a
-// row's result does not depend on how many rows share the pass.
+// The product runs on the matrix cores like the bf16 one, against the same
+// hi/lo activation tiles read straight from L2.  A code c becomes the exact
+// bf16 value 128 + c with one and-or per code pair (c fills the low mantissa
+// bits of 128.0), so an MFMA of the codes' tile accumulates
+//   sum_i (128 + c_i) x_i,
+// and a second MFMA with a tile of ones the group's sum_i x_i.  Per row and
+// group of 64 inputs the weight sum is then
+//   sum_i (c_i - z) s x_i = s * (sum_i (128 + c_i) x_i - (128 + z) * sum_i x_i),
+// applied to the two accumulators in fp32 after each group.  Every product is
+// exact and each column (activation row) is independent, so a row's result
+// does not depend on how many rows share the pass.
 #include "gemv_common.h"
 
 namespace sd {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4q_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Packing (setup).  Source: codes uint8 [N][K/2] (even input in the low
 // nibble), then fp16 scale [N][K/64], then fp16 zero [N][K/64].
 // Destination, per 16-row group g and 128-input block b:
-//   codes  [g][b][lane][4 words]: lane l holds row l % 16, inputs
-//          128 b + 32 (l / 16) .. +31; word j covers 8 of them with input
-//          2c in nibble c and input 2c + 1 in nibble c + 4 (c = 0..3), so an
-//          and-or with 0x000F000F after a shift by 4c yields the fp16 pair.
-//   scales [g][b][half][16 rows] of (scale, zero) fp16 pairs.
+//   codes  [g][b][lane][4 words]: lane l holds row l % 16; word j covers
+//          inputs 128 b + 32 j + 8 (l / 16) .. +7 (the MFMA operand A
+//          slice of k-block j), input 2c of the eight in nibble c and input
+//          2c + 1 in nibble c + 4, so that ((word >> 4c) & 0x000F000F)
+//          holds operand pair c;
+//   scales [g][b][half][16 rows] of (scale, zero) fp16 pairs, rows in the
+//          order of the MFMA result (lane l reads rows 4 (l / 16) .. +3).
 // A block past K (K % 128 == 64) holds zero codes and zero scale / zero.
 // ---------------------------------------------------------------------------
 __global__ void pack_q4_kernel(const uint8_t* __restrict__ src, int rows, int K, int kind, int hd, int group_base,
@@ -44,17 +47,14 @@ __global__ void pack_q4_kernel(const uint8_t* __restrict__ src, int rows, int K,
        idx += (size_t)gridDim.x * blockDim.x) {
     const int r = (int)(idx / ((size_t)NB * 4));
     const int rem = (int)(idx % ((size_t)NB * 4));
-    const int b = rem >> 2, qq = rem & 3;
+    const int b = rem >> 2, j = rem & 3;   // block, k-block within it
     int g, i;
     pack_row_slot(kind, r, hd, g, i);
     g += group_base;
-    const int lane = qq * 16 + i;
-    const int k0 = b * 128 + 32 * qq;
-    uint32_t* dst = codes + (((size_t)g * NB + b) * 64 + lane) * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int q = 0; q < 4; ++q) {
       uint32_t word = 0;
-      const int kk = k0 + 8 * j;
+      const int kk = b * 128 + 32 * j + 8 * q;
       if (kk < K) {
         const uint8_t* sb = src + (size_t)r * (K / 2) + kk / 2;
 #pragma unroll
@@ -64,16 +64,16 @@ __global__ void pack_q4_kernel(const uint8_t* __restrict__ src, int rows, int K,
           word |= (byte >> 4) << (16 + 4 * c);
         }
       }
-      dst[j] = word;
+      codes[(((size_t)g * NB + b) * 64 + (q * 16 + i)) * 4 + j] = word;
     }
-    if ((qq & 1) == 0) {
-      const int gi = 2 * b + (qq >> 1);
+    if (j < 2) {
+      const int gi = 2 * b + j;
       uint32_t sz = 0;
       if (gi * 64 < K) {
         const size_t si = (size_t)r * (K / 64) + gi;
         sz = (uint32_t)sc[si] | ((uint32_t)zc[si] << 16);
       }
-      scales[(((size_t)g * NB + b) * 2 + (qq >> 1)) * 16 + i] = sz;
+      scales[(((size_t)g * NB + b) * 2 + j) * 16 + i] = sz;
     }
   }
 }
@@ -90,275 +90,249 @@ hipError_t launch_pack_q4(const void* src, int rows, int K, int kind, int hd, in
 }
 
 // ---------------------------------------------------------------------------
-// 4-bit skinny product.  Workgroup = WG_ROWS row groups x WK k-split waves
-// (PARTIAL: one row group, split nsplit ways over the workgroups).
+// 4-bit skinny product.
 // ---------------------------------------------------------------------------
-struct Q4Params {
-  const u32x4_t* codes;
-  const uint32_t* scales;
-  int K;    // inputs
-  int NB;   // 128-input blocks
+constexpr uint32_t kQ4Magic = 0x43004300u;   // bf16 128.0 in both halves
+constexpr int32_t kBf16OnePair = 0x3F803F80;
+
+// Operand A of one k-block: eight codes -> eight bf16 values 128 + code.
+__device__ __forceinline__ i32x4q_t q4_decode(uint32_t w) {
+  i32x4q_t a;
+  a[0] = (int32_t)((w & 0x000F000Fu) | kQ4Magic);
+  a[1] = (int32_t)(((w >> 4) & 0x000F000Fu) | kQ4Magic);
+  a[2] = (int32_t)(((w >> 8) & 0x000F000Fu) | kQ4Magic);
+  a[3] = (int32_t)(((w >> 12) & 0x000F000Fu) | kQ4Magic);
+  return a;
+}
+
+__device__ __forceinline__ f32x4_t mfma_q(const i32x4q_t& a, const i32x4q_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit skinny product.  A workgroup of kQ4RWaves waves takes up to `rg`
+// row groups over one k-range (a split of the K range for the down
+// projection; one split holds at most kQ4RWaves * kQ4RBlocks blocks of 128
+// inputs).  Wave w keeps the activation tiles of its <= kQ4RBlocks blocks in
+// registers, with their per-group sums, and streams the code tiles of the
+// workgroup's row groups through them, the next row group's codes requested
+// before the current one is computed.  The activations are the MFMA's
+// operand A and the codes operand B, so the result C[m'][n] holds
+// activation column m' (the hi or lo part of a row) against output row
+// n = lane % 16: each lane applies one row's scale per group.  A pass of more
+// than 8 rows repeats this per column tile of 8 rows (the codes streamed once
+// per tile), so each row's arithmetic -- the k-range of every wave, the
+// order of its blocks and the wave order of the sum -- does not depend on the
+// pass.  The waves' partials meet in LDS; wave w runs the epilogues of row
+// groups w, w + kQ4RWaves, ...
+// ---------------------------------------------------------------------------
+#ifndef SD_Q4_AHEAD
+#define SD_Q4_AHEAD 3
+#endif
+#ifndef SD_Q4_WAVES
+#define SD_Q4_WAVES 8
+#endif
+constexpr int kQ4RWaves = SD_Q4_WAVES, kQ4RBlocks = kQ4MaxBlocks / kQ4RWaves;
+static_assert(kQ4RWaves * kQ4RBlocks == kQ4MaxBlocks, "one split's blocks");
+// row groups of codes in flight per wave (fewer for wide passes: registers)
+template <int NT>
+struct Q4Ahead {
+  static constexpr int value = NT == 1 ? SD_Q4_AHEAD : 2;
+};
+template <int NT>
+struct Q4RGroups {
+  // LDS: the partials of RG row groups from every wave, <= ~110 KB
+  static constexpr int value = (NT == 1 ? 12 : NT == 2 ? 6 : NT == 3 ? 4 : 3) * 8 / kQ4RWaves;
 };
 
-template <int WG_ROWS, int WK, int U, Epi E>
-__global__ __launch_bounds__(64 * WG_ROWS * WK) void q4_gemv_kernel(GemvParams p, Q4Params q) {
-  EpiPre<8> pre;
-  // the gate word (the length stands in for a null gate) and the cache
-  // position are requested together, before any branch
-  const int gv = *(p.gate ? p.gate : p.d_len);
-  if constexpr (E == Epi::QKV) pre.pos0 = *p.d_len;
-  if (p.gate && gv == 0) return;
-  constexpr int NW = WG_ROWS * WK;
-  constexpr int NC = 8;
-  constexpr int RPW = (kQ4MaxRows + NW - 1) / NW;
-  constexpr int NT = 64 * NW;
-  extern __shared__ __align__(16) unsigned char q4_lds[];
-  __shared__ float red[NW][16][NC + 1];
+template <int NT, Epi E>
+__global__ __launch_bounds__(64 * kQ4RWaves) void q4_gemv_kernel(const int32_t* gate, const int32_t* d_len,
+                                                                 const u32x4_t* __restrict__ codes,
+                                                                 const uint32_t* __restrict__ scales,
+                                                                 const bf16x8_t* __restrict__ B, int KB, int NB,
+                                                                 int n_groups, int rows, int nsplit_arg, int rg_per_wg,
+                                                                 GemvParams p) {
+  constexpr int NW = kQ4RWaves, NC = 8 * NT, BLK = kQ4RBlocks, RG = Q4RGroups<NT>::value;
+  constexpr int kQ4Ahead = Q4Ahead<NT>::value;
+  constexpr int RPW = (NC + NW - 1) / NW;
+  EpiPre<NC> pre;
+  if constexpr (E == Epi::QKV) pre.pos0 = *d_len;
+  if (gate) {
+    if (*gate == 0) return;
+  }
+  __shared__ float red[RG][NW][16][NC + 1];
   __shared__ float rsc[kMaxRows];
-
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = w / WK, ks = w % WK;
-  const int nsplit = (E == Epi::PARTIAL) ? p.nsplit : 1;
-  const int sidx = (E == Epi::PARTIAL) ? (int)(blockIdx.x % nsplit) : 0;
-  const int g = (E == Epi::PARTIAL) ? (int)(blockIdx.x / nsplit) : (int)(blockIdx.x * WG_ROWS + rg);
-  const int M = p.rows;
-  // 32-bit unsigned arithmetic (small terms; a 64-bit division is long)
-  const int b0s = (int)((unsigned)sidx * (unsigned)q.NB / (unsigned)nsplit);
-  const int b1s = (int)((unsigned)(sidx + 1) * (unsigned)q.NB / (unsigned)nsplit);
-  const int KR = (b1s - b0s) * 128;
-  _Float16* xs = reinterpret_cast<_Float16*>(q4_lds);                       // [M][KR]
-  float* x8 = reinterpret_cast<float*>(q4_lds + (size_t)M * KR * 2);       // [M][KR / 8] sums of 8
-
-  // The activation rows of this split are staged in LDS as fp16 (x = hi + lo
-  // of the tiles) with the float sum of every 8 staged values.  Their loads
-  // (L2-resident) go out first, SP per thread, then the wave's first batch of
-  // codes (HBM): loads complete in issue order, so writing the activations to
-  // LDS then waits for them only.  The loads are unconditional (an index past
-  // the rows re-reads entry 0): guarded loads into registers are each waited on.
-  const bf16_bits* bt = reinterpret_cast<const bf16_bits*>(p.B);
-  const int k8n = KR >> 3, nstage = M * k8n;
-  // staging pairs in flight per thread: enough for one activation row of
-  // the 7B-shape splits in one pass (the down projection's split is longest)
-  constexpr int SP = (E == Epi::PARTIAL) ? 3 : 1;
-  uint4 hv[SP], lv[SP];
-  auto stage_load = [&](int base) {
-#pragma unroll
-    for (int j = 0; j < SP; ++j) {
-      int idx = base + (int)threadIdx.x + NT * j;
-      if (idx >= nstage) idx = 0;
-      const int m = idx / k8n;
-      int k = b0s * 128 + (idx % k8n) * 8;
-      if (k >= q.K) k = 0;   // the block past K reads a valid tile and stores zeros
-      const size_t bi = btile_index(p.KB, m, k);
-      hv[j] = *reinterpret_cast<const uint4*>(bt + bi);
-      lv[j] = *reinterpret_cast<const uint4*>(bt + bi + kBtileLo);
-    }
-  };
-  auto stage_store = [&](int base) {
-#pragma unroll
-    for (int j = 0; j < SP; ++j) {
-      const int idx = base + (int)threadIdx.x + NT * j;
-      if (idx < nstage) {
-        const int m = idx / k8n, k = b0s * 128 + (idx % k8n) * 8;
-        half8_t o;
-        if (k < q.K) {
-          const uint32_t hw[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w}, lw[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[2 * e] = (_Float16)(__uint_as_float(hw[e] << 16) + __uint_as_float(lw[e] << 16));
-            o[2 * e + 1] = (_Float16)(__uint_as_float(hw[e] & 0xFFFF0000u) + __uint_as_float(lw[e] & 0xFFFF0000u));
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (_Float16)0.0f;
-        }
-        *reinterpret_cast<half8_t*>(xs + (size_t)m * KR + (k - b0s * 128)) = o;
-        float s8 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s8 += (float)o[e];
-        x8[idx] = s8;
-      }
-    }
-  };
+  const int nsplit = (E == Epi::PARTIAL) ? nsplit_arg : 1;
+  const unsigned slot = blockIdx.x >> 3;
+  const int sidx = (E == Epi::PARTIAL) ? (int)(slot % (unsigned)nsplit) : 0;
+  const int unit = (E == Epi::PARTIAL) ? (int)((slot / (unsigned)nsplit) * 8 + (blockIdx.x & 7)) : (int)blockIdx.x;
+  const int g0 = unit * rg_per_wg;
+  int nrg = n_groups - g0;
+  if (nrg > rg_per_wg) nrg = rg_per_wg;
+  const int M = rows;
+  // this wave's blocks of this split
+  const unsigned un = (unsigned)nsplit, ub = (unsigned)NB;
+  const int s0 = (int)((unsigned)sidx * ub / un), s1 = (int)((unsigned)(sidx + 1) * ub / un);
+  const unsigned span = (unsigned)(s1 - s0);
+  const int b0 = s0 + (int)((unsigned)w * span / NW), b1 = s0 + (int)((unsigned)(w + 1) * span / NW);
+  const int nb = b1 - b0;   // <= BLK (the launch sizes the splits so)
 
   constexpr bool kNorm = (E == Epi::QKV || E == Epi::SWIGLU);
   float ssv[RPW][4];
-  const bool active = g < p.n_groups;
-  const int nb = b1s - b0s;
-  const int kb0 = b0s + (int)((unsigned)ks * (unsigned)nb / WK), kb1 = b0s + (int)((unsigned)(ks + 1) * (unsigned)nb / WK);
-  const int n = active ? kb1 - kb0 : 0;
-  const u32x4_t* cp = q.codes + (size_t)(active ? g : 0) * q.NB * 64 + lane;
-  const uint32_t* sp = q.scales + (size_t)(active ? g : 0) * q.NB * 32 + (lane >> 5) * 16 + (lane & 15);
+  if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
 
-  // Runs once per wave after its first code requests: the small prefetches,
-  // the staging writes (and any further staging) and the workgroup barrier.
-  auto after_first = [&] {
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kNorm) norm_prefetch<RPW, NW>(p, w, lane, M, ssv);
-    if (ks == 0) {
-      epi_prefetch_x<E, NC>(p, lane, g, M, pre);
-      epi_prefetch_rope<E, NC>(p, lane, g, M, pre);
+  const int col = lane & 15, q = lane >> 4;
+  const u32x4_t* cbase = codes + (size_t)b0 * 64 + lane;
+  const uint32_t* sbase = scales + (size_t)b0 * 32 + col;
+  auto load_rg = [&](int g, u32x4_t (&c)[BLK], uint32_t (&sc)[BLK][2]) {
+#pragma unroll
+    for (int jb = 0; jb < BLK; ++jb) {
+      const int b = jb < nb ? jb : 0;
+      c[jb] = __builtin_nontemporal_load(cbase + ((size_t)g * NB + b) * 64);
+      sc[jb][0] = __builtin_nontemporal_load(sbase + ((size_t)g * NB + b) * 32);
+      sc[jb][1] = __builtin_nontemporal_load(sbase + ((size_t)g * NB + b) * 32 + 16);
     }
-    stage_store(0);
-    for (int base = SP * NT; base < nstage; base += SP * NT) {
-      stage_load(base);
-      stage_store(base);
-    }
-    __syncthreads();
   };
-
-  float y[kQ4MaxRows];
+  const i32x4q_t ones = {kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+#pragma unroll 1
+  for (int t = 0; t < NT; ++t) {
+    // activation tiles of column tile t for the wave's blocks (operand A):
+    // unconditional loads of clamped indices; operand columns past the rows
+    // read row 0's slot (their products are never used)
+    const int aslot = btile_slot((col >> 1) < M - 8 * t ? col : (col & 1), q);
+    const i32x4q_t* bt = reinterpret_cast<const i32x4q_t*>(B) + (size_t)t * KB * 64 + aslot;
+    i32x4q_t act[BLK][4];
 #pragma unroll
-  for (int m = 0; m < kQ4MaxRows; ++m) y[m] = 0.f;
-  const int qq = lane >> 4;
-  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  // One batch of U code blocks from block b: straight-line loads (slots past
-  // the wave's last block re-read it and are skipped), then the blocks in order.
-  auto batch = [&](int b, bool first) {
-    u32x4_t cv[U];
-    uint32_t sv[U];
+    for (int jb = 0; jb < BLK; ++jb)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int bb = b + u < kb1 ? b + u : kb1 - 1;
-      cv[u] = __builtin_nontemporal_load(cp + (size_t)bb * 64);
-      sv[u] = __builtin_nontemporal_load(sp + (size_t)bb * 32);
+      for (int j = 0; j < 4; ++j) {
+        int kb = 4 * (b0 + jb) + j;
+        if (jb >= nb || kb >= KB) kb = 0;   // a valid tile, never used
+        act[jb][j] = bt[(size_t)kb * 64];
+      }
+    // the codes of the first kQ4Ahead - 1 row groups go out with the activation
+    // loads; row group r + kQ4Ahead - 1 is requested before r is computed
+    u32x4_t cv[kQ4Ahead][BLK];
+    uint32_t sw[kQ4Ahead][BLK][2];
+#pragma unroll
+    for (int k = 0; k < kQ4Ahead - 1; ++k)
+      if (k < nrg) load_rg(g0 + k, cv[k], sw[k]);
+    if (t == 0 && w < nrg) {
+      // the epilogue operands of this wave's row group (wave r ends row group r)
+      epi_prefetch_x<E, NC>(p, lane, g0 + w, M, pre);
+      epi_prefetch_rope<E, NC>(p, lane, g0 + w, M, pre);
     }
-    if (first) after_first();
+    f32x4_t sgs[BLK][2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (b + u >= kb1) break;
-      half2_t qv[16];
-      const uint32_t cw[4] = {cv[u][0], cv[u][1], cv[u][2], cv[u][3]};
+    for (int jb = 0; jb < BLK; ++jb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t t = ((cw[j] >> (4 * c)) & 0x000F000Fu) | 0x64006400u;
-          qv[4 * j + c] = __builtin_bit_cast(half2_t, t) - k1024;
-        }
-      const half2_t szh = __builtin_bit_cast(half2_t, sv[u]);
-      const float s = (float)szh[0], z = (float)szh[1];
-      const int xoff = (b + u - b0s) * 128 + 32 * qq;
-#pragma unroll
-      for (int m = 0; m < kQ4MaxRows; ++m) {
-        if (m < M) {
-          const half8_t* xp = reinterpret_cast<const half8_t*>(xs + (size_t)m * KR + xoff);
-          const float4 xq = *reinterpret_cast<const float4*>(x8 + (size_t)m * k8n + (xoff >> 3));
-          float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const half8_t xv = xp[v];
-            a0 = __builtin_amdgcn_fdot2(qv[4 * v], half2_t{xv[0], xv[1]}, a0, false);
-            a1 = __builtin_amdgcn_fdot2(qv[4 * v + 1], half2_t{xv[2], xv[3]}, a1, false);
-            a0 = __builtin_amdgcn_fdot2(qv[4 * v + 2], half2_t{xv[4], xv[5]}, a0, false);
-            a1 = __builtin_amdgcn_fdot2(qv[4 * v + 3], half2_t{xv[6], xv[7]}, a1, false);
-          }
-          const float xsum = ((xq.x + xq.y) + xq.z) + xq.w;
-          y[m] = fmaf(s, (a0 + a1) - z * xsum, y[m]);
+      for (int h = 0; h < 2; ++h) {
+        sgs[jb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (jb < nb && 4 * (b0 + jb) + 2 * h < KB) {
+          sgs[jb][h] = mfma_q(act[jb][2 * h], ones, sgs[jb][h]);
+          sgs[jb][h] = mfma_q(act[jb][2 * h + 1], ones, sgs[jb][h]);
         }
       }
+    for (int r0 = 0; r0 < nrg; r0 += kQ4Ahead) {
+#pragma unroll
+      for (int k = 0; k < kQ4Ahead; ++k) {
+        const int r = r0 + k;
+        if (r >= nrg) break;
+        // stage k holds row group r; stage (k + kQ4Ahead - 1) % kQ4Ahead takes r + kQ4Ahead - 1
+        constexpr int kA = Q4Ahead<NT>::value;
+        if (r + kA - 1 < nrg) load_rg(g0 + r + kA - 1, cv[(k + kA - 1) % kA], sw[(k + kA - 1) % kA]);
+        f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < BLK; ++jb) {
+          if (jb >= nb) break;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if (4 * (b0 + jb) + 2 * h >= KB) break;
+            f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+            ag = mfma_q(act[jb][2 * h], q4_decode(cv[k][jb][2 * h]), ag);
+            ag = mfma_q(act[jb][2 * h + 1], q4_decode(cv[k][jb][2 * h + 1]), ag);
+            // output row n = lane % 16: y += s * (ag - (128 + z) * sg)
+            const half2_t sz = __builtin_bit_cast(half2_t, sw[k][jb][h]);
+            const float sc = (float)sz[0], tz = sc * (128.0f + (float)sz[1]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = fmaf(-tz, sgs[jb][h][e], fmaf(sc, ag[e], y[e]));
+          }
+        }
+        // C[m'][n], m' = 4 q + e: the hi and lo parts of activation row m' / 2
+        red[r][w][col][8 * t + 2 * q] = y[0] + y[1];
+        red[r][w][col][8 * t + 2 * q + 1] = y[2] + y[3];
+      }
     }
-  };
-
-  stage_load(0);
-  if (n <= 0) {
-    after_first();
-  } else {
-    // the first batch is peeled: the staging registers are dead after it
-    batch(kb0, true);
-    for (int b = kb0 + U; b < kb1; b += U) batch(b, false);
   }
   if constexpr (kNorm) norm_finish<RPW, NW>(p, w, lane, M, ssv, rsc);
-  // the four quarters of a row (lanes i, i+16, i+32, i+48), then the waves
-#pragma unroll
-  for (int m = 0; m < kQ4MaxRows; ++m) {
-    float v = y[m];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    if (lane < 16 && m < M) red[w][lane][m] = v;
-  }
   __syncthreads();
-  // one wave per row group sums the group's k-split partials (in wave
-  // order) into its first wave's slot and runs the epilogue from there
-  if (ks != 0 || g >= p.n_groups) return;
-  constexpr int kE = (16 * kQ4MaxRows + 63) / 64;
-  float v[kE];
-#pragma unroll
-  for (int j = 0; j < kE; ++j) {
-    const int idx = lane + 64 * j;
-    if (idx < 16 * M) {
-      const int i = idx / M, m = idx % M;
-      v[j] = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < WK; ++s2) v[j] += red[rg * WK + s2][i][m];
+  // wave w ends row groups w, w + NW, ...: the k-range partials of the row
+  // group in wave order, then its epilogue (operands of the first prefetched
+  // under the stream)
+  for (int rr = w; rr < nrg; rr += NW) {
+    if (rr != w) {
+      epi_prefetch_x<E, NC>(p, lane, g0 + rr, M, pre);
+      epi_prefetch_rope<E, NC>(p, lane, g0 + rr, M, pre);
     }
-  }
+    float (*rw)[16][NC + 1] = red[rr];
+    for (int idx = lane; idx < 16 * M; idx += 64) {
+      const int i = idx & 15, m = idx >> 4;
+      float v = 0.f;
 #pragma unroll
-  for (int j = 0; j < kE; ++j) {
-    const int idx = lane + 64 * j;
-    if (idx < 16 * M) red[rg * WK][idx / M][idx % M] = v[j];
+      for (int s2 = 0; s2 < NW; ++s2) v += rw[s2][i][m];
+      rw[0][i][m] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    gemv_epilogue<RG, NC, E>(p, reinterpret_cast<float(*)[16][NC + 1]>(&red[0][0]) + rr * (NW - 1), rsc, pre, w,
+                             lane, rr, 0, g0 + rr, sidx, M);
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  gemv_epilogue<WG_ROWS, NC, E>(p, red + rg * (WK - 1), rsc, pre, w, lane, rg, 0, g, sidx, M);
 }
 
-// Launch shapes (row groups per workgroup, k-split waves, code blocks in
-// flight per wave); the down projection takes one row group per workgroup.
-#ifndef SD_Q4_QKV
-#define SD_Q4_QKV 1, 8, 4
-#endif
-#ifndef SD_Q4_O
-#define SD_Q4_O 1, 8, 4
-#endif
-#ifndef SD_Q4_GU
-#define SD_Q4_GU 2, 4, 8
-#endif
-#ifndef SD_Q4_DOWN
-#define SD_Q4_DOWN 4, 10
-#endif
-template <int R, int W, int T>
-constexpr int Q4Rows() { return R; }
-
-size_t q4_lds_bytes(int rows, int K, int nsplit) {
-  const int NB = (K + 127) / 128;
-  const int per = (NB + nsplit - 1) / nsplit + 1;
-  const size_t KR = (size_t)per * 128;
-  return (size_t)rows * KR * 2 + (size_t)rows * (KR / 8) * 4;
-}
-
-template <int WG_ROWS, int WK, int U, Epi E>
-static hipError_t launch_q4(const GemvParams& p, const Q4Params& q, int grid, hipStream_t s) {
-  const int nsplit = (E == Epi::PARTIAL) ? p.nsplit : 1;
-  const int b0 = 0;
-  (void)b0;
-  // largest split of this launch
-  int most = 0;
-  for (int si = 0; si < nsplit; ++si) {
-    int a = (int)(((long)si * q.NB) / nsplit), b = (int)(((long)(si + 1) * q.NB) / nsplit);
-    if (b - a > most) most = b - a;
-  }
-  const size_t lds = (size_t)p.rows * most * 128 * 2 + (size_t)p.rows * most * 16 * 4;
-  q4_gemv_kernel<WG_ROWS, WK, U, E><<<grid, 64 * WG_ROWS * WK, lds, s>>>(p, q);
+template <int NT, Epi E>
+static hipError_t launch_q4(const GemvParams& p, const uint8_t* codes, const uint8_t* scales, int NB, int nsplit,
+                            hipStream_t s) {
+  // row groups per workgroup: about one workgroup per CU
+  int rg = (p.n_groups * nsplit + 255) / 256;
+  if (rg < 1) rg = 1;
+  if (rg > Q4RGroups<NT>::value) rg = Q4RGroups<NT>::value;
+  const int units = (p.n_groups + rg - 1) / rg;
+  const int grid = E == Epi::PARTIAL ? (units + 7) / 8 * 8 * nsplit : units;
+  GemvParams q = p;
+  q.nsplit = nsplit;
+  q4_gemv_kernel<NT, E><<<grid, 64 * kQ4RWaves, 0, s>>>(p.gate, p.d_len, reinterpret_cast<const u32x4_t*>(codes),
+                                                         reinterpret_cast<const uint32_t*>(scales), p.B, p.KB, NB,
+                                                         p.n_groups, p.rows, nsplit, rg, q);
   return hipGetLastError();
+}
+
+template <int NT>
+static hipError_t launch_q4_nt(Q4Linear which, const GemvParams& p, const uint8_t* codes, const uint8_t* scales,
+                               int NB, hipStream_t s) {
+  constexpr int reach = kQ4RWaves * kQ4RBlocks;
+  switch (which) {
+    case Q4Linear::QKV: return launch_q4<NT, Epi::QKV>(p, codes, scales, NB, 1, s);
+    case Q4Linear::O: return launch_q4<NT, Epi::RESID>(p, codes, scales, NB, 1, s);
+    case Q4Linear::GATE_UP: return launch_q4<NT, Epi::SWIGLU>(p, codes, scales, NB, 1, s);
+    case Q4Linear::DOWN: return launch_q4<NT, Epi::PARTIAL>(p, codes, scales, NB, (NB + reach - 1) / reach, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_q4_linear(Q4Linear which, const GemvParams& p, const uint8_t* codes, const uint8_t* scales, int K,
                             hipStream_t s) {
-  Q4Params q;
-  q.codes = reinterpret_cast<const u32x4_t*>(codes);
-  q.scales = reinterpret_cast<const uint32_t*>(scales);
-  q.K = K;
-  q.NB = (K + 127) / 128;
-  switch (which) {
-    case Q4Linear::QKV:
-      return launch_q4<SD_Q4_QKV, Epi::QKV>(p, q, (p.n_groups + Q4Rows<SD_Q4_QKV>() - 1) / Q4Rows<SD_Q4_QKV>(), s);
-    case Q4Linear::O:
-      return launch_q4<SD_Q4_O, Epi::RESID>(p, q, (p.n_groups + Q4Rows<SD_Q4_O>() - 1) / Q4Rows<SD_Q4_O>(), s);
-    case Q4Linear::GATE_UP:
-      return launch_q4<SD_Q4_GU, Epi::SWIGLU>(p, q, (p.n_groups + Q4Rows<SD_Q4_GU>() - 1) / Q4Rows<SD_Q4_GU>(), s);
-    case Q4Linear::DOWN: return launch_q4<1, SD_Q4_DOWN, Epi::PARTIAL>(p, q, p.n_groups * p.nsplit, s);
+  const int NB = (K + 127) / 128;
+  // one split covers kQ4MaxBlocks blocks: the K of QKV, O and gate/up, and
+  // kMaxSplit splits of the down projection's K (checked with the shape)
+  if ((which != Q4Linear::DOWN && NB > kQ4MaxBlocks) || NB > kMaxSplit * kQ4MaxBlocks) return hipErrorInvalidValue;
+  switch ((p.rows + 7) / 8) {
+    case 1: return launch_q4_nt<1>(which, p, codes, scales, NB, s);
+    case 2: return launch_q4_nt<2>(which, p, codes, scales, NB, s);
+    case 3: return launch_q4_nt<3>(which, p, codes, scales, NB, s);
+    case 4: return launch_q4_nt<4>(which, p, codes, scales, NB, s);
   }
   return hipErrorInvalidValue;
 }

@@ -171,8 +171,7 @@ int specdec_workspace_init(void* d_ws, size_t ws_bytes, void* stream);
  * d_tokens int32 [rows] (device).  Outputs (any may be NULL): d_logits fp32
  * [rows][vocab], d_argmax int32 [rows] (lowest index on ties), d_lse fp32
  * [rows] (log-sum-exp of the row).  This is the decode step (rows = 1) and
- * the block verify (rows = k or k+1).  4-bit models take rows <= 4
- * (SPECDEC_ECAPACITY beyond). */
+ * the block verify (rows = k or k+1). */
 int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t rows,
                         float* d_logits, int32_t* d_argmax, float* d_lse, void* d_ws, size_t ws_bytes,
                         void* stream);
@@ -190,9 +189,8 @@ int specdec_decode_step(const specdec_model* m, specdec_cache* c, const int32_t*
 /* Tree verify: the target's forward of all n (1..SPECDEC_MAX_TREE) nodes at
  * the current length t.  Node i attends to the cached positions 0 .. t-1 and
  * to its ancestors-or-self only, and appends its K/V at slot t + i; then
- * length = t + n.  The nodes run in passes of up to SPECDEC_MAX_ROWS (4 for
- * a 4-bit model) in node order, so a tree wider than a pass costs one
- * weight stream per pass.  d_logits fp32 [n][V], d_argmax int32 [n] and
+ * length = t + n.  The nodes run in passes of up to SPECDEC_MAX_ROWS in node
+ * order, so a tree wider than a pass costs one weight stream per pass.  d_logits fp32 [n][V], d_argmax int32 [n] and
  * d_lse fp32 [n] as for specdec_decode_step (any may be NULL; d_argmax is
  * what specdec_tree_accept reads).  A chain (d_parents = -1, 0, 1, ...)
  * computes exactly the block verify.  A parent that is not an earlier node
@@ -261,8 +259,7 @@ int specdec_decode_step_noalloc(const specdec_model* m, specdec_cache* c, const 
 int specdec_static_init(void* stream);
 
 /* Prefill `n` tokens in passes of `chunk` rows (chunk clipped to
- * SPECDEC_MAX_ROWS, or to 4 for a 4-bit model), starting at the current
- * length.  Writes the last row's
+ * SPECDEC_MAX_ROWS), starting at the current length.  Writes the last row's
  * logits / argmax / lse (any may be NULL). */
 int specdec_prefill(const specdec_model* m, specdec_cache* c, const int32_t* d_tokens, int32_t n, int32_t chunk,
                     float* d_last_logits, int32_t* d_last_argmax, float* d_last_lse, void* d_ws,

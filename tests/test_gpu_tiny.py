@@ -420,16 +420,17 @@ def q4env(env):
     return dict(model=qm, ow=q4_oracle_weights(S, env["w"], qt))
 
 
-@pytest.mark.parametrize("rows", [1, 3, 4])
-def test_q4_forward_matches_oracle(env, q4env, rows):
+@pytest.mark.parametrize("rows,chunk", [(1, 4), (3, 32), (9, 5), (32, 32)])
+def test_q4_forward_matches_oracle(env, q4env, rows, chunk):
     """The 4-bit substitute model (shared bf16 embedding / LM head) against the oracle
-    forward with the dequantised weights: prefill (4-row chunks) and a block of rows."""
+    forward with the dequantised weights: prefill (in `chunk`-row passes) and a block of
+    rows."""
     from oracle.model import OracleCache, forward, prefill
     b, S = env["b"], env["shape"]
     cache, ws = _fresh(env)
     t = torch.from_numpy(np.asarray(env["prompt"], np.int32)).cuda()
     saved = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
-    b.prefill(q4env["model"], cache, t, ws, chunk=4, logits=saved)
+    b.prefill(q4env["model"], cache, t, ws, chunk=chunk, logits=saved)
     oc = OracleCache(S, 512)
     o_saved = prefill(q4env["ow"], oc, env["prompt"])
     assert_logits_close(to_np(saved), o_saved, "q4 prefill saved_next")
@@ -448,20 +449,23 @@ def test_q4_forward_matches_oracle(env, q4env, rows):
 
 
 def test_q4_batch_invariance_and_row_limit(env, q4env):
+    """A row's 4-bit product does not depend on the pass: 17 rows at once (three column
+    tiles) equal the same rows one at a time and in a pass of 8, bit for bit."""
     b, S = env["b"], env["shape"]
     cache, ws = _fresh(env)
     t = torch.from_numpy(np.asarray(env["prompt"], np.int32)).cuda()
-    b.prefill(q4env["model"], cache, t, ws, chunk=4)
-    toks = torch.from_numpy(np.array([5, 77, 1024, 4095], np.int32)).cuda()
-    lb = torch.empty((4, S.vocab), dtype=torch.float32, device="cuda")
+    b.prefill(q4env["model"], cache, t, ws, chunk=32)
+    toks = torch.from_numpy(np.random.default_rng(17).integers(0, S.vocab, 17).astype(np.int32)).cuda()
+    lb = torch.empty((17, S.vocab), dtype=torch.float32, device="cuda")
     b.decode_step(q4env["model"], cache, toks, ws, logits=lb)
     cache.trim(P, ws)
-    ls = torch.empty((4, S.vocab), dtype=torch.float32, device="cuda")
-    for i in range(4):
+    ls = torch.empty((17, S.vocab), dtype=torch.float32, device="cuda")
+    b.decode_step(q4env["model"], cache, toks[:8], ws, logits=ls[:8])
+    for i in range(8, 17):
         b.decode_step(q4env["model"], cache, toks[i:i + 1], ws, logits=ls[i])
     assert torch.equal(lb.view(torch.int32), ls.view(torch.int32))
     with pytest.raises(b.SpecdecError):
-        b.decode_step(q4env["model"], cache, torch.zeros(5, dtype=torch.int32, device="cuda"), ws)
+        b.decode_step(q4env["model"], cache, torch.zeros(33, dtype=torch.int32, device="cuda"), ws)
 
 
 def test_q4_substitute_draft_rounds(env, q4env, gpu_ar):

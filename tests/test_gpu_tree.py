@@ -365,8 +365,8 @@ def q4draft(env):
     return b.Model(S, make_q4_draft(S, env["w"]), weight_format=b.W_Q4G64, share=env["model"])
 
 
-def test_q4_tree_draft_in_passes_of_four(env, q4draft):
-    """The 4-bit substitute builds with k = 6 leaves a step (passes of 4 and 2 rows)."""
+def test_q4_tree_draft_follows_the_selection_rule(env, q4draft):
+    """The 4-bit substitute builds with k = 6 leaves a step."""
     c, ws = _cache(env)
     c.trim(P - 1, ws)
     toks, pars, sc = _draft_tree(env, c, ws, 6, 3, draft=q4draft)
