@@ -45,15 +45,23 @@ namespace sd {
 // accumulated in order either way), so multi-tile passes cap it by the
 // registers a wave of this workgroup size may hold: (1 + NT) 4-register
 // tiles per k-block in flight, ~40 registers for the rest.
+// Passes of three or four column tiles keep at most 128 registers for tiles
+// in flight (two waves per SIMD or more; 29-row forwards 2418 -> 2285 us).
+#ifndef SD_WIDE_VGPRS
+#define SD_WIDE_VGPRS 128
+#endif
 template <int R, int W, int T>
 struct LaunchCfg {
   static constexpr int WG_ROWS = R, WK = W, THREADS = 64 * R * W;
-  static constexpr int kVgprs = (512 / (THREADS / 256 > 1 ? THREADS / 256 : 1)) < 256
-                                    ? 512 / (THREADS / 256 > 1 ? THREADS / 256 : 1) : 256;
+  static constexpr int kVgprsFit = (512 / (THREADS / 256 > 1 ? THREADS / 256 : 1)) < 256
+                                       ? 512 / (THREADS / 256 > 1 ? THREADS / 256 : 1) : 256;
+  template <int NT>
+  static constexpr int kVgprs = NT >= 3 && kVgprsFit > SD_WIDE_VGPRS ? SD_WIDE_VGPRS : kVgprsFit;
   template <int NT>
   static constexpr int U = NT == 1 ? T
-                                   : ((kVgprs - 40) / ((1 + NT) * 4) < T
-                                          ? ((kVgprs - 40) / ((1 + NT) * 4) > 1 ? (kVgprs - 40) / ((1 + NT) * 4) : 1)
+                                   : ((kVgprs<NT> - 40) / ((1 + NT) * 4) < T
+                                          ? ((kVgprs<NT> - 40) / ((1 + NT) * 4) > 1 ? (kVgprs<NT> - 40) / ((1 + NT) * 4)
+                                                                                     : 1)
                                           : T);
 };
 using CfgQKV = LaunchCfg<SD_CFG_QKV>;
