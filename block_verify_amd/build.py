@@ -27,12 +27,16 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    """Compile and link the library.  SPECDEC_EXTRA_DEFINES (space-separated NAME=VALUE)
+    adds preprocessor definitions, e.g. SD_VECTOR_GEMV=1 for the vector-product build the
+    MFMA product is measured against."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
+    extra = [f"-D{d}" for d in os.environ.get("SPECDEC_EXTRA_DEFINES", "").split()]
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops' is not a recognized feature" not in l)

@@ -403,24 +403,17 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, float (*fin)[
   }
 }
 
-// After the product of a skinny GEMV (bf16 or 4-bit): the hi and lo columns of
-// each accumulator added in registers, the k-split waves' partials through
-// LDS in a fixed order, then the epilogue.  red holds NW = WG_ROWS * WK wave
-// slots; fin (LM head only) one slot per row group.
+// After the product of a skinny GEMV: red holds NW = WG_ROWS * WK wave slots
+// of 16 output rows x NT * 8 activation rows; fin (LM head only) one slot per
+// row group.
+// The waves' partials in LDS (written by the product, see below), the
+// reduction over the k-split waves in a fixed order and the epilogue.
 template <int NT, int WG_ROWS, int WK, Epi E>
-__device__ __forceinline__ void gemv_finish(const GemvParams& p, const f32x4_t (&acc)[NT], float (*red)[16][NT * 8 + 1],
-                                            float (*fin)[16][NT * 8 + 1], const float* rsc,
-                                            const EpiPre<NT * 8>& pre, int w, int lane, int rg, int ks, int g,
-                                            int sidx, int M, int n_groups) {
+__device__ __forceinline__ void gemv_reduce_epilogue(const GemvParams& p, float (*red)[16][NT * 8 + 1],
+                                                     float (*fin)[16][NT * 8 + 1], const float* rsc,
+                                                     const EpiPre<NT * 8>& pre, int w, int lane, int rg, int ks,
+                                                     int g, int sidx, int M, int n_groups) {
   constexpr int NC = NT * 8;
-  // hi + lo (columns 2c and 2c + 1) in registers, then the waves' partials in LDS
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = acc[t][r] + swap1(acc[t][r]);
-      if ((lane & 1) == 0) red[w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
-    }
   __syncthreads();
   if constexpr (E == Epi::SWIGLU) {
     // the epilogue wave sums the k-split partials of its own entries, in the
@@ -479,6 +472,23 @@ __device__ __forceinline__ void gemv_finish(const GemvParams& p, const f32x4_t (
   __syncthreads();
 
   gemv_epilogue<WG_ROWS, NC, E>(p, fin, rsc, pre, w, lane, rg, ks, g, sidx, M);
+}
+
+// gemv_reduce_epilogue after an MFMA product: the hi and lo columns of
+// each accumulator are added in registers and stored as the wave's partials.
+template <int NT, int WG_ROWS, int WK, Epi E>
+__device__ __forceinline__ void gemv_finish(const GemvParams& p, const f32x4_t (&acc)[NT], float (*red)[16][NT * 8 + 1],
+                                            float (*fin)[16][NT * 8 + 1], const float* rsc,
+                                            const EpiPre<NT * 8>& pre, int w, int lane, int rg, int ks, int g,
+                                            int sidx, int M, int n_groups) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[t][r] + swap1(acc[t][r]);
+      if ((lane & 1) == 0) red[w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
+    }
+  gemv_reduce_epilogue<NT, WG_ROWS, WK, E>(p, red, fin, rsc, pre, w, lane, rg, ks, g, sidx, M, n_groups);
 }
 
 }  // namespace sd

@@ -357,6 +357,93 @@ __device__ __forceinline__ void mfma_stream_shared(const bf16x8_t* __restrict__ 
   if (nmax <= 0) issued();
 }
 
+// ---------------------------------------------------------------------------
+// Vector alternative to the MFMA product, built with SD_VECTOR_GEMV=1 to
+// measure the MFMA choice against: each lane keeps the weight tile's eight
+// inputs of its row, takes each activation row's hi and lo values of those
+// inputs from the operand tile by a row broadcast (DPP), and accumulates with
+// the bf16 two-way dot product in fp32; the four input quarters of a row are
+// added at the end.  Its summation order differs from the MFMA's, so the two
+// agree within rounding, not bit for bit.
+// ---------------------------------------------------------------------------
+#ifndef SD_VECTOR_GEMV
+#define SD_VECTOR_GEMV 0
+#endif
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int C>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + C, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// activation rows Mi.. of one tile (operand columns 2m and 2m + 1) against
+// the lane's eight weights
+template <int Mi>
+__device__ __forceinline__ void vec_rows(const i32x4_t& a, const i32x4_t& b, float (&acc)[8], int mmax) {
+  if constexpr (Mi < 8) {
+    if (Mi < mmax) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t ad = (uint32_t)a[d], bd = (uint32_t)b[d];
+        acc[Mi] = dot2bf(ad, row_bcast<2 * Mi>(bd), acc[Mi]);
+        acc[Mi] = dot2bf(ad, row_bcast<2 * Mi + 1>(bd), acc[Mi]);
+      }
+      vec_rows<Mi + 1>(a, b, acc, mmax);
+    }
+  }
+}
+
+template <int NT, int R, typename Issued>
+__device__ __forceinline__ void vec_batch(const i32x4_t* a, const i32x4_t* const (&b)[NT], int i, float (&vacc)[NT][8],
+                                          int M, bool first, Issued& issued) {
+  i32x4_t av[R];
+  i32x4_t bv[R][NT];
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bv[u][t] = b[t][(size_t)(i + u) * 64];
+#pragma unroll
+  for (int u = 0; u < R; ++u) av[u] = __builtin_nontemporal_load(a + (size_t)(i + u) * 64);
+  if (first) {
+    __builtin_amdgcn_sched_barrier(0);
+    issued();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vec_rows<0>(av[u], bv[u][t], vacc[t], M - 8 * t);
+}
+
+template <int NT, int U, typename Issued>
+__device__ __forceinline__ void vec_tail(const i32x4_t* a, const i32x4_t* const (&b)[NT], int i, int r,
+                                         float (&vacc)[NT][8], int M, bool first, Issued& issued) {
+  if constexpr (U > 1) {
+    if (r == U - 1) vec_batch<NT, (U > 1 ? U - 1 : 1)>(a, b, i, vacc, M, first, issued);
+    else vec_tail<NT, (U > 1 ? U - 1 : 1)>(a, b, i, r, vacc, M, first, issued);
+  }
+}
+
+template <int NT, int U, typename Issued>
+__device__ __forceinline__ void vec_stream(const bf16x8_t* __restrict__ A, const bf16x8_t* __restrict__ B, int KB,
+                                           int kb0, int kb1, int lane, const int (&bslot)[NT], float (&vacc)[NT][8],
+                                           int M, Issued&& issued) {
+  const i32x4_t* a = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
+  const i32x4_t* b[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    b[t] = reinterpret_cast<const i32x4_t*>(B) + (size_t)(t * KB + kb0) * 64 + bslot[t];
+  const int n = kb1 - kb0;
+  if (n <= 0) {
+    issued();
+    return;
+  }
+  int i = 0;
+  for (; i + U <= n; i += U) vec_batch<NT, U>(a, b, i, vacc, M, i == 0, issued);
+  if (i < n) vec_tail<NT, U>(a, b, i, n - i, vacc, M, i == 0, issued);
+}
+
 // The fields the weight stream needs come first as plain arguments, which
 // the launch preloads into scalar registers; the rest of GemvParams is read
 // from the argument block where it is used.
@@ -377,7 +464,7 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   constexpr int RPW = (NC + NW - 1) / NW;   // norm rows per wave (NC covers every row)
   // row groups of a workgroup share their activation tiles through LDS when
   // the batch fits (the arithmetic is the same either way)
-  constexpr bool kShareB = WG_ROWS > 1 && U % WG_ROWS == 0 && WK * U * NT * 1024 <= 48 * 1024;
+  constexpr bool kShareB = !SD_VECTOR_GEMV && WG_ROWS > 1 && U % WG_ROWS == 0 && WK * U * NT * 1024 <= 48 * 1024;
   __shared__ i32x4_t bsh[kShareB ? WK : 1][kShareB ? U : 1][NT][64];
   __shared__ float red[NW][16][NC + 1];
   __shared__ float fin[E == Epi::LMHEAD ? WG_ROWS : 1][16][NC + 1];   // whole-workgroup epilogue only
@@ -441,6 +528,28 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
     const int col = lane & 15;
     bslot[t] = btile_slot((col >> 1) < M - 8 * t ? col : (col & 1), lane >> 4);
   }
+#if SD_VECTOR_GEMV
+  float vacc[NT][8];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) vacc[t][m] = 0.f;
+  if (g < n_groups) vec_stream<NT, U>(A + (size_t)g * KB * 64, B, KB, kb0, kb1, lane, bslot, vacc, M, prefetch);
+  else prefetch();
+  if constexpr (kNorm) norm_finish<RPW, NW>(p, w, lane, M, ssv, rsc);
+  // the four input quarters of each row, then the wave's partials
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      float v = vacc[t][m];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (lane < 16) red[w][lane][t * 8 + m] = v;
+    }
+  gemv_reduce_epilogue<NT, WG_ROWS, WK, E>(p, red, fin, rsc, pre, w, lane, rg, ks, g, sidx, M, n_groups);
+  return;
+#endif
   if constexpr (kShareB) {
     const int nmax = (int)((span + WK - 1) / WK);
     const int gg = g < n_groups ? g : 0;
