@@ -265,3 +265,33 @@ def test_tree_verify_and_accept_29_nodes(big):
             assert torch.equal(k1[:, dst], k0[:, src]) and torch.equal(v1[:, dst], v0[:, src])
     assert big["ws"].error_bits() == 0
     say(f"1.5B tree: path {path}, committed {com}, {exempt} rows with oracle margin < {MARGIN}")
+
+
+def test_q4_substitute_short_prompt(big):
+    """The 4-bit substitute of the 1.5B shape (down projection split over three
+    workgroups, five row groups a workgroup for gate/up) against the oracle with the
+    dequantised weights on a 48-token prompt: saved_next and a 6-row block, then the same
+    rows one at a time bit for bit."""
+    from block_verify_amd.synth import make_q4_draft
+    from oracle.model import OracleCache, forward, prefill
+    from gpu_helpers import q4_oracle_weights
+    b, S = big["b"], big["S"]
+    qt = make_q4_draft(S, big["w"])
+    qm = b.Model(S, qt, weight_format=b.W_Q4G64, share=big["model"])
+    ow = q4_oracle_weights(S, big["w"], qt, cache=False)
+    prompt = big["prompt"][:48]
+    cache, ws = b.Cache(S, 128), b.Workspace(S, 128)
+    saved = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(qm, cache, torch.from_numpy(prompt).cuda(), ws, logits=saved)
+    oc = OracleCache(S, 128)
+    o_saved = prefill(ow, oc, prompt)
+    assert_logits_close(to_np(saved), o_saved, "1.5B q4 prefill saved_next")
+    toks = np.random.default_rng(61).integers(0, S.vocab, 6).astype(np.int32)
+    lg = torch.empty((6, S.vocab), dtype=torch.float32, device="cuda")
+    b.decode_step(qm, cache, torch.from_numpy(toks).cuda(), ws, logits=lg)
+    assert_logits_close(to_np(lg), forward(ow, oc, toks), "1.5B q4 block rows=6")
+    cache.trim(48, ws)
+    ls = torch.empty_like(lg)
+    for i in range(6):
+        b.decode_step(qm, cache, torch.from_numpy(toks[i:i + 1]).cuda(), ws, logits=ls[i])
+    assert torch.equal(lg.view(torch.int32), ls.view(torch.int32)) and ws.error_bits() == 0
