@@ -1,6 +1,6 @@
 """Build libspecdec.so (gfx950) in-tree with hipcc.
 
-Usage: python -m block_verify_amd.build   (or __graft_entry__.build())
+Usage: python -m block_verify_amd.build
 """
 from __future__ import annotations
 
