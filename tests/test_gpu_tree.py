@@ -426,3 +426,43 @@ def test_tree_argument_checks(env):
     with pytest.raises(b.SpecdecError):
         b.tree_verify(env["model"], c, big[:513], big[:513], ws)
     assert c.length() == P
+
+
+def test_largest_tree_and_single_node(env):
+    """SPECDEC_MAX_TREE = 512 nodes (a chain of 200 nodes, then a fan of the rest under
+    node 150, so the ancestor masks use their last word) against the oracle's tree
+    forward and acceptance; then a tree of the root alone (no path, one committed token)."""
+    from oracle.tree import tree_accept_greedy, tree_forward
+    b, S = env["b"], env["S"]
+    n = b.MAX_TREE
+    pars = [-1] + list(range(199)) + [150] * (n - 200)
+    toks = [int(x) for x in np.random.default_rng(512).integers(0, S.vocab, n)]
+    c, ws = b.Cache(S, 1024), b.Workspace(S, 1024)
+    b.prefill(env["model"], c, torch.from_numpy(env["prompt"]).cuda(), ws)
+    t, p, lg, am = _tree(env, c, ws, toks, pars)
+    oc = _oracle_cache(env, 1024)
+    ol = tree_forward(env["ow"], oc, toks, pars)
+    assert_logits_close(to_np(lg), ol, "tiny 512-node tree verify")
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    b.tree_accept(c, t, p, am, out, cnt, err)
+    path, com = tree_accept_greedy(toks, pars, list(to_np(am)))
+    assert int(cnt.item()) == len(com) and c.length() == P + 1 + len(path) and ws.error_bits() == 0
+    # the root alone
+    c.trim(P, ws)
+    t1, p1, lg1, am1 = _tree(env, c, ws, [toks[0]], [-1])
+    b.tree_accept(c, t1, p1, am1, out[:1], cnt, err)
+    assert int(cnt.item()) == 1 and int(out[0].item()) == int(am1[0].item()) and c.length() == P + 1
+    assert int(err.item()) == 0
+
+
+def _oracle_cache(env, max_len):
+    from oracle.model import OracleCache
+    oc = OracleCache(env["S"], max_len)
+    src = env["oc"]
+    for l in range(env["S"].n_layers):
+        oc.k[l][:, :P] = src.k[l][:, :P]
+        oc.v[l][:, :P] = src.v[l][:, :P]
+    oc.length = P
+    return oc
