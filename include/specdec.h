@@ -14,7 +14,12 @@
  *    (accept with min(1, p/q), resample from norm(max(0, p-q)), bonus on full
  *    acceptance).
  *  - "SubSpec" summary (jjl357.github.io), sections 4.1.1-4.1.3 (4-bit group-64
- *    substitute draft sharing embedding, LM head and the KV cache).
+ *    substitute draft sharing embedding, LM head and the KV cache) and 4.2
+ *    (the context-aware draft tree, sharpened with temperature 0.2, verified
+ *    in one tree-causal target pass).
+ *  - "SpecDec-Context-Scaling 项目解读", section 7.2 (acceptance relaxed by a
+ *    logit gap), and the wmrh.cn explainer, sections 3.3, 4.2 and 8
+ *    (temperature, and top-k / top-p applied after the accept test).
  *
  * Conventions for every entry point:
  *  - Pointers prefixed d_ are device pointers (hipMalloc or a framework's
