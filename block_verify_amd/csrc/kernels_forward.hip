@@ -1031,14 +1031,17 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   // query tiles of 16 rows per kv head, spread over up to kAttnTileSplit
   // workgroups per chunk (each tile's arithmetic is the same either way)
   const int ntq = (a.rows * d.group() + 15) / 16;
-  // With a chunk workgroup per CU or more (a long cache), a chunk's query
-  // tiles stay in as few workgroups as their LDS allows, which then read the
-  // chunk's K and V once; with fewer chunks the tiles are spread over up to
-  // kAttnTileSplit workgroups for parallelism.
   const int ts_min = (ntq + kAttnMaxWgTiles - 1) / kAttnMaxWgTiles;
-  int ts = pl.max_chunks * d.nkv >= 256 ? ts_min : (ntq < kAttnTileSplit ? ntq : kAttnTileSplit);
+  int ts = ntq < kAttnTileSplit ? ntq : kAttnTileSplit;
   if (ts < ts_min) ts = ts_min;
-  dim3 ag(pl.max_chunks, d.nkv, ts);
+  // A chunk's tile workgroups sit gx * nkv apart in dispatch order; with that
+  // a multiple of eight, round-robin dispatch puts them on one XCD, whose L2
+  // then serves the chunk's K and V to every reader after the first.  The
+  // padding workgroups start past every cache and return at once.
+  int gx = pl.max_chunks;
+  if (ts > 1)
+    while ((gx * d.nkv) % 8) ++gx;
+  dim3 ag(gx, d.nkv, ts);
   const int wt = (ntq + ts - 1) / ts;   // query tiles per workgroup
   if (d.hd == 128) {
     launch_attn<128>(wt, ag, s, a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l), a.rows, a.c->max_len,
