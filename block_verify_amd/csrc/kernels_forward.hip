@@ -794,20 +794,22 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
   }
 }
 
-// Merge: one workgroup of four waves per (row, query head, 64 head dims);
-// lane l owns head dim 64 * blockIdx.y + l and wave w the chunks c = w, w + 4,
-// ...  The partial loads of the first batch of chunks and the first
-// statistics are issued before the cache length arrives (entries past the
-// row's chunk count are read but never used).  Thread t owns chunks t,
-// t + 256, ...: it stores their statistics in LDS, the row maximum is a
-// workgroup maximum (exact in any order), and it forms its chunks' weights
-// and their part of the normaliser (its chunks in increasing order, then a
-// fixed tree over the wave and the waves in order).  Each wave sums its
-// chunks' weighted partials in increasing order, then the four wave sums are
-// added in wave order and divided by the normaliser.  Every order depends
-// only on the row's own position.
+// Merge of the chunk partials of one (row, query head, 64 head dims); lane l
+// owns head dim 64 * blockIdx.y + l.  Chunk c's weight is exp(m_c - max),
+// with max the row maximum over the row's chunks (exact in any order).  The
+// output and its normaliser accumulate in four interleaved sums, s over the
+// chunks c = s, s + 4, ... in increasing order, added as (s0 + s1) +
+// (s2 + s3) and divided.  Every order depends only on the row's own
+// position, and the two launch forms below give the same bits.
+//
+// Four-wave form (caches of more than kMerge1Chunks chunks): wave w takes the
+// chunks c = w, w + 4, ...  The partial loads of the first batch of chunks
+// and the first statistics are issued before the cache length arrives
+// (entries past the row's chunk count are read but never used).  Thread t
+// owns chunks t, t + 256, ...: it stores their statistics in LDS, and forms
+// their weights once the workgroup maximum is known.
 constexpr int kMaxMergeChunks = 1024;
-constexpr int kMergeWaves = 4;
+constexpr int kMergeWaves = 4;   // the four residue classes
 
 template <int HD>
 __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
@@ -861,22 +863,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
   float mx = wred[0];
 #pragma unroll
   for (int v = 1; v < kMergeWaves; ++v) mx = fmaxf(mx, wred[v]);
-  // chunk weights, and the normaliser: each thread's chunks in increasing
-  // order, then a fixed tree over the wave and the waves in order
-  float lloc = 0.f;
-  for (int c = threadIdx.x; c < nch; c += NT) {
-    const float e = (sm[c] == -INFINITY) ? 0.f : __expf(sm[c] - mx);
-    sw[c] = e;
-    lloc = fmaf(e, sl[c], lloc);
-  }
-  lloc = warp_sum(lloc);
-  if (lane == 0) wl[w] = lloc;
+  // chunk weights
+  for (int c = threadIdx.x; c < nch; c += NT) sw[c] = (sm[c] == -INFINITY) ? 0.f : __expf(sm[c] - mx);
   __syncthreads();
-  float acc = 0.f;
+  // the wave's residue class: weighted partials and normaliser terms
+  float acc = 0.f, lac = 0.f;
 #pragma unroll
   for (int u = 0; u < BATCH; ++u) {
     const int c = w + kMergeWaves * u;
-    if (c < nch) acc = fmaf(sw[c], ov[u], acc);
+    if (c < nch) {
+      acc = fmaf(sw[c], ov[u], acc);
+      lac = fmaf(sw[c], sl[c], lac);
+    }
   }
   for (int c0 = kMergeWaves * BATCH; c0 < nch; c0 += kMergeWaves * BATCH) {
 #pragma unroll
@@ -887,20 +885,89 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int c = c0 + w + kMergeWaves * u;
-      if (c < nch) acc = fmaf(sw[c], ov[u], acc);
+      if (c < nch) {
+        acc = fmaf(sw[c], ov[u], acc);
+        lac = fmaf(sw[c], sl[c], lac);
+      }
     }
   }
   wsum[w][lane] = acc;
+  if (lane == 0) wl[w] = lac;
   __syncthreads();
   if (w == 0) {
-    float L = wl[0];
-#pragma unroll
-    for (int v = 1; v < kMergeWaves; ++v) L += wl[v];
-    float o = 0.f;
-#pragma unroll
-    for (int v = 0; v < kMergeWaves; ++v) o += wsum[v][lane];
+    const float o = (wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane]);
+    const float L = (wl[0] + wl[1]) + (wl[2] + wl[3]);
     btile_put(ob, (nq * HD) >> 5, m, hq * HD + d, o / L);
   }
+}
+
+// One-wave form (caches of at most kMerge1Chunks chunks): every partial of
+// a lane and every chunk's statistics are requested at once, before the
+// cache length arrives; lane c forms chunk c's weight and leaves it in LDS
+// for the other lanes, which keep the four residue-class sums side by side.
+// Without barriers or cross-wave sums it is the faster form for short
+// caches; one wave cannot keep the partials of a long cache in flight.
+constexpr int kMerge1Chunks = 48;
+static_assert(kMerge1Chunks % 4 == 0 && kMerge1Chunks <= 64, "one chunk per lane, whole residue classes");
+
+template <int HD>
+__global__ __launch_bounds__(64) void attn_merge1_kernel(const int32_t* gate, const int32_t* __restrict__ d_len,
+                                                         const float* __restrict__ o_part,
+                                                         const float* __restrict__ ml_part, int rows, int max_len,
+                                                         int nq, int nkv, int max_chunks, bf16_bits* __restrict__ ob) {
+  constexpr int B = kMerge1Chunks;
+  __shared__ float sw[B], sl[B];
+  const int gv = *(gate ? gate : d_len);   // requested with the length, before any branch
+  const int len = *d_len;
+  const int m = blockIdx.x / nq, hq = blockIdx.x % nq;
+  const int G = nq / nkv, h = hq / G, r = m * G + hq % G;
+  const size_t rstride = (size_t)kMaxRows * 8;
+  const size_t cst = rstride * HD, mst = rstride * 2;
+  const int lane = threadIdx.x;
+  const float* ml = ml_part + ((size_t)h * max_chunks * rstride + r) * 2;
+  const float* op = o_part + ((size_t)h * max_chunks * rstride + r) * HD + 64 * blockIdx.y + lane;
+  // indices clamped to the launch's chunks (max_chunks <= B); entries past
+  // the row's chunk count are read but never used
+  float ov[B];
+#pragma unroll
+  for (int u = 0; u < B; ++u) ov[u] = op[(size_t)(u < max_chunks ? u : max_chunks - 1) * cst];
+  const int c0 = lane < max_chunks ? lane : max_chunks - 1;
+  const float m0 = ml[(size_t)c0 * mst], l0 = ml[(size_t)c0 * mst + 1];
+  if (gate && gv == 0) return;
+  int pos = len + m;
+  if (pos >= max_len) pos = max_len - 1;
+  const int nch = pos / kAttnChunk + 1;   // <= max_chunks
+  const float mx = warp_max(lane < nch ? m0 : -INFINITY);
+  if (lane < nch) {
+    sw[lane] = (m0 == -INFINITY) ? 0.f : __expf(m0 - mx);
+    sl[lane] = l0;
+  }
+  __syncthreads();
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, lac[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < B; ++c) {
+    if (c < nch) {
+      const float wc = sw[c];
+      acc[c & 3] = fmaf(wc, ov[c], acc[c & 3]);
+      lac[c & 3] = fmaf(wc, sl[c], lac[c & 3]);
+    }
+  }
+  const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  const float L = (lac[0] + lac[1]) + (lac[2] + lac[3]);
+  btile_put(ob, (nq * HD) >> 5, m, hq * HD + 64 * blockIdx.y + lane, o / L);
+}
+
+// The merge form follows the cache capacity only (never the row count), and
+// both forms give the same bits.
+template <int HD>
+static void launch_merge(hipStream_t s, int row_heads, const int32_t* gate, const int32_t* d_len, const float* o_part,
+                         const float* ml_part, int rows, int max_len, int nq, int nkv, int max_chunks, bf16_bits* ob) {
+  const dim3 grid(row_heads, HD / 64);
+  if (max_chunks <= kMerge1Chunks)
+    attn_merge1_kernel<HD><<<grid, 64, 0, s>>>(gate, d_len, o_part, ml_part, rows, max_len, nq, nkv, max_chunks, ob);
+  else
+    attn_merge_kernel<HD><<<grid, 64 * kMergeWaves, 0, s>>>(gate, d_len, o_part, ml_part, rows, max_len, nq, nkv,
+                                                            max_chunks, ob);
 }
 
 // ---------------------------------------------------------------------------
@@ -1046,13 +1113,13 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   if (d.hd == 128) {
     launch_attn<128>(wt, ag, s, a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l), a.rows, a.c->max_len,
                      a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, tree_anc, a.tree_n0);
-    attn_merge_kernel<128><<<dim3(a.rows * d.nq, 2), 64 * kMergeWaves, 0, s>>>(
-        a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
+    launch_merge<128>(s, a.rows * d.nq, a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv,
+                      pl.max_chunks, ob);
   } else {
     launch_attn<64>(wt, ag, s, a.gate, a.c->d_len, qb, a.c->k_layer(l), a.c->v_layer(l), a.rows, a.c->max_len,
                     a.c->lp, d.group(), att_o, att_ml, pl.max_chunks, tree_anc, a.tree_n0);
-    attn_merge_kernel<64><<<dim3(a.rows * d.nq, 1), 64 * kMergeWaves, 0, s>>>(
-        a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv, pl.max_chunks, ob);
+    launch_merge<64>(s, a.rows * d.nq, a.gate, a.c->d_len, att_o, att_ml, a.rows, a.c->max_len, d.nq, d.nkv,
+                     pl.max_chunks, ob);
   }
 
   // O projection + residual; next input is the MLP norm
