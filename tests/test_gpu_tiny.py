@@ -104,8 +104,10 @@ def test_block_forward_rows(env, rows):
 @pytest.mark.parametrize("rows", [1, 5, 9])
 def test_long_cache_launch_shapes_give_the_same_logits(env, rows):
     """A long cache launches many more chunk workgroups (the grid padded so that
-    a chunk's query-tile workgroups share an XCD); the arithmetic of every
-    tile is unchanged, so the logits equal those of a short cache bit for bit."""
+    a chunk's query-tile workgroups share an XCD) and merges them in the
+    four-wave form instead of the one-wave form; the arithmetic of every tile
+    and the merge's summation order are unchanged, so the logits equal those
+    of a short cache bit for bit."""
     say(f"tiny long cache rows={rows}")
     toks = np.random.default_rng(100 + rows).integers(0, env["shape"].vocab, rows)
     out = []
