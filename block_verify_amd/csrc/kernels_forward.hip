@@ -564,6 +564,137 @@ __global__ __launch_bounds__(64 * WG_ROWS * WK) void gemv_kernel(const int32_t* 
   gemv_finish<NT, WG_ROWS, WK, E>(p, acc, red, fin, rsc, pre, w, lane, rg, ks, g, sidx, M, n_groups);
 }
 
+// Gate/up with several row groups per workgroup: wave w keeps the activation
+// tiles of its k-range in registers while the workgroup's row groups stream
+// past, and requests the next group's weight tiles before the current
+// group's products.  The k-split, the product order and the epilogue's sums
+// are those of gemv_kernel, so the results are the same bits.  KBW bounds
+// the k-blocks of a wave's range (shorter ranges re-read their last tile and
+// skip its product).
+template <int NT, int WK, int KBW, int RGMAX>
+__global__ __launch_bounds__(64 * WK) void gemv_rg_kernel(const int32_t* gate, const bf16x8_t* __restrict__ A,
+                                                          const bf16x8_t* __restrict__ B, int KB, int n_groups,
+                                                          int rows, int rg, GemvParams p) {
+  if (gate) {
+    if (*gate == 0) return;
+  }
+  constexpr int NC = NT * 8;
+  constexpr int RPW = (NC + WK - 1) / WK;   // norm rows per wave
+  __shared__ float red[RGMAX * WK][16][NC + 1];
+  __shared__ float rsc[kMaxRows];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = rows;
+  const int g0 = blockIdx.x * rg;
+  int nrg = n_groups - g0;
+  if (nrg > rg) nrg = rg;   // rg <= RGMAX (checked by the launch)
+  const unsigned uk = (unsigned)KB;
+  const int kb0 = (int)((unsigned)w * uk / WK), kb1 = (int)((unsigned)(w + 1) * uk / WK);
+  const int n = kb1 - kb0;   // 1 .. KBW (checked by the launch)
+  int bslot[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = lane & 15;
+    bslot[t] = btile_slot((col >> 1) < M - 8 * t ? col : (col & 1), lane >> 4);
+  }
+  // the wave's activation tiles, once
+  i32x4_t bv[KBW][NT];
+#pragma unroll
+  for (int j = 0; j < KBW; ++j) {
+    const int kb = kb0 + (j < n ? j : n - 1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      bv[j][t] = reinterpret_cast<const i32x4_t*>(B)[(size_t)(t * KB + kb) * 64 + bslot[t]];
+  }
+  const i32x4_t* a0 = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
+  i32x4_t av[2][KBW];
+  auto load_a = [&](int gg, i32x4_t(&dst)[KBW]) {
+    const i32x4_t* a = a0 + (size_t)gg * KB * 64;
+#pragma unroll
+    for (int j = 0; j < KBW; ++j) dst[j] = __builtin_nontemporal_load(a + (size_t)(j < n ? j : n - 1) * 64);
+  };
+  load_a(g0, av[0]);
+  float ssv[RPW][4];
+  __builtin_amdgcn_sched_barrier(0);
+  norm_prefetch<RPW, WK>(p, w, lane, M, ssv);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int rr = 0; rr < RGMAX; ++rr) {
+    if (rr >= nrg) break;
+    if (rr + 1 < nrg) load_a(g0 + rr + 1, av[(rr + 1) & 1]);
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KBW; ++j)
+      if (j < n)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[rr & 1][j]),
+                                                          __builtin_bit_cast(bf16x8_t, bv[j][t]), acc[t], 0, 0, 0);
+    // hi and lo columns added in registers: the wave's partials of this group
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[t][r] + swap1(acc[t][r]);
+        if ((lane & 1) == 0) red[rr * WK + w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
+      }
+  }
+  norm_finish<RPW, WK>(p, w, lane, M, ssv, rsc);
+  __syncthreads();
+  // SwiGLU epilogue: wave w takes row groups w, w + WK, ...; it sums the
+  // k-split partials of each entry in wave order
+  const int KBo = p.F >> 5;
+  for (int rr = w; rr < nrg; rr += WK) {
+    const int g = g0 + rr;
+    for (int idx = lane; idx < 8 * M; idx += 64) {
+      const int i = idx & 7, m = idx >> 3;
+      float gt = 0.f, up = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < WK; ++s2) {
+        gt += red[rr * WK + s2][i][m];
+        up += red[rr * WK + s2][i + 8][m];
+      }
+      const float r = rsc[m];
+      gt *= r;
+      up *= r;
+      btile_put(p.hb_out, KBo, m, 8 * g + i, gt / (1.0f + __expf(-gt)) * up);
+    }
+  }
+}
+
+// The row-group form of gate/up: about one workgroup per CU, each taking
+// rg = ceil(row groups / 256) of them, for passes of 3 to 8 rows (where the
+// activation tiles span two or more row pairs) and a k-split of at most 8
+// k-blocks a wave.  Returns false when it does not apply; both forms give
+// the same bits, so the choice never shows in the results.
+constexpr int kGuRgMinRows = 3;
+
+template <int NT>
+static bool launch_gu_rg(hipStream_t s, const GemvParams& p) {
+  constexpr int WK = CfgGU::WK;
+  constexpr int RGMAX = 8;
+  if constexpr (NT != 1) {
+    return false;
+  } else {
+    if (p.rows < kGuRgMinRows || p.KB < WK) return false;
+    const int kbw = (p.KB + WK - 1) / WK;
+    const int rg = (p.n_groups + 255) / 256;
+    if (rg > RGMAX || kbw > 8) return false;
+    const int grid = (p.n_groups + rg - 1) / rg;
+    if (kbw <= 2)
+      gemv_rg_kernel<NT, WK, 2, RGMAX><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    else if (kbw <= 4)
+      gemv_rg_kernel<NT, WK, 4, RGMAX><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    else if (kbw <= 6)
+      gemv_rg_kernel<NT, WK, 6, RGMAX><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    else
+      gemv_rg_kernel<NT, WK, 8, RGMAX><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    return true;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Causal grouped-query attention over the cache, split by 64-key chunks whose
 // boundaries are fixed by absolute key index, then a fixed-order merge of the
@@ -1141,7 +1272,7 @@ static void launch_gemvs_layer(const FwdArgs& a, int l, GemvParams base) {
   p.A = L.wgu; p.B = reinterpret_cast<const bf16x8_t*>(xb); p.KB = d.H / 32; p.n_groups = d.F / 8;
   p.ss_in = ss; p.hb_out = hb;
   if (q4) launch_q4_linear(Q4Linear::GATE_UP, p, L.q_wgu, L.s_wgu, d.H, s);
-  else
+  else if (!launch_gu_rg<NT>(s, p))
     launch_gemv<NT, CfgGU::WG_ROWS, CfgGU::WK, CfgGU::template U<NT>, Epi::SWIGLU>(
         (p.n_groups + CfgGU::WG_ROWS - 1) / CfgGU::WG_ROWS, s, p);
 
