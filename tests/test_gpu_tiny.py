@@ -585,3 +585,41 @@ def test_stochastic_zero_noise_accepts_every_draft(env):
     assert st.accepted_total == K * st.round
     assert st.n_committed == (K + 1) * st.round
     assert r.ws.error_bits() == 0
+
+
+@pytest.mark.parametrize("H,nq,hd,F", [(768, 12, 64, 4160), (1536, 12, 128, 2848), (2048, 16, 128, 4160)])
+def test_gate_up_forms_give_the_same_bits(H, nq, hd, F):
+    """Passes of 3 to 8 rows run gate/up over several row groups per workgroup
+    (activation tiles held in registers), passes of 1 or 2 rows one row group
+    per workgroup.  One-layer decoders whose k-split gives 3, 6 and 8 k-blocks
+    a wave and 2 or 3 row groups a workgroup (one with a short last
+    workgroup): a pass of M rows equals M single-row steps bit for bit, and
+    the pass matches the oracle."""
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import ModelShape
+    from block_verify_amd.synth import make_prompt, make_weights
+    from oracle.model import OracleCache, OracleWeights, forward, prefill
+    S = ModelShape(f"gu{H}", 1, H, nq, 2, hd, F, 2048)
+    say(f"gate/up forms H={H} F={F}")
+    w = make_weights(S, 7)
+    model = b.Model(S, w)
+    prompt = make_prompt(S.vocab, 40, seed=8)
+    pt = torch.from_numpy(prompt).cuda()
+    for M in (3, 8):
+        toks = np.random.default_rng(M).integers(0, S.vocab, M).astype(np.int32)
+        t = torch.from_numpy(toks).cuda()
+        c1, w1 = b.Cache(S, 128), b.Workspace(S, 128)
+        c2, w2 = b.Cache(S, 128), b.Workspace(S, 128)
+        b.prefill(model, c1, pt, w1)
+        b.prefill(model, c2, pt, w2)
+        lb = torch.empty((M, S.vocab), dtype=torch.float32, device="cuda")
+        b.decode_step(model, c1, t, w1, logits=lb)
+        ls = torch.empty((M, S.vocab), dtype=torch.float32, device="cuda")
+        for i in range(M):
+            b.decode_step(model, c2, t[i:i + 1], w2, logits=ls[i])
+        assert torch.equal(lb.view(torch.int32), ls.view(torch.int32)), f"M={M}"
+        assert w1.error_bits() == 0 and w2.error_bits() == 0
+    ow = OracleWeights(S, w)
+    oc = OracleCache(S, 128)
+    prefill(ow, oc, prompt)
+    assert_logits_close(to_np(lb), forward(ow, oc, toks), f"H={H} pass of 8 rows")
