@@ -928,19 +928,29 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_chunk_kernel(
 // Merge of the chunk partials of one (row, query head, 64 head dims); lane l
 // owns head dim 64 * blockIdx.y + l.  Chunk c's weight is exp(m_c - max),
 // with max the row maximum over the row's chunks (exact in any order).  The
-// output and its normaliser accumulate in four interleaved sums, s over the
-// chunks c = s, s + 4, ... in increasing order, added as (s0 + s1) +
-// (s2 + s3) and divided.  Every order depends only on the row's own
-// position, and the two launch forms below give the same bits.
+// output and its normaliser accumulate in eight interleaved sums, s over
+// the chunks c = s, s + 8, ... in increasing order, added as a pairwise tree
+// and divided.  Every order depends only on the row's own position, and the
+// two launch forms below give the same bits.
 //
-// Four-wave form (caches of more than kMerge1Chunks chunks): wave w takes the
-// chunks c = w, w + 4, ...  The partial loads of the first batch of chunks
-// and the first statistics are issued before the cache length arrives
-// (entries past the row's chunk count are read but never used).  Thread t
-// owns chunks t, t + 256, ...: it stores their statistics in LDS, and forms
-// their weights once the workgroup maximum is known.
+// Eight-wave form (caches of more than kMerge1Chunks chunks): wave w takes
+// the chunks c = w, w + 8, ...  The partial loads of the first batch of
+// chunks and the first statistics are issued before the cache length
+// arrives (entries past the row's chunk count are read but never used).
+// Thread t owns chunks t, t + 512, ...: it stores their statistics in LDS,
+// and forms their weights once the workgroup maximum is known.
 constexpr int kMaxMergeChunks = 1024;
-constexpr int kMergeWaves = 4;   // the four residue classes
+constexpr int kMergeWaves = 8;   // residue classes of chunks, one wave each in the multi-wave form
+
+// Pairwise sum of N values: ((v0 + v1) + (v2 + v3)) + ((v4 + v5) + (v6 + v7))
+// for N = 8.
+template <int N>
+__device__ __forceinline__ float pair_tree(const float* v) {
+  if constexpr (N == 1)
+    return v[0];
+  else
+    return pair_tree<N / 2>(v) + pair_tree<N / 2>(v + N / 2);
+}
 
 template <int HD>
 __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
@@ -1026,8 +1036,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
   if (lane == 0) wl[w] = lac;
   __syncthreads();
   if (w == 0) {
-    const float o = (wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane]);
-    const float L = (wl[0] + wl[1]) + (wl[2] + wl[3]);
+    float ov4[kMergeWaves], lv4[kMergeWaves];
+#pragma unroll
+    for (int v = 0; v < kMergeWaves; ++v) {
+      ov4[v] = wsum[v][lane];
+      lv4[v] = wl[v];
+    }
+    const float o = pair_tree<kMergeWaves>(ov4);
+    const float L = pair_tree<kMergeWaves>(lv4);
     btile_put(ob, (nq * HD) >> 5, m, hq * HD + d, o / L);
   }
 }
@@ -1035,11 +1051,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
 // One-wave form (caches of at most kMerge1Chunks chunks): every partial of
 // a lane and every chunk's statistics are requested at once, before the
 // cache length arrives; lane c forms chunk c's weight and leaves it in LDS
-// for the other lanes, which keep the four residue-class sums side by side.
+// for the other lanes, which keep the eight residue-class sums side by side.
 // Without barriers or cross-wave sums it is the faster form for short
 // caches; one wave cannot keep the partials of a long cache in flight.
 constexpr int kMerge1Chunks = 48;
-static_assert(kMerge1Chunks % 4 == 0 && kMerge1Chunks <= 64, "one chunk per lane, whole residue classes");
+static_assert(kMerge1Chunks % kMergeWaves == 0 && kMerge1Chunks <= 64, "one chunk per lane, whole residue classes");
 
 template <int HD>
 __global__ __launch_bounds__(64) void attn_merge1_kernel(const int32_t* gate, const int32_t* __restrict__ d_len,
@@ -1074,17 +1090,20 @@ __global__ __launch_bounds__(64) void attn_merge1_kernel(const int32_t* gate, co
     sl[lane] = l0;
   }
   __syncthreads();
-  float acc[4] = {0.f, 0.f, 0.f, 0.f}, lac[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NR = kMergeWaves;
+  float acc[NR], lac[NR];
+#pragma unroll
+  for (int v = 0; v < NR; ++v) acc[v] = lac[v] = 0.f;
 #pragma unroll
   for (int c = 0; c < B; ++c) {
     if (c < nch) {
       const float wc = sw[c];
-      acc[c & 3] = fmaf(wc, ov[c], acc[c & 3]);
-      lac[c & 3] = fmaf(wc, sl[c], lac[c & 3]);
+      acc[c % NR] = fmaf(wc, ov[c], acc[c % NR]);
+      lac[c % NR] = fmaf(wc, sl[c], lac[c % NR]);
     }
   }
-  const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  const float L = (lac[0] + lac[1]) + (lac[2] + lac[3]);
+  const float o = pair_tree<NR>(acc);
+  const float L = pair_tree<NR>(lac);
   btile_put(ob, (nq * HD) >> 5, m, hq * HD + 64 * blockIdx.y + lane, o / L);
 }
 
