@@ -664,25 +664,124 @@ __global__ __launch_bounds__(64 * WK) void gemv_rg_kernel(const int32_t* gate, c
   }
 }
 
-// The row-group form of gate/up: about one workgroup per CU, each taking
-// rg = ceil(row groups / 256) of them, for passes of 3 to 8 rows (where the
-// activation tiles span two or more row pairs) and a k-split of at most 8
-// k-blocks a wave.  Returns false when it does not apply; both forms give
-// the same bits, so the choice never shows in the results.
+// The same for passes of two or more column tiles, whose partials of every
+// row group would not fit LDS at once: the waves' partials of a row group go
+// to one of two LDS slots, one barrier per row group, and wave rr % WK runs
+// row group rr's epilogue while the others stream the next group (the next
+// barrier keeps a slot from being rewritten before its epilogue has read
+// it).  Same k-split, product order and sums as gemv_kernel.
+template <int NT, int WK, int KBW>
+__global__ __launch_bounds__(64 * WK) void gemv_rg2_kernel(const int32_t* gate, const bf16x8_t* __restrict__ A,
+                                                           const bf16x8_t* __restrict__ B, int KB, int n_groups,
+                                                           int rows, int rg, GemvParams p) {
+  if (gate) {
+    if (*gate == 0) return;
+  }
+  constexpr int NC = NT * 8;
+  constexpr int RPW = (NC + WK - 1) / WK;   // norm rows per wave
+  __shared__ float red[2][WK][16][NC + 1];
+  __shared__ float rsc[kMaxRows];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = rows;
+  const int g0 = blockIdx.x * rg;
+  int nrg = n_groups - g0;
+  if (nrg > rg) nrg = rg;
+  const unsigned uk = (unsigned)KB;
+  const int kb0 = (int)((unsigned)w * uk / WK), kb1 = (int)((unsigned)(w + 1) * uk / WK);
+  const int n = kb1 - kb0;   // 1 .. KBW (checked by the launch)
+  int bslot[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = lane & 15;
+    bslot[t] = btile_slot((col >> 1) < M - 8 * t ? col : (col & 1), lane >> 4);
+  }
+  i32x4_t bv[KBW][NT];
+#pragma unroll
+  for (int j = 0; j < KBW; ++j) {
+    const int kb = kb0 + (j < n ? j : n - 1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      bv[j][t] = reinterpret_cast<const i32x4_t*>(B)[(size_t)(t * KB + kb) * 64 + bslot[t]];
+  }
+  const i32x4_t* a0 = reinterpret_cast<const i32x4_t*>(A) + (size_t)kb0 * 64 + lane;
+  auto load_a = [&](int gg, i32x4_t(&dst)[KBW]) {
+    const i32x4_t* a = a0 + (size_t)gg * KB * 64;
+#pragma unroll
+    for (int j = 0; j < KBW; ++j) dst[j] = __builtin_nontemporal_load(a + (size_t)(j < n ? j : n - 1) * 64);
+  };
+  i32x4_t av0[KBW], av1[KBW];
+  load_a(g0, av0);
+  float ssv[RPW][4];
+  __builtin_amdgcn_sched_barrier(0);
+  norm_prefetch<RPW, WK>(p, w, lane, M, ssv);
+  __builtin_amdgcn_sched_barrier(0);
+  const int KBo = p.F >> 5;
+  auto step = [&](int rr, i32x4_t(&cur)[KBW], i32x4_t(&nxt)[KBW]) {
+    if (rr + 1 < nrg) load_a(g0 + rr + 1, nxt);
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KBW; ++j)
+      if (j < n)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur[j]),
+                                                          __builtin_bit_cast(bf16x8_t, bv[j][t]), acc[t], 0, 0, 0);
+    float(*slot)[16][NC + 1] = red[rr & 1];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[t][r] + swap1(acc[t][r]);
+        if ((lane & 1) == 0) slot[w][4 * (lane >> 4) + r][t * 8 + ((lane & 15) >> 1)] = v;
+      }
+    if (rr == 0) norm_finish<RPW, WK>(p, w, lane, M, ssv, rsc);
+    __syncthreads();
+    if (w == rr % WK) {
+      const int g = g0 + rr;
+      for (int idx = lane; idx < 8 * M; idx += 64) {
+        const int i = idx & 7, m = idx >> 3;
+        float gt = 0.f, up = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < WK; ++s2) {
+          gt += slot[s2][i][m];
+          up += slot[s2][i + 8][m];
+        }
+        const float r = rsc[m];
+        gt *= r;
+        up *= r;
+        btile_put(p.hb_out, KBo, m, 8 * g + i, gt / (1.0f + __expf(-gt)) * up);
+      }
+    }
+  };
+  for (int rr = 0; rr < nrg; rr += 2) {
+    step(rr, av0, av1);
+    if (rr + 1 < nrg) step(rr + 1, av1, av0);
+  }
+}
+
+// The row-group forms of gate/up: about one workgroup per CU, each taking
+// rg = ceil(row groups / 256) of them, for a k-split of at most 8 k-blocks a
+// wave; gemv_rg_kernel for passes of 3 to 8 rows, gemv_rg2_kernel for 17 to
+// 32 (where the activation tiles outweigh the weights).  Passes of 1, 2 and
+// 9 to 16 rows keep one row group per workgroup (faster there).  Returns
+// false when no row-group form applies; every form gives the same bits, so
+// the choice never shows in the results.
 constexpr int kGuRgMinRows = 3;
 
 template <int NT>
 static bool launch_gu_rg(hipStream_t s, const GemvParams& p) {
   constexpr int WK = CfgGU::WK;
   constexpr int RGMAX = 8;
-  if constexpr (NT != 1) {
-    return false;
-  } else {
-    if (p.rows < kGuRgMinRows || p.KB < WK) return false;
-    const int kbw = (p.KB + WK - 1) / WK;
-    const int rg = (p.n_groups + 255) / 256;
-    if (rg > RGMAX || kbw > 8) return false;
-    const int grid = (p.n_groups + rg - 1) / rg;
+  if (p.rows < kGuRgMinRows || p.KB < WK) return false;
+  const int kbw = (p.KB + WK - 1) / WK;
+  const int rg = (p.n_groups + 255) / 256;
+  if (kbw > 8) return false;
+  const int grid = (p.n_groups + rg - 1) / rg;
+  if constexpr (NT == 1) {
+    if (rg > RGMAX) return false;
     if (kbw <= 2)
       gemv_rg_kernel<NT, WK, 2, RGMAX><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
     else if (kbw <= 4)
@@ -692,6 +791,18 @@ static bool launch_gu_rg(hipStream_t s, const GemvParams& p) {
     else
       gemv_rg_kernel<NT, WK, 8, RGMAX><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
     return true;
+  } else if constexpr (NT >= 3) {
+    if (kbw <= 2)
+      gemv_rg2_kernel<NT, WK, 2><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    else if (kbw <= 4)
+      gemv_rg2_kernel<NT, WK, 4><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    else if (kbw <= 6)
+      gemv_rg2_kernel<NT, WK, 6><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    else
+      gemv_rg2_kernel<NT, WK, 8><<<grid, 64 * WK, 0, s>>>(p.gate, p.A, p.B, p.KB, p.n_groups, p.rows, rg, p);
+    return true;
+  } else {
+    return false;
   }
 }
 

@@ -589,12 +589,14 @@ def test_stochastic_zero_noise_accepts_every_draft(env):
 
 @pytest.mark.parametrize("H,nq,hd,F", [(768, 12, 64, 4160), (1536, 12, 128, 2848), (2048, 16, 128, 4160)])
 def test_gate_up_forms_give_the_same_bits(H, nq, hd, F):
-    """Passes of 3 to 8 rows run gate/up over several row groups per workgroup
-    (activation tiles held in registers), passes of 1 or 2 rows one row group
-    per workgroup.  One-layer decoders whose k-split gives 3, 6 and 8 k-blocks
-    a wave and 2 or 3 row groups a workgroup (one with a short last
-    workgroup): a pass of M rows equals M single-row steps bit for bit, and
-    the pass matches the oracle."""
+    """Passes of 3 to 8 and of 17 to 32 rows run gate/up over several row
+    groups per workgroup (activation tiles held in registers; one LDS slot per
+    group for one column tile, two slots in turn for three or four), the
+    other passes one row group per workgroup.  One-layer decoders whose
+    k-split gives 3, 6 and 8 k-blocks a wave and 2 or 3 row groups a
+    workgroup (one with a short last workgroup): a pass of 3, 8, 12 or 29 rows
+    equals the same rows in single-row steps bit for bit, and the 29-row pass
+    matches the oracle."""
     from block_verify_amd import lib as b
     from block_verify_amd.shapes import ModelShape
     from block_verify_amd.synth import make_prompt, make_weights
@@ -605,7 +607,7 @@ def test_gate_up_forms_give_the_same_bits(H, nq, hd, F):
     model = b.Model(S, w)
     prompt = make_prompt(S.vocab, 40, seed=8)
     pt = torch.from_numpy(prompt).cuda()
-    for M in (3, 8):
+    for M in (3, 8, 12, 29):
         toks = np.random.default_rng(M).integers(0, S.vocab, M).astype(np.int32)
         t = torch.from_numpy(toks).cuda()
         c1, w1 = b.Cache(S, 128), b.Workspace(S, 128)
@@ -622,4 +624,4 @@ def test_gate_up_forms_give_the_same_bits(H, nq, hd, F):
     ow = OracleWeights(S, w)
     oc = OracleCache(S, 128)
     prefill(ow, oc, prompt)
-    assert_logits_close(to_np(lb), forward(ow, oc, toks), f"H={H} pass of 8 rows")
+    assert_logits_close(to_np(lb), forward(ow, oc, toks), f"H={H} pass of 29 rows")
