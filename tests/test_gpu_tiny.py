@@ -111,14 +111,17 @@ def test_long_cache_launch_shapes_give_the_same_logits(env, rows):
     say(f"tiny long cache rows={rows}")
     toks = np.random.default_rng(100 + rows).integers(0, env["shape"].vocab, rows)
     out = []
-    for max_len in (512, 8448):
+    # 8 chunks, the last capacity of the one-wave merge (48 chunks), the first
+    # of the eight-wave one (49), and a long cache
+    for max_len in (512, 3072, 3136, 8448):
         cache, ws = _fresh(env, max_len)
         _gpu_prefill(env, cache, ws, env["prompt"])
         logits, am, lse = _gpu_forward(env, cache, ws, toks)
         assert cache.length() == P + rows and ws.error_bits() == 0
         out.append((logits, am, lse))
-    assert np.array_equal(out[0][0], out[1][0])
-    assert np.array_equal(out[0][1], out[1][1]) and np.array_equal(out[0][2], out[1][2])
+    for o in out[1:]:
+        assert np.array_equal(out[0][0], o[0])
+        assert np.array_equal(out[0][1], o[1]) and np.array_equal(out[0][2], o[2])
 
 
 def test_batch_invariance_block_equals_single_steps(env):
