@@ -628,3 +628,24 @@ def test_gate_up_forms_give_the_same_bits(H, nq, hd, F):
     oc = OracleCache(S, 128)
     prefill(ow, oc, prompt)
     assert_logits_close(to_np(lb), forward(ow, oc, toks), f"H={H} pass of 29 rows")
+
+
+def test_single_chunk_cache_gives_the_same_logits(env):
+    """A cache of one attention chunk (capacity 48: one chunk workgroup per
+    head and tile, a merge over one partial) gives the same logits, argmax and
+    lse as a long cache, bit for bit, and the oracle's values."""
+    from oracle.model import OracleCache, forward, prefill
+    prompt = env["prompt"][:40]
+    toks = np.random.default_rng(77).integers(0, env["shape"].vocab, 5)
+    out = []
+    for max_len in (48, 8448):
+        cache, ws = _fresh(env, max_len)
+        _gpu_prefill(env, cache, ws, prompt, chunk=13)
+        logits, am, lse = _gpu_forward(env, cache, ws, toks)
+        assert cache.length() == 45 and ws.error_bits() == 0
+        out.append((logits, am, lse))
+    for a, b_ in zip(out[0], out[1]):
+        assert np.array_equal(a, b_)
+    oc = OracleCache(env["shape"], 48)
+    prefill(env["ow"], oc, prompt)
+    assert_logits_close(out[0][0], forward(env["ow"], oc, toks), "one-chunk cache")
