@@ -598,8 +598,9 @@ def test_gate_up_forms_give_the_same_bits(H, nq, hd, F):
     other passes one row group per workgroup.  One-layer decoders whose
     k-split gives 3, 6 and 8 k-blocks a wave and 2 or 3 row groups a
     workgroup (one with a short last workgroup): a pass of 3, 8, 12 or 29 rows
-    equals the same rows in single-row steps bit for bit, and the 29-row pass
-    matches the oracle."""
+    equals the same rows in single-row steps bit for bit, the 29-row pass on a
+    long cache (head dims 64 and 128 through both merge forms) too, and the
+    29-row pass matches the oracle."""
     from block_verify_amd import lib as b
     from block_verify_amd.shapes import ModelShape
     from block_verify_amd.synth import make_prompt, make_weights
@@ -624,6 +625,12 @@ def test_gate_up_forms_give_the_same_bits(H, nq, hd, F):
             b.decode_step(model, c2, t[i:i + 1], w2, logits=ls[i])
         assert torch.equal(lb.view(torch.int32), ls.view(torch.int32)), f"M={M}"
         assert w1.error_bits() == 0 and w2.error_bits() == 0
+    # a long cache (more chunk workgroups, the eight-wave merge) gives the same bits
+    c3, w3 = b.Cache(S, 8448), b.Workspace(S, 8448)
+    b.prefill(model, c3, pt, w3)
+    ll = torch.empty((M, S.vocab), dtype=torch.float32, device="cuda")
+    b.decode_step(model, c3, t, w3, logits=ll)
+    assert torch.equal(lb.view(torch.int32), ll.view(torch.int32)) and w3.error_bits() == 0
     ow = OracleWeights(S, w)
     oc = OracleCache(S, 128)
     prefill(ow, oc, prompt)
