@@ -775,7 +775,8 @@ template <int NT>
 static bool launch_gu_rg(hipStream_t s, const GemvParams& p) {
   constexpr int WK = CfgGU::WK;
   constexpr int RGMAX = 8;
-  if (p.rows < kGuRgMinRows || p.KB < WK) return false;
+  // the vector comparison build keeps every product on gemv_kernel
+  if (SD_VECTOR_GEMV || p.rows < kGuRgMinRows || p.KB < WK) return false;
   const int kbw = (p.KB + WK - 1) / WK;
   const int rg = (p.n_groups + 255) / 256;
   if (kbw > 8) return false;
