@@ -1,0 +1,90 @@
+"""GPU parity on seeded random decoder shapes (one or two layers).
+
+Every launch path of the forward depends on the shape: the k-split of each
+product, the row-group forms of gate/up, the attention's query tiles per
+workgroup, the grid padding and the merge form (by cache capacity).  Each case
+draws a shape within the library's documented limits (head dim 64 or 128, up
+to 8 query heads per kv head, hidden up to 4096, multiples of 32), a prompt
+length, a pass of 1..32 rows and a cache capacity, then checks
+
+- the pass against the oracle forward (logit tolerance of the parity bar);
+- the pass against the same rows in single-row steps, bit for bit (batch
+  invariance across every launch form);
+
+and the 4-bit cases the same against the oracle with the dequantised weights.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_logits_close, q4_oracle_weights, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, q4=False):
+    rng = np.random.default_rng(seed)
+    while True:
+        hd = int(rng.choice([64, 128]))
+        nkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 6, 7, 8]))
+        H = int(rng.choice([256, 512, 768, 896, 1024, 1536, 2048]))
+        F = 32 * int(rng.integers(8, 160))
+        V = 16 * int(rng.integers(64, 512))
+        L = int(rng.choice([1, 2]))
+        qd = nkv * G * hd
+        ok = qd % 32 == 0 and qd <= 4096
+        if q4:
+            ok = ok and H % 64 == 0 and F % 64 == 0 and qd % 64 == 0
+        if ok:
+            break
+    P = int(rng.integers(1, 300))
+    M = int(rng.integers(1, 33))
+    cap = max(int(rng.choice([P + M, P + M + 7, 512, 3072, 3136, 4200])), P + M)
+    chunk = int(rng.integers(1, 33))
+    return dict(L=L, H=H, F=F, V=V, nq=nkv * G, nkv=nkv, hd=hd, P=P, M=M, cap=cap, chunk=chunk, seed=seed)
+
+
+def _run(c, q4):
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import ModelShape
+    from block_verify_amd.synth import make_prompt, make_q4_draft, make_weights
+    from oracle.model import OracleCache, OracleWeights, forward, prefill
+    S = ModelShape(f"rand{c['seed']}", c["L"], c["H"], c["nq"], c["nkv"], c["hd"], c["F"], c["V"])
+    say(f"random shape {c} q4={q4}")
+    w = make_weights(S, 1000 + c["seed"])
+    model = b.Model(S, w)
+    ow = OracleWeights(S, w)
+    if q4:
+        qt = make_q4_draft(S, w)
+        model = b.Model(S, qt, weight_format=b.W_Q4G64, share=model)
+        ow = q4_oracle_weights(S, w, qt)
+    prompt = make_prompt(S.vocab, c["P"], seed=2000 + c["seed"])
+    toks = np.random.default_rng(3000 + c["seed"]).integers(0, S.vocab, c["M"]).astype(np.int32)
+    pt, t = torch.from_numpy(prompt).cuda(), torch.from_numpy(toks).cuda()
+    M, cap = c["M"], c["cap"]
+    c1, w1 = b.Cache(S, cap), b.Workspace(S, cap)
+    b.prefill(model, c1, pt, w1, chunk=c["chunk"])
+    lb = torch.empty((M, S.vocab), dtype=torch.float32, device="cuda")
+    b.decode_step(model, c1, t, w1, logits=lb)
+    assert w1.error_bits() == 0 and c1.length() == c["P"] + M
+    c2, w2 = b.Cache(S, cap), b.Workspace(S, cap)
+    b.prefill(model, c2, pt, w2)
+    ls = torch.empty((M, S.vocab), dtype=torch.float32, device="cuda")
+    for i in range(M):
+        b.decode_step(model, c2, t[i:i + 1], w2, logits=ls[i])
+    assert w2.error_bits() == 0
+    assert torch.equal(lb.view(torch.int32), ls.view(torch.int32)), "a pass differs from single-row steps"
+    oc = OracleCache(S, cap)
+    prefill(ow, oc, prompt)
+    assert_logits_close(to_np(lb), forward(ow, oc, toks), f"random shape {c}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape_bf16(seed):
+    _run(_case(seed), q4=False)
+
+
+@pytest.mark.parametrize("seed", range(100, 108))
+def test_random_shape_q4(seed):
+    _run(_case(seed, q4=True), q4=True)
