@@ -12,6 +12,8 @@ length, a pass of 1..32 rows and a cache capacity, then checks
   invariance across every launch form);
 
 and the 4-bit cases the same against the oracle with the dequantised weights.
+Greedy rounds on random shapes (k up to 16, so verify passes of up to 17
+rows) must commit the GPU's own greedy AR decode token for token.
 """
 import numpy as np
 import pytest
@@ -88,3 +90,42 @@ def test_random_shape_bf16(seed):
 @pytest.mark.parametrize("seed", range(100, 108))
 def test_random_shape_q4(seed):
     _run(_case(seed, q4=True), q4=True)
+
+
+@pytest.mark.parametrize("seed", range(200, 208))
+def test_random_shape_rounds_commit_gpu_ar(seed):
+    """Greedy rounds on a random shape (draft table corrupted with a random
+    rate, k in 1..16, schedule A or B, a random capacity margin): the committed
+    tokens equal the GPU's greedy AR decode token for token, and the cache
+    length equals prompt + committed after the job."""
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import ModelShape
+    from block_verify_amd.synth import make_draft_table, make_prompt, make_weights
+    c = _case(seed)
+    rng = np.random.default_rng(5000 + seed)
+    k = int(rng.integers(1, 17))
+    schedule = int(rng.integers(0, 2))
+    corrupt = float(rng.choice([0.0, 0.3, 0.6, 1.0]))
+    n_new = int(rng.integers(8, 41))
+    S = ModelShape(f"rr{seed}", c["L"], c["H"], c["nq"], c["nkv"], c["hd"], c["F"], c["V"])
+    say(f"random rounds {c} k={k} schedule={'AB'[schedule]} c={corrupt} n={n_new}")
+    w = make_weights(S, 4000 + seed)
+    model = b.Model(S, w)
+    prompt = make_prompt(S.vocab, c["P"], seed=6000 + seed)
+    max_len = c["P"] + n_new + 2 * (k + 2) + int(rng.integers(0, 200))
+    # greedy AR on the GPU, one step at a time
+    cache, ws = b.Cache(S, max_len), b.Workspace(S, max_len)
+    n_ar = n_new + k + 1
+    toks = torch.zeros(n_ar + 1, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(S.vocab, dtype=torch.float32, device="cuda")
+    b.prefill(model, cache, torch.from_numpy(prompt).cuda(), ws, logits=scratch, argmax=toks[0:1])
+    for i in range(n_ar - 1):
+        b.decode_step(model, cache, toks[i:i + 1], ws, logits=scratch, argmax=toks[i + 1:i + 2])
+    ar = [int(x) for x in to_np(toks)[:n_ar]]
+    table = make_draft_table(np.array(ar), S.vocab, corrupt, seed=7000 + seed)
+    r = b.Round(model, k, schedule=schedule, table=table, max_len=max_len)
+    r.prefill(prompt)
+    st, got = r.run(n_new)
+    assert list(got[:n_new]) == ar[:n_new]
+    assert r.tcache.length() == c["P"] + st.n_committed - (1 if schedule == 1 else 0)
+    assert r.ws.error_bits() == 0
