@@ -129,3 +129,55 @@ def test_random_shape_rounds_commit_gpu_ar(seed):
     assert list(got[:n_new]) == ar[:n_new]
     assert r.tcache.length() == c["P"] + st.n_committed - (1 if schedule == 1 else 0)
     assert r.ws.error_bits() == 0
+
+
+@pytest.mark.parametrize("seed", range(300, 306))
+def test_random_shape_stochastic_rounds_match_oracle_rule(seed):
+    """Modified rejection sampling on a random shape and vocabulary (noisy
+    self-draft, k in 1..8, schedule A, a random temperature, top-k / top-p and
+    bonus setting): every round's draft samples and accept / resample / bonus
+    decisions, replayed by the oracle on the GPU's own logits, agree (up to
+    counted boundary cases), and the cache length equals prompt + committed."""
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import ModelShape
+    from block_verify_amd.synth import make_noise, make_prompt, make_weights
+    from gpu_helpers import check_stochastic_round
+    c = _case(seed)
+    rng = np.random.default_rng(8000 + seed)
+    k = int(rng.integers(1, 9))
+    kw = dict(temperature=float(rng.choice([1.0, 0.7, 1.3])), bonus=bool(rng.integers(0, 2)))
+    if rng.integers(0, 2):
+        kw["top_k"] = int(rng.choice([1, 5, 50]))
+    if rng.integers(0, 2):
+        kw["top_p"] = float(rng.choice([0.5, 0.9]))
+    n_new = int(rng.integers(8, 25))
+    S = ModelShape(f"rs{seed}", 1, c["H"], c["nq"], c["nkv"], c["hd"], c["F"], c["V"])
+    say(f"random stochastic {c} k={k} {kw} n={n_new}")
+    w = make_weights(S, 9000 + seed)
+    model = b.Model(S, w)
+    prompt = make_prompt(S.vocab, c["P"], seed=9500 + seed)
+    max_len = c["P"] + n_new + 2 * (k + 2) + 64
+    noise = float(rng.choice([1.0, 0.2])) * make_noise(n_new + 2 * k + 2, S.vocab, seed=9700 + seed)
+    r = b.Round(model, k, mode=b.STOCHASTIC, draft_source=b.DRAFT_NOISY_SELF, noise=noise, seed=seed,
+                max_len=max_len, **kw)
+    r.prefill(prompt)
+    r.reset(n_new)
+    V = S.vocab
+    exempt, n0, rounds = 0, 0, 0
+    while n0 < n_new:
+        saved = to_np(r.debug_view(0)).copy()
+        st0, _ = r.read_state()
+        r.step()
+        st, toks = r.read_state()
+        rows = to_np(r.debug_view(1)).reshape(k + 1, V)[:k].copy()
+        qz = to_np(r.debug_view(2)).reshape(k, V).copy()
+        drafts = [int(x) for x in to_np(r.debug_view(3, torch.int32))[:k]]
+        com = [int(x) for x in toks[n0:st.n_committed]]
+        exempt += check_stochastic_round(saved, rows, qz, drafts, st.m_last, com, seed, st0.round, kw["bonus"],
+                                         kw["temperature"], kw.get("top_k", 0), kw.get("top_p", 1.0))
+        assert r.tcache.length() == c["P"] + st.n_committed
+        n0 = st.n_committed
+        rounds += 1
+    assert r.ws.error_bits() == 0
+    say(f"  {rounds} rounds, {exempt} boundary exemptions")
+    assert exempt <= 1
