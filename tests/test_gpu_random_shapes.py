@@ -181,3 +181,40 @@ def test_random_shape_stochastic_rounds_match_oracle_rule(seed):
     assert r.ws.error_bits() == 0
     say(f"  {rounds} rounds, {exempt} boundary exemptions")
     assert exempt <= 1
+
+
+@pytest.mark.parametrize("seed", range(400, 406))
+def test_random_shape_trees_match_oracle(seed):
+    """A random draft tree (1..64 nodes, each parent an earlier node) on a random
+    shape and cache capacity: the tree verify's logits against the oracle's
+    tree forward, its argmax against its logits, and the cache length after
+    the tree; passes of up to 32 rows with the ancestor mask."""
+    from block_verify_amd import lib as b
+    from block_verify_amd.shapes import ModelShape
+    from block_verify_amd.synth import make_prompt, make_weights
+    from oracle.model import OracleCache, OracleWeights, prefill
+    from oracle.tree import tree_forward
+    c = _case(seed)
+    rng = np.random.default_rng(10000 + seed)
+    n = int(rng.integers(1, 65))
+    pars = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
+    S = ModelShape(f"rt{seed}", c["L"], c["H"], c["nq"], c["nkv"], c["hd"], c["F"], c["V"])
+    toks = rng.integers(0, S.vocab, n).astype(np.int32)
+    say(f"random tree {c} n={n}")
+    w = make_weights(S, 11000 + seed)
+    model = b.Model(S, w)
+    prompt = make_prompt(S.vocab, c["P"], seed=12000 + seed)
+    cap = max(c["cap"], c["P"] + n)
+    cache, ws = b.Cache(S, cap), b.Workspace(S, cap)
+    b.prefill(model, cache, torch.from_numpy(prompt).cuda(), ws)
+    lg = torch.empty((n, S.vocab), dtype=torch.float32, device="cuda")
+    am = torch.empty(n, dtype=torch.int32, device="cuda")
+    b.tree_verify(model, cache, torch.from_numpy(toks).cuda(), torch.from_numpy(np.asarray(pars, np.int32)).cuda(),
+                  ws, logits=lg, argmax=am)
+    assert ws.error_bits() == 0 and cache.length() == c["P"] + n
+    g = to_np(lg)
+    assert np.array_equal(to_np(am), g.argmax(axis=1))
+    ow = OracleWeights(S, w)
+    oc = OracleCache(S, cap)
+    prefill(ow, oc, prompt)
+    assert_logits_close(g, tree_forward(ow, oc, toks, pars), f"random tree {c} n={n}")
