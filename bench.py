@@ -878,9 +878,12 @@ def main():
                 raise RuntimeError(f"{nm}: jobs with the same seeds committed different tokens")
             st = o1[0][0]
             t, idn = sj.terms(2)
+            # the self-draft's k target steps counted as free (reported on their own, as the draft term)
+            excl = [n_new * args.steps / (x - args.steps * st.round * t["draft"] * 1e-3) for x in sec]
             legs[nm] = {"tok_s": stats([n_new * args.steps / x for x in sec]), "rounds_per_job": st.round,
                         "accepted_per_round": round(st.accepted_total / max(st.round, 1), 3), "terms_ms": t,
-                        "cost_model": idn, "accept_us": round(t["accept"] * 1e3, 1), **kw}
+                        "cost_model": idn, "accept_us": round(t["accept"] * 1e3, 1),
+                        "tok_s_excl_self_draft": stats(excl), **kw}
             del sj
             log(f"leg {nm} done")
         out["legs"] = legs
